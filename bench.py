@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark: KDA multi-token recurrent prefill on one MI355X.
+
+One step is one ``kda_prefill`` call -- the whole hot path (gate cumsum,
+gated K K^T / Q K^T, triangular solve, chunk recurrence, outputs, final
+state) -- over the B8 T8192 H12 K=V=128 bf16 workload with an fp32 initial
+state, inputs resident in HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/sec and ms/call, H=12 K=V=128 bf16 at B8 T8192; MFMA util %"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, vendor figure
+# The pages' number for this shape (110-SM SM120, no initial state): 0.881 ms
+PAGES_TOKENS_PER_S = 8 * 8192 / 0.881e-3
+KERNEL_SOURCE = os.path.join(ROOT, "kda_gated_delta_chunked_amd", "csrc", "kda_fused.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_b8_t8192.json")
+
+
+def algorithmic_bytes(p) -> int:
+    """HBM bytes the method must move: q, k, v (bf16), g (fp32), beta (fp32)
+    in, out (bf16) written, and the fp32 state read and written per
+    (sequence, head)."""
+    th = p.T_total * p.H
+    per_token_head = 128 * 2 * 3 + 128 * 4 + 4 + 128 * 2
+    state = 128 * 128 * 4 * p.N * p.H
+    return th * per_token_head + state * ((1 if p.initial_state is not None else 0) + 1)
+
+
+def algorithmic_flops(p) -> float:
+    """Matrix flops of the chunked form per token-head (C = 64): state read
+    for X and O and the state update (3 K V), the in-chunk K K^T / Q K^T and
+    M U / N Y products (C (3K + 2V) / 2), and the C^2/6 solve."""
+    C, K, V = 64, 128, 128
+    per = 2 * (3 * K * V + C * (3 * K + 2 * V) / 2 + C * C / 6)
+    return float(per) * p.T_total * p.H
+
+
+def executed_mfma_flops(p, vsplit: int) -> float:
+    """Flops of the v_mfma_f32_16x16x32_bf16 instructions the fused kernel
+    issues (hi/lo passes included), from its schedule: per workgroup and
+    segment, 112 for the gate products and 90 per 16-column tile for the
+    recurrence."""
+    ntile = 128 // vsplit // 16
+    per_wg_seg = 112 + 90 * ntile
+    segs = 0
+    for n in range(p.N):
+        L = int(p.cu_seqlens[n + 1] - p.cu_seqlens[n])
+        s = (L + 63) // 64
+        if p.ckpt_offsets is not None:
+            off = int(p.ckpt_offsets[n])
+            if 0 < off < L and off % 64 != 0:
+                s += 1
+        segs += s
+    return float(per_wg_seg * 16 * 16 * 32 * 2) * segs * p.H * vsplit
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256") != kernel_sha() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(p, sample_tokens: int):
+    """Time the fp64 oracle (as it stands) on the first `sample_tokens` tokens
+    of every sequence of the workload, all heads, on all host cores."""
+    import oracle
+    oracle.build()
+    idx = np.concatenate([np.arange(p.cu_seqlens[n], p.cu_seqlens[n] + min(sample_tokens,
+                          p.cu_seqlens[n + 1] - p.cu_seqlens[n])) for n in range(p.N)])
+    lens = [min(sample_tokens, int(p.cu_seqlens[n + 1] - p.cu_seqlens[n])) for n in range(p.N)]
+    cu = np.zeros(p.N + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.prefill(p.q[idx], p.k[idx], p.v[idx], p.g[idx], p.beta[idx], scale=p.scale,
+                   num_seqs=p.N, cu_seqlens=cu, initial_state=p.initial_state, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": float(cu[-1]) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of each of the {p.N} sequences, all {p.H} "
+                      f"heads ({int(cu[-1]) * p.H} token-heads), fp64 token recurrence, "
+                      f"{dt:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b8_t8192")
+    ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this path runs per (sequence, head) on a single "
+              f"MI355X and has no multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    from kda_gated_delta_chunked_amd import synth
+
+    p = synth.workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    q, k, v = bf16(p.q), bf16(p.k), bf16(p.v)
+    g = torch.from_numpy(p.g).to(dev)
+    beta = torch.from_numpy(p.beta).to(dev)
+    cu = None if p.fixed else torch.from_numpy(p.cu_seqlens).to(dev)
+    s0 = None if p.initial_state is None else torch.from_numpy(p.initial_state).to(dev)
+    offs = None if p.ckpt_offsets is None else torch.from_numpy(p.ckpt_offsets).to(dev)
+    out = torch.empty_like(v)
+    fin = torch.empty((p.N, p.H, 128, 128), dtype=torch.float32, device=dev)
+    ck = None if offs is None else torch.empty_like(fin)
+    prob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, value_split=args.value_split)
+    variant, vsplit = K.plan(prob)
+    stream = torch.cuda.current_stream(dev)
+
+    def ptr(t):
+        return 0 if t is None else t.data_ptr()
+
+    def step():
+        st = K.prefill_raw(prob, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), ptr(s0),
+                           ptr(out), ptr(fin), ptr(offs), ptr(ck), 0, 0, stream.cuda_stream)
+        if st != 0:
+            raise K.KDAError(st, "kda_prefill")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_launch = float(np.mean(per_launch_ms))
+    ms_step = wall * 1e3 / args.steps
+    tokens = p.T_total
+    value = tokens / (ms_step * 1e-3)
+
+    alg_b = algorithmic_bytes(p)
+    achieved = alg_b / (ms_launch * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "kda_fused_kernel", "kernel_ms": round(ms_launch, 4),
+            "algorithmic_bytes": alg_b}
+    ex_fl = executed_mfma_flops(p, vsplit)
+    alg_fl = algorithmic_flops(p)
+    mfma = {"executed_tflops": round(ex_fl / (ms_launch * 1e-3) / 1e12, 1),
+            "executed_util": round(ex_fl / (ms_launch * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
+            "algorithmic_tflops": round(alg_fl / (ms_launch * 1e-3) / 1e12, 1),
+            "algorithmic_util": round(alg_fl / (ms_launch * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
+            "peak_tflops": BF16_MFMA_PEAK_TFLOPS}
+    res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": round(value / PAGES_TOKENS_PER_S, 3) if args.workload == "b8_t8192" else None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": args.workload, "B": p.N if p.fixed else None,
+                      "T": int(p.seq_lens[0]) if p.fixed else None, "num_seqs": p.N,
+                      "total_tokens": p.T_total, "H": p.H, "K": 128, "V": 128,
+                      "initial_state": p.initial_state is not None,
+                      "checkpoints": p.ckpt_offsets is not None,
+                      "variant": variant, "value_split": vsplit},
+           "roofline": roof, "mfma": mfma}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

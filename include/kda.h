@@ -1,0 +1,132 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) multi-token recurrent
+ * prefill on AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes.  For every sequence n of a fixed or packed batch and
+ * every head h, independently, starting from an fp32 K x V state S (K = V =
+ * 128, row d = key channel; the initial state, or zeros) and for each token t
+ * of the sequence in order:
+ *
+ *   S   <- Diag(exp(g_t)) S                     decay per key channel, g_t <= 0
+ *   S   <- S + beta_t k_t (v_t - S^T k_t)^T      delta-rule rank-1 correction
+ *   o_t <- scale * S^T q_t                        read-out of the updated state
+ *
+ * This is Kimi Delta Attention as used by Kimi Linear: a fixed-size recurrent
+ * state per head (FlashKDA page, item description), with the prefill contract
+ * of lmdeploy PR #5050 (Modification: BF16 inputs, K/V dimensions of 128, FP32
+ * recurrent state, gate lower bound in [-5, 0], checkpoint export at a
+ * requested position) and of FlashInfer PR #4262 "cake_kda" (Dispatch
+ * contract: fixed [B, T, H, 128] or packed inputs with cu_seqlens).  q and k
+ * are taken as given (callers L2-normalise them beforehand), g is a finished
+ * natural-log decay and beta an already-activated strength in [0, 1].
+ *
+ * The device computes the chunk-parallel form of the same recurrence (chunks
+ * of 64 tokens aligned to each sequence start), so results equal the token
+ * recurrence up to floating-point rounding.
+ *
+ * Layouts (all row-major, last index fastest, all buffers device memory):
+ *   q, k, v        bf16  [T_total, H, 128]
+ *   g              fp32  [T_total, H, 128]   lower_bound <= g <= 0
+ *   beta           fp32  [T_total, H]
+ *   cu_seqlens     int32 [N + 1], or NULL for a fixed batch of N sequences of
+ *                  T_total / N tokens.  Contract when given (not checked on the
+ *                  device, as in lmdeploy PR #5050, Modification: offset values
+ *                  stay the caller's responsibility so nothing synchronises):
+ *                  cu[0] = 0, cu[N] = T_total, non-decreasing.
+ *   initial_state  fp32  [N, H, 128, 128] (K x V), or NULL for zeros
+ *   out            bf16  [T_total, H, 128]; may be exactly v (same pointer)
+ *   final_state    fp32  [N, H, 128, 128], or NULL; may be exactly
+ *                  initial_state (in-place update, FlashInfer PR #4262,
+ *                  Physical schedules and true in-place state update)
+ *   ckpt_offsets   int32 [N], or NULL: ckpt_offsets[n] = number of tokens of
+ *                  sequence n consumed when its state is exported (0 exports
+ *                  the initial state, L_n the final state).  Offsets outside
+ *                  [0, L_n] export nothing and leave that slot untouched.
+ *   ckpt_state     fp32  [N, H, 128, 128] caller-owned, contiguous; NULL iff
+ *                  ckpt_offsets is NULL; must not overlap either state buffer.
+ *
+ * Ownership and streams: every buffer belongs to the caller; the library
+ * allocates nothing, keeps no pointer after returning and holds no state
+ * between calls.  All work is enqueued on `stream` with no host
+ * synchronisation and no device-to-host copy, so a call can be captured in a
+ * HIP graph without warm-up.  Errors are detected on the host before anything
+ * is enqueued; device-resident values (cu_seqlens, offsets, g) are not read on
+ * the host.  A zero-length sequence keeps its initial state bit for bit.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = -1,      /* bad sizes, NULL where required, bad scalar */
+  KDA_ERR_UNSUPPORTED = -2,      /* head dims other than 128, unknown variant */
+  KDA_ERR_ALIGNMENT = -3,        /* a pointer not 16-byte aligned */
+  KDA_ERR_OVERLAP = -4,          /* buffers overlap other than the allowed exact aliases */
+  KDA_ERR_WORKSPACE_TOO_SMALL = -5,
+  KDA_ERR_TOO_LARGE = -6,        /* T_total * H * 128 exceeds 2^31 - 1 */
+  KDA_ERR_HIP = -7               /* a HIP runtime call or launch failed */
+} kda_status;
+
+typedef enum {
+  KDA_VARIANT_AUTO = 0,          /* pick the schedule from the problem shape and CU count */
+  KDA_VARIANT_FUSED = 2          /* one launch: chunk preparation and recurrence per workgroup */
+} kda_variant;
+
+typedef struct {
+  int32_t num_seqs;          /* N >= 1 (fixed layout: the batch size B) */
+  int64_t total_tokens;      /* T_total >= 0 (fixed layout: B * T) */
+  int32_t num_heads;         /* H >= 1, shared by q, k and v */
+  int32_t head_dim_k;        /* must be 128 */
+  int32_t head_dim_v;        /* must be 128 */
+  float scale;               /* read-out scale, finite (typically 1/sqrt(128)) */
+  float gate_lower_bound;    /* caller's promise g >= bound; must lie in [-5, 0] */
+  int32_t variant;           /* kda_variant */
+  int32_t value_split;       /* 0 = automatic, else 2 or 4: workgroups per (sequence, head),
+                                each owning 128/value_split columns of the state */
+} kda_problem;
+
+/* Bytes of caller workspace kda_prefill needs for this problem (host only, no
+ * device access).  The current schedules need none, so this reports 0; a
+ * caller may still pass a buffer. */
+kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes);
+
+/* Host-side argument checks of kda_prefill without launching anything: sizes,
+ * the K = V = 128 and gate-bound contract, NULL rules, 16-byte alignment,
+ * overlap (only out == v and final_state == initial_state may alias, and
+ * only exactly), workspace size and the INT32 bound on T_total * H * 128
+ * (FlashInfer PR #4633, Description: the flat output is bounded on the host).
+ * Pointers are compared, never dereferenced, so host addresses may be used. */
+kda_status kda_validate(const kda_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const int32_t* cu_seqlens,
+                        const float* initial_state, const void* out, const float* final_state,
+                        const int32_t* ckpt_offsets, const float* ckpt_state,
+                        const void* workspace, size_t workspace_bytes);
+
+/* Enqueue one prefill on `stream` (a hipStream_t; NULL = the null stream).
+ * q, k, v, out are bf16 bit patterns (uint16_t).  Returns KDA_OK once the work
+ * is enqueued; any other status means nothing was enqueued, except
+ * KDA_ERR_HIP, which reports a failed launch. */
+kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const float* g, const float* beta,
+                       const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                       float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string for a status code. */
+const char* kda_status_string(kda_status s);
+
+/* Number of workgroups per (sequence, head) kda_prefill would use for this
+ * problem on the current device (host only; reads the device's CU count). */
+kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,198 @@
+// kda_api.hip -- host side of libkda: argument validation, schedule choice and
+// launch.  The declarations and the contract are in include/kda.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_kernels.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int64_t kInt32Max = 2147483647LL;
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+  bool empty() const { return lo == hi; }
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+  Range r;
+  if (p && bytes) {
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + bytes;
+  }
+  return r;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+bool exact(const Range& a, const Range& b) { return !a.empty() && a.lo == b.lo && a.hi == b.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_problem(const kda_problem* p) {
+  if (!p) return KDA_ERR_INVALID_ARG;
+  if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
+  if (p->num_seqs < 1 || p->num_heads < 1 || p->total_tokens < 0) return KDA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale)) return KDA_ERR_INVALID_ARG;
+  // gate lower bound contract: [-5, 0], both ends included
+  if (!std::isfinite(p->gate_lower_bound) || p->gate_lower_bound < -5.0f ||
+      p->gate_lower_bound > 0.0f)
+    return KDA_ERR_INVALID_ARG;
+  if (p->variant != KDA_VARIANT_AUTO && p->variant != KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;
+  if (p->value_split != 0 && p->value_split != 2 && p->value_split != 4) return KDA_ERR_UNSUPPORTED;
+  // the flat output index T_total * H * 128 must fit in int32
+  if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
+  if ((int64_t)p->num_seqs * p->num_heads > kInt32Max / 8) return KDA_ERR_TOO_LARGE;
+  return KDA_OK;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Schedule choice.  Each workgroup carries one (sequence, head) pair and a
+// slice of the state's columns; the chunk preparation is repeated by every
+// workgroup of a pair, the recurrence is split.  Two workgroups per pair is
+// the default; four when there are too few pairs to occupy half the CUs.
+void choose(const kda_problem* p, int cus, int32_t* variant, int32_t* vsplit) {
+  *variant = KDA_VARIANT_FUSED;
+  if (p->value_split) {
+    *vsplit = p->value_split;
+    return;
+  }
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
+  *vsplit = (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case KDA_ERR_OVERLAP: return "buffers overlap";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KDA_ERR_TOO_LARGE: return "problem exceeds the int32 flat-index bound";
+    case KDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes) {
+  if (!bytes) return KDA_ERR_INVALID_ARG;
+  const kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  *bytes = 0;
+  return KDA_OK;
+}
+
+kda_status kda_validate(const kda_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const int32_t* cu_seqlens,
+                        const float* initial_state, const void* out, const float* final_state,
+                        const int32_t* ckpt_offsets, const float* ckpt_state,
+                        const void* workspace, size_t workspace_bytes) {
+  kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  const int64_t T = p->total_tokens;
+  const int64_t N = p->num_seqs, H = p->num_heads;
+  if (!cu_seqlens && (T % N) != 0) return KDA_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
+  if ((ckpt_offsets == nullptr) != (ckpt_state == nullptr)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                        ckpt_offsets, ckpt_state, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
+  size_t need = 0;
+  st = kda_prefill_workspace_size(p, &need);
+  if (st != KDA_OK) return st;
+  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+  const uint64_t tok_bf16 = (uint64_t)T * H * kHeadDim * 2;
+  const uint64_t tok_f32 = (uint64_t)T * H * kHeadDim * 4;
+  const uint64_t state = (uint64_t)N * H * kHeadDim * kHeadDim * 4;
+  const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
+  const Range rg = range_of(g, tok_f32), rb = range_of(beta, (uint64_t)T * H * 4);
+  const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4);
+  const Range rs0 = range_of(initial_state, state);
+  const Range rout = range_of(out, tok_bf16), rfin = range_of(final_state, state);
+  const Range roff = range_of(ckpt_offsets, (uint64_t)N * 4);
+  const Range rck = range_of(ckpt_state, state);
+  const Range rws = range_of(workspace, workspace_bytes);
+
+  // out: may be exactly v; must not touch any other buffer
+  for (const Range& r : {rq, rk, rg, rb, rcu, rs0, rfin, roff, rck, rws})
+    if (overlaps(rout, r)) return KDA_ERR_OVERLAP;
+  if (overlaps(rout, rv) && !exact(rout, rv)) return KDA_ERR_OVERLAP;
+  // final state: may be exactly the initial state
+  for (const Range& r : {rq, rk, rv, rg, rb, rcu, roff, rck, rws})
+    if (overlaps(rfin, r)) return KDA_ERR_OVERLAP;
+  if (overlaps(rfin, rs0) && !exact(rfin, rs0)) return KDA_ERR_OVERLAP;
+  // checkpoint buffer: no overlap with anything
+  for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff, rws})
+    if (overlaps(rck, r)) return KDA_ERR_OVERLAP;
+  return KDA_OK;
+}
+
+kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split) {
+  if (!variant || !value_split) return KDA_ERR_INVALID_ARG;
+  const kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  choose(p, device_cu_count(), variant, value_split);
+  return KDA_OK;
+}
+
+kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const float* g, const float* beta,
+                       const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                       float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const kda_status st = kda_validate(p, q, k, v, g, beta, cu_seqlens, initial_state, out,
+                                     final_state, ckpt_offsets, ckpt_state, workspace,
+                                     workspace_bytes);
+  if (st != KDA_OK) return st;
+  int32_t variant = 0, vsplit = 0;
+  choose(p, device_cu_count(), &variant, &vsplit);
+
+  kda::FusedArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  a.s0 = initial_state;
+  a.out = out;
+  a.final_state = final_state;
+  a.ckpt_off = ckpt_offsets;
+  a.ckpt = ckpt_state;
+  a.N = p->num_seqs;
+  a.H = p->num_heads;
+  a.num_pairs = p->num_seqs * p->num_heads;
+  a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
+  a.scale = p->scale;
+  const hipError_t err = kda::launch_fused(a, vsplit, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

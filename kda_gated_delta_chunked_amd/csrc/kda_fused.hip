@@ -1,0 +1,740 @@
+// kda_fused.hip -- one-launch chunked KDA prefill for gfx950 (MI355X).
+//
+// One workgroup of 512 threads (8 wave64s) owns one (sequence, head) pair and
+// a slice of VW columns of its 128 x 128 fp32 state (VSPLIT = 128 / VW
+// workgroups share a pair; the columns of the state evolve independently).
+// It walks the sequence in segments of at most 64 tokens aligned to the
+// sequence start; a checkpoint offset inside a chunk splits that chunk in two,
+// so the exported state is the exact state after that many tokens.
+//
+// Per segment of c <= 64 rows (placed in the last c rows of a 64-row tile;
+// the rows before them are zero and contribute nothing),
+// with G_r = g_0 + ... + g_r per key channel:
+//   A[r,s] = sum_d k_rd k_sd exp(G_rd - G_sd)   s < r    (gated K K^T)
+//   M[r,s] = sum_d q_rd k_sd exp(G_rd - G_sd)   s <= r   (gated Q K^T)
+//   T = (I + diag(beta) A)^-1,  N = T - I
+//   X = V - (K exp(G)) S,  Y = diag(beta) X,  U = Y + N Y
+//   O = scale ((Q exp(G)) S + M U)
+//   S <- diag(exp(G_end)) S + (K exp(G_end - G))^T U
+// which is the token recurrence (decay, delta-rule correction, read-out of
+// the updated state) regrouped by chunks.
+//
+// Exponent range: exp(G_r - G_s) is split as a product of two factors around
+// a reference inside the chunk.  Rows are grouped in 16-row blocks; with
+// g >= -5 (the gate lower bound of the KDA prefill contract, lmdeploy PR
+// #5050, Modification) no factor exceeds exp(80), which fp32 and bf16 hold.
+// Per row r of block i: Ef_r = exp(G_r - G_{16i-1}) <= 1 (prefix product of
+// exp(g) inside the block) and Eb_r = exp(G_{16i+15} - G_r) <= 1 (suffix
+// product); bd_i = exp(sum of g over block i).
+//   block (i,i):    exp(G_r - G_s) = Ef_r * (Eb_s / bd_i)
+//   block (i,i-1):  exp(G_r - G_s) = Ef_r * Eb_s
+//   block (i,j<i-1):exp(G_r - G_s) = Ef_r * Eb_s * prod_{j<m<i} bd_m
+//
+// Matrix products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+// Precision: bf16 operands everywhere except where rounding would reach the
+// fp32 state or the output directly: U is fed as bf16 hi + lo pairs to the
+// state update and to M U, the last 16 rows of K exp(G_end - G) are hi + lo,
+// the diagonal blocks of M use hi + lo operands, and the identity part of T
+// is applied in fp32 (U = Y + N Y).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_kernels.h"
+
+namespace kda {
+namespace {
+
+constexpr int CH = 64;        // chunk rows
+constexpr int DK = 128;       // key channels
+constexpr int DVT = 128;      // value channels (total)
+constexpr int NT = 512;       // threads per workgroup (8 wave64s)
+constexpr int KP = DK + 8;    // bf16 pitch of [row][d] operand tiles
+constexpr int RP = CH + 8;    // bf16 pitch of [*][r] tiles (64 wide)
+constexpr int LP = 16 + 8;    // bf16 pitch of the 16-wide lo tile
+constexpr int FP = CH + 4;    // fp32 pitch of 64 x 64 matrices
+constexpr int LDP = 16 + 4;   // fp32 pitch of the 16 x 16 diagonal L blocks
+constexpr int TP = 32 + 8;    // bf16 pitch of 32 x 32 solve tiles
+constexpr int SP = 16 + 8;    // bf16 pitch of 16 x 16 solve tiles
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+// hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint16_t ha = f2bf(a), hb = f2bf(b);
+  hi = (uint32_t)ha | ((uint32_t)hb << 16);
+  lo = pack2(a - bf2f(ha), b - bf2f(hb));
+}
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+template <int VW>
+struct Layout {
+  static constexpr int NTILE = VW / 16;
+  // gate-operand phase (rows x KP bf16)
+  static constexpr int G_KF = 0;
+  static constexpr int G_QF = G_KF + 64 * KP * 2;
+  static constexpr int G_QFLO = G_QF + 64 * KP * 2;
+  static constexpr int G_KR = G_QFLO + 64 * KP * 2;
+  static constexpr int G_KRLO = G_KR + 64 * KP * 2;
+  static constexpr int G_KB = G_KRLO + 64 * KP * 2;   // 48 rows: blocks 0..2
+  static constexpr int G_KW = G_KB + 48 * KP * 2;     // 3 x 16 rows
+  static constexpr int G_END = G_KW + 48 * KP * 2;
+  // prepared operands (same region, after the gate products)
+  static constexpr int P_KT = 0;                       // -K exp(G)   [64][KP]
+  static constexpr int P_QT = P_KT + 64 * KP * 2;      //  Q exp(G)   [64][KP]
+  static constexpr int P_KHT = P_QT + 64 * KP * 2;     //  K exp(G_end - G), transposed [128][RP]
+  static constexpr int P_KHLO = P_KHT + DK * RP * 2;   //  lo part of its last 16 rows [128][LP]
+  static constexpr int P_M = P_KHLO + DK * LP * 2;     //  M bf16 [64][RP]
+  static constexpr int P_N = P_M + 64 * RP * 2;        //  N bf16 [64][RP]
+  static constexpr int P_END = P_N + 64 * RP * 2;
+  // triangular-solve scratch (after the gate products, before the recurrence)
+  static constexpr int S_LDT = P_END;                  // diag blocks of L, transposed, fp32 [4][16][LDP]
+  static constexpr int S_LB = S_LDT + 4 * 16 * LDP * 4;  // L bf16 [64][RP] (off-diagonal blocks)
+  static constexpr int S_TAT = S_LB + 64 * RP * 2;     // [[T00,0],[T10,T11]]^T bf16 [32][TP]
+  static constexpr int S_TBR = S_TAT + 32 * TP * 2;    // [[T22,0],[T32,T33]]   bf16 [32][TP]
+  static constexpr int S_T22T = S_TBR + 32 * TP * 2;   // T22^T bf16 [16][SP]
+  static constexpr int S_T11R = S_T22T + 16 * SP * 2;  // T11   bf16 [16][SP]
+  static constexpr int S_PT = S_T11R + 16 * SP * 2;    // (L10 T00)^T, (L32 T22)^T bf16 [2][16][SP]
+  static constexpr int S_QT = S_PT + 2 * 16 * SP * 2;  // (L[32:64,0:32] Ta)^T bf16 [32][TP]
+  static constexpr int S_END = S_QT + 32 * TP * 2;
+  // recurrence scratch (after the solve; aliases the solve scratch)
+  static constexpr int D_ST = P_END;                   // S^T bf16 [VW][KP]
+  static constexpr int D_UHI = D_ST + VW * KP * 2;     // U^T hi [VW][RP]
+  static constexpr int D_ULO = D_UHI + VW * RP * 2;    // U^T lo [VW][RP]
+  static constexpr int D_END = D_ULO + VW * RP * 2;
+  static constexpr int M1 = G_END > S_END ? G_END : S_END;
+  static constexpr int REGION = M1 > D_END ? M1 : D_END;
+  // always-live
+  static constexpr int A_V = (REGION + 15) / 16 * 16;  // V slice bf16 [64][VW+8]
+  static constexpr int VP = VW + 8;
+  static constexpr int A_BETA = A_V + 64 * VP * 2;     // [64] fp32
+  static constexpr int A_GAM = A_BETA + 64 * 4;        // [128] fp32
+  static constexpr int A_BD = A_GAM + DK * 4;          // [4][128] fp32
+  static constexpr int A_HALF = A_BD + 4 * DK * 4;     // [8][128] fp32 half-block products
+  static constexpr int A_Y = A_HALF + 8 * DK * 4;      // Y^T bf16 [VW][RP]
+  static constexpr int TOTAL = A_Y + VW * RP * 2;
+};
+
+// Raw inputs of one segment for one thread of the elementwise role (rows
+// 16ib + 8hb .. +7, channels d0, d0+1), plus its share of the V slice and beta.
+struct SegmentLoads {
+  float2 g[8];
+  uint32_t k[8], q[8];
+  uint4 v;
+  float beta;
+};
+
+template <int VW>
+__global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
+  using Lay = Layout<VW>;
+  constexpr int VSPLIT = DVT / VW;
+  constexpr int NTILE = Lay::NTILE;                  // 16-column tiles owned
+  constexpr int NTW = NTILE >= 2 ? NTILE / 2 : 1;    // tiles per wave in the row-block phases
+  constexpr int PER_ROW = VW / 8;                    // 16-byte pieces per V row
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::TOTAL];
+
+  // ---- which (sequence, head, column slice) this workgroup owns --------------
+  // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8); keep
+  // the VSPLIT workgroups of a pair on the same XCD so they share L2 for q/k/g.
+  const int bx = blockIdx.x;
+  const int xcd = bx & 7, rest = bx >> 3;
+  const int vs = rest % VSPLIT;
+  const int pair = (rest / VSPLIT) * 8 + xcd;
+  if (pair >= a.num_pairs) return;
+  const int n = pair / a.H, h = pair % a.H;
+  const int H = a.H;
+
+  int64_t bos, len;
+  if (a.cu_seqlens) {
+    bos = a.cu_seqlens[n];
+    len = (int64_t)a.cu_seqlens[n + 1] - bos;
+  } else {
+    len = a.T_fixed;
+    bos = (int64_t)n * len;
+  }
+  const int64_t ckpt_at = a.ckpt_off ? (int64_t)a.ckpt_off[n] : -1;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // w is wave-uniform
+  const int lr = l & 15, lg = l >> 4;   // MFMA lane row / lane group
+  const int col0 = vs * VW;             // first state column owned
+
+  uint16_t* gKf = reinterpret_cast<uint16_t*>(smem + Lay::G_KF);
+  uint16_t* gQf = reinterpret_cast<uint16_t*>(smem + Lay::G_QF);
+  uint16_t* gQfLo = reinterpret_cast<uint16_t*>(smem + Lay::G_QFLO);
+  uint16_t* gKr = reinterpret_cast<uint16_t*>(smem + Lay::G_KR);
+  uint16_t* gKrLo = reinterpret_cast<uint16_t*>(smem + Lay::G_KRLO);
+  uint16_t* gKb = reinterpret_cast<uint16_t*>(smem + Lay::G_KB);
+  uint16_t* gKw = reinterpret_cast<uint16_t*>(smem + Lay::G_KW);
+  uint16_t* pKt = reinterpret_cast<uint16_t*>(smem + Lay::P_KT);
+  uint16_t* pQt = reinterpret_cast<uint16_t*>(smem + Lay::P_QT);
+  uint16_t* pKhT = reinterpret_cast<uint16_t*>(smem + Lay::P_KHT);
+  uint16_t* pKhLo = reinterpret_cast<uint16_t*>(smem + Lay::P_KHLO);
+  uint16_t* pM = reinterpret_cast<uint16_t*>(smem + Lay::P_M);
+  uint16_t* pN = reinterpret_cast<uint16_t*>(smem + Lay::P_N);
+  float* sLdT = reinterpret_cast<float*>(smem + Lay::S_LDT);
+  uint16_t* sLb = reinterpret_cast<uint16_t*>(smem + Lay::S_LB);
+  uint16_t* sTaT = reinterpret_cast<uint16_t*>(smem + Lay::S_TAT);
+  uint16_t* sTbR = reinterpret_cast<uint16_t*>(smem + Lay::S_TBR);
+  uint16_t* sT22T = reinterpret_cast<uint16_t*>(smem + Lay::S_T22T);
+  uint16_t* sT11R = reinterpret_cast<uint16_t*>(smem + Lay::S_T11R);
+  uint16_t* sPT = reinterpret_cast<uint16_t*>(smem + Lay::S_PT);
+  uint16_t* sQT = reinterpret_cast<uint16_t*>(smem + Lay::S_QT);
+  uint16_t* dST = reinterpret_cast<uint16_t*>(smem + Lay::D_ST);
+  uint16_t* dUhi = reinterpret_cast<uint16_t*>(smem + Lay::D_UHI);
+  uint16_t* dUlo = reinterpret_cast<uint16_t*>(smem + Lay::D_ULO);
+  uint16_t* mV = reinterpret_cast<uint16_t*>(smem + Lay::A_V);
+  float* mBeta = reinterpret_cast<float*>(smem + Lay::A_BETA);
+  float* mGam = reinterpret_cast<float*>(smem + Lay::A_GAM);
+  float* mBd = reinterpret_cast<float*>(smem + Lay::A_BD);
+  float* mHalf = reinterpret_cast<float*>(smem + Lay::A_HALF);
+  uint16_t* mY = reinterpret_cast<uint16_t*>(smem + Lay::A_Y);
+
+  // ---- state: wave w owns rows d in [16w, 16w+16), all VW columns ------------
+  // S[nt][e] = S[16w + 4lg + e][col0 + 16nt + lr]
+  f32x4 S[NTILE];
+  const size_t state_base = (size_t)pair * DK * DVT;
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * w + 4 * lg + e;
+      const int j = col0 + 16 * nt + lr;
+      S[nt][e] = a.s0 ? a.s0[state_base + (size_t)d * DVT + j] : 0.f;
+    }
+
+  auto export_state = [&](float* dst) {
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * w + 4 * lg + e;
+        const int j = col0 + 16 * nt + lr;
+        dst[state_base + (size_t)d * DVT + j] = S[nt][e];
+      }
+  };
+
+  if (ckpt_at == 0) export_state(a.ckpt);
+
+  // elementwise role: block ib, rows 16ib + 8hb .. +7, channels d0, d0+1
+  const int ib = w >> 1;
+  const int hb = w & 1;
+  const int d0 = 2 * l;
+  // row-block role in the recurrence: block rb, column tiles [nt0, nt0 + NTW)
+  const int rb = w & 3;
+  const int nt0 = NTILE >= 2 ? (w >> 2) * NTW : 0;
+  const bool rb_active = NTILE >= 2 || w < 4;
+  // V-slice piece of this thread
+  const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
+  const bool v_thread = tid < 64 * PER_ROW;
+
+  // Segment geometry: at most 64 tokens, never crossing a multiple of 64 from
+  // the sequence start, split at the checkpoint offset.  The segment's c
+  // tokens sit in the LAST c rows of the 64-row tile (rows before `off` are
+  // zero and contribute nothing), so its final 16 tokens are always tile rows
+  // 48..63, the rows whose K exp(G_end - G) carries a lo part.  Tile row r
+  // holds token tok0 + r.
+  auto seg_end_of = [&](int64_t p0) {
+    const int64_t ce = (p0 / CH + 1) * CH < len ? (p0 / CH + 1) * CH : len;
+    return (ckpt_at > p0 && ckpt_at < ce) ? ckpt_at : ce;
+  };
+  auto load_segment = [&](int64_t p0, SegmentLoads& L) {
+    const int off = CH - (int)(seg_end_of(p0) - p0);
+    const int64_t t0 = bos + p0 - off;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 16 * ib + 8 * hb + e;
+      if (r >= off) {
+        const size_t base = ((size_t)(t0 + r) * H + h) * DK + d0;
+        L.g[e] = *reinterpret_cast<const float2*>(a.g + base);
+        L.k[e] = *reinterpret_cast<const uint32_t*>(a.k + base);
+        L.q[e] = *reinterpret_cast<const uint32_t*>(a.q + base);
+      } else {
+        L.g[e] = make_float2(0.f, 0.f);
+        L.k[e] = 0u;
+        L.q[e] = 0u;
+      }
+    }
+    L.v = make_uint4(0, 0, 0, 0);
+    if (v_thread && vr >= off)
+      L.v = *reinterpret_cast<const uint4*>(a.v + ((size_t)(t0 + vr) * H + h) * DVT + col0 + 8 * vc8);
+    L.beta = (tid < 64 && tid >= off) ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+  };
+
+  SegmentLoads ld;
+  int64_t pos = 0;
+  if (pos < len) load_segment(pos, ld);
+  while (pos < len) {
+    const int64_t seg_end = seg_end_of(pos);
+    const int c = (int)(seg_end - pos);
+    const int off = CH - c;
+    const int64_t tok0 = bos + pos - off;
+    // per-iteration copies of the lane coordinates: keeps the compiler from
+    // hoisting every derived LDS address out of the segment loop
+    int lane_it = l;
+    asm volatile("" : "+v"(lane_it));
+    const int lr = lane_it & 15, lg = lane_it >> 4, d0 = 2 * lane_it;
+    const int vr = (64 * w + lane_it) / PER_ROW, vc8 = (64 * w + lane_it) % PER_ROW;
+
+    // ================= phase A: gate factors and gate-product operands ========
+    if (v_thread) *reinterpret_cast<uint4*>(mV + vr * Lay::VP + 8 * vc8) = ld.v;
+    if (tid < 64) mBeta[tid] = ld.beta;
+    float kk[8][2], qq[8][2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kk[e][0] = __uint_as_float(ld.k[e] << 16); kk[e][1] = __uint_as_float(ld.k[e] & 0xffff0000u);
+      qq[e][0] = __uint_as_float(ld.q[e] << 16); qq[e][1] = __uint_as_float(ld.q[e] & 0xffff0000u);
+    }
+    // exp(g); prefix (Ef) and suffix (Eb) products within this half block
+    float Ef[8][2], Eb[8][2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      float ex[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ex[e] = __expf(ch ? ld.g[e].y : ld.g[e].x);
+      float run = 1.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { run *= ex[e]; Ef[e][ch] = run; }
+      run = 1.f;
+#pragma unroll
+      for (int e = 7; e >= 0; --e) { Eb[e][ch] = run; run *= ex[e]; }
+    }
+    *reinterpret_cast<float2*>(mHalf + (2 * ib + hb) * DK + d0) = make_float2(Ef[7][0], Ef[7][1]);
+    __syncthreads();  // (1) half-block products visible
+    {
+      const float2 other = *reinterpret_cast<const float2*>(mHalf + (2 * ib + (1 - hb)) * DK + d0);
+      if (hb == 0)
+        *reinterpret_cast<float2*>(mBd + ib * DK + d0) =
+            make_float2(Ef[7][0] * other.x, Ef[7][1] * other.y);
+      // complete the in-block products: Ef_r = exp(G_r - G_{16ib-1}), Eb_r = exp(G_{16ib+15} - G_r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (hb == 1) { Ef[e][0] *= other.x; Ef[e][1] *= other.y; }
+        else { Eb[e][0] *= other.x; Eb[e][1] *= other.y; }
+      }
+    }
+    __syncthreads();  // (2) block decays visible
+
+    float cref[2], Pend[2], rbd[2], W1[2], W2[2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      float bd[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) bd[m] = mBd[m * DK + d0 + ch];
+      float cr = 1.f, pe = 1.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < ib) cr *= bd[m];
+        if (m > ib) pe *= bd[m];
+      }
+      cref[ch] = cr; Pend[ch] = pe;
+      rbd[ch] = 1.f / bd[ib];
+      // block 0 rows feed blocks 2 and 3 (factors bd1 and bd1*bd2); block 1 rows feed block 3 (bd2)
+      W1[ch] = ib == 0 ? bd[1] : bd[2];
+      W2[ch] = bd[1] * bd[2];
+      if (ib == 0 && hb == 0) mGam[d0 + ch] = bd[0] * bd[1] * bd[2] * bd[3];
+    }
+    // gate-product operands; keep the fp32 pieces for the prepared operands
+    // kept for the prepared operands after the gate products: K exp(G) and
+    // Q exp(G) as bf16 pairs (their block-start factor is applied later and
+    // they only feed bf16 operands), K exp(G_end - G) in fp32 (its last rows
+    // carry a lo part)
+    uint32_t kfp[8], qfp[8];
+    float kb[8][2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int rl = 8 * hb + e;        // row within the block
+      const int r = 16 * ib + rl;
+      float kf[2], qf[2];
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        kf[ch] = kk[e][ch] * Ef[e][ch];
+        qf[ch] = qq[e][ch] * Ef[e][ch];
+        kb[e][ch] = kk[e][ch] * Eb[e][ch];
+      }
+      kfp[e] = pack2(kf[0], kf[1]);
+      *reinterpret_cast<uint32_t*>(gKf + r * KP + d0) = kfp[e];
+      uint32_t hi, lo;
+      split2(qf[0], qf[1], hi, lo);
+      qfp[e] = hi;
+      *reinterpret_cast<uint32_t*>(gQf + r * KP + d0) = hi;
+      *reinterpret_cast<uint32_t*>(gQfLo + r * KP + d0) = lo;
+      split2(kb[e][0] * rbd[0], kb[e][1] * rbd[1], hi, lo);
+      *reinterpret_cast<uint32_t*>(gKr + r * KP + d0) = hi;
+      *reinterpret_cast<uint32_t*>(gKrLo + r * KP + d0) = lo;
+      if (ib <= 2) *reinterpret_cast<uint32_t*>(gKb + r * KP + d0) = pack2(kb[e][0], kb[e][1]);
+      if (ib == 0) {
+        *reinterpret_cast<uint32_t*>(gKw + rl * KP + d0) =
+            pack2(kb[e][0] * W1[0], kb[e][1] * W1[1]);
+        *reinterpret_cast<uint32_t*>(gKw + (16 + rl) * KP + d0) =
+            pack2(kb[e][0] * W2[0], kb[e][1] * W2[1]);
+      } else if (ib == 1) {
+        *reinterpret_cast<uint32_t*>(gKw + (32 + rl) * KP + d0) =
+            pack2(kb[e][0] * W1[0], kb[e][1] * W1[1]);
+      }
+    }
+    __syncthreads();  // (3) gate operands ready
+
+    // ================= phase B: gated K K^T and Q K^T blocks ==================
+    // units (i, j <= i), u = i(i+1)/2 + j, dealt to waves u % 8
+    auto unit_i = [](int u) { return u >= 6 ? 3 : (u >= 3 ? 2 : (u >= 1 ? 1 : 0)); };
+    f32x4 accA[2], accM[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int u = w + 8 * s;
+      accA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accM[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < 10) {
+        const int i = unit_i(u), j = u - i * (i + 1) / 2;
+        const uint16_t* left_k = gKf + (16 * i + lr) * KP;
+        const uint16_t* left_q = gQf + (16 * i + lr) * KP;
+        const uint16_t* right;
+        if (i == j) right = gKr + (16 * i + lr) * KP;
+        else if (j == i - 1) right = gKb + (16 * j + lr) * KP;
+        else right = gKw + ((i == 2 ? 0 : (j == 0 ? 16 : 32)) + lr) * KP;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int off8 = 32 * ks + 8 * lg;
+          const bf16x8 bk = lds8(right + off8);
+          accA[s] = mfma(lds8(left_k + off8), bk, accA[s]);
+          accM[s] = mfma(lds8(left_q + off8), bk, accM[s]);
+          if (i == j) {
+            accM[s] = mfma(lds8(left_q + off8), lds8(gKrLo + (16 * i + lr) * KP + off8), accM[s]);
+            accM[s] = mfma(lds8(gQfLo + (16 * i + lr) * KP + off8), bk, accM[s]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // (4) gate operands consumed; region reused below
+
+    // L = diag(beta) A (strictly lower): diagonal blocks fp32 transposed for the
+    // 16x16 inversions, off-diagonal blocks bf16 for the matrix-core merges.
+    // M (lower incl. diagonal) bf16.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int u = w + 8 * s;
+      if (u < 10) {
+        const int i = unit_i(u), j = u - i * (i + 1) / 2;
+        const int sc = 16 * j + lr;
+        float lv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * lg + e;
+          lv[e] = sc < r ? mBeta[r] * accA[s][e] : 0.f;
+          pM[r * RP + sc] = f2bf(sc <= r ? accM[s][e] : 0.f);
+          if (i != j) sLb[r * RP + sc] = f2bf(lv[e]);
+        }
+        if (i == j)
+          *reinterpret_cast<float4*>(sLdT + (16 * i + lr) * LDP + 4 * lg) =
+              make_float4(lv[0], lv[1], lv[2], lv[3]);
+      }
+    }
+    // zero the upper blocks of M and N that the M U and N Y products read: (0,1), (2,3)
+    {
+      const int blk = tid >> 8, rr = (tid >> 4) & 15, cc = tid & 15;
+      const int r = blk == 0 ? rr : 32 + rr, sc = blk == 0 ? 16 + cc : 48 + cc;
+      pM[r * RP + sc] = 0;
+      pN[r * RP + sc] = 0;
+    }
+    // prepared operands: -K exp(G), Q exp(G), K exp(G_end - G) (transposed)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 16 * ib + 8 * hb + e;
+      *reinterpret_cast<uint32_t*>(pKt + r * KP + d0) =
+          pack2(-__uint_as_float(kfp[e] << 16) * cref[0], -__uint_as_float(kfp[e] & 0xffff0000u) * cref[1]);
+      *reinterpret_cast<uint32_t*>(pQt + r * KP + d0) =
+          pack2(__uint_as_float(qfp[e] << 16) * cref[0], __uint_as_float(qfp[e] & 0xffff0000u) * cref[1]);
+    }
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      uint16_t hv[8], lv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = kb[e][ch] * Pend[ch];
+        hv[e] = f2bf(x);
+        lv[e] = f2bf(x - bf2f(hv[e]));
+      }
+      *reinterpret_cast<uint4*>(pKhT + (d0 + ch) * RP + 16 * ib + 8 * hb) =
+          *reinterpret_cast<uint4*>(&hv[0]);
+      if (ib == 3)
+        *reinterpret_cast<uint4*>(pKhLo + (d0 + ch) * LP + 8 * hb) =
+            *reinterpret_cast<uint4*>(&lv[0]);
+    }
+    // prefetch the next segment's inputs; they land during phases C and D
+    if (seg_end < len) load_segment(seg_end, ld);
+    __syncthreads();  // (5) L, M and prepared operands ready
+
+    // ================= phase C: N = (I + L)^-1 - I ============================
+    // C1: the four 16x16 diagonal blocks T_ii = (I + L_ii)^-1 by column-wise
+    // forward substitution in fp32; wave w < 4 inverts block w, lane column lr.
+    if (w < 4) {
+      const int cc = lr;
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = r == cc ? 1.f : 0.f;
+      const float* LT = sLdT + (16 * w) * LDP;   // LT[s][r] = L[r][s]
+#pragma unroll
+      for (int s2 = 0; s2 < 15; ++s2) {
+        float lcol[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(LT + s2 * LDP + 4 * q4);
+          lcol[4 * q4] = v4.x; lcol[4 * q4 + 1] = v4.y; lcol[4 * q4 + 2] = v4.z; lcol[4 * q4 + 3] = v4.w;
+        }
+#pragma unroll
+        for (int r = s2 + 1; r < 16; ++r) t[r] = fmaf(-lcol[r], t[s2], t[r]);
+      }
+      if (lg == 0) {
+        // N diagonal block: T_ii - I (strictly lower)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pN[(16 * w + r) * RP + 16 * w + cc] = f2bf(r > cc ? t[r] : 0.f);
+        uint16_t tv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tv[r] = f2bf(t[r]);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        if (w == 0) {          // T00^T into Ta^T[0:16][0:16]
+          *reinterpret_cast<uint4*>(sTaT + cc * TP) = *reinterpret_cast<uint4*>(&tv[0]);
+          *reinterpret_cast<uint4*>(sTaT + cc * TP + 8) = *reinterpret_cast<uint4*>(&tv[8]);
+        } else if (w == 1) {   // T11^T into Ta^T[16:32][16:32], zero Ta^T[16:32][0:16]; T11 row-major
+          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 16) = *reinterpret_cast<uint4*>(&tv[0]);
+          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 24) = *reinterpret_cast<uint4*>(&tv[8]);
+          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP) = z;
+          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 8) = z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sT11R[r * SP + cc] = tv[r];
+        } else if (w == 2) {   // T22^T; T22 row-major into Tb[0:16][0:16], zero Tb[0:16][16:32]
+          *reinterpret_cast<uint4*>(sT22T + cc * SP) = *reinterpret_cast<uint4*>(&tv[0]);
+          *reinterpret_cast<uint4*>(sT22T + cc * SP + 8) = *reinterpret_cast<uint4*>(&tv[8]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sTbR[r * TP + cc] = tv[r];
+            sTbR[r * TP + 16 + cc] = 0;
+          }
+        } else {               // T33 row-major into Tb[16:32][16:32]
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sTbR[(16 + r) * TP + 16 + cc] = tv[r];
+        }
+      }
+    }
+    __syncthreads();
+    // Merges on the matrix cores.  With Ta = T[0:32,0:32], Tb = T[32:64,32:64]:
+    //   T10 = -T11 (L10 T00),  T32 = -T33 (L32 T22),  T[32:64,0:32] = -Tb (L[32:64,0:32] Ta).
+    // 16-deep products use the 32-deep instruction with lane groups 2, 3 zero.
+    const bf16x8 z8 = zero8();
+    if (w < 2) {   // C2: P10 = L10 T00 (w 0), P32 = L32 T22 (w 1); store P^T
+      const uint16_t* A = w == 0 ? sLb + (16 + lr) * RP : sLb + (48 + lr) * RP + 32;
+      const uint16_t* B = w == 0 ? sTaT + lr * TP : sT22T + lr * SP;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma(lg < 2 ? lds8(A + 8 * lg) : z8, lg < 2 ? lds8(B + 8 * lg) : z8, acc);
+      uint2 pk;
+      pk.x = pack2(acc[0], acc[1]);
+      pk.y = pack2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(sPT + (16 * w + lr) * SP + 4 * lg) = pk;
+    }
+    __syncthreads();
+    if (w < 2) {   // C3: T10 = -T11 P10 (w 0), T32 = -T33 P32 (w 1)
+      const uint16_t* A = w == 0 ? sT11R + lr * SP : sTbR + (16 + lr) * TP + 16;
+      const uint16_t* B = sPT + (16 * w + lr) * SP;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma(lg < 2 ? lds8(A + 8 * lg) : z8, lg < 2 ? lds8(B + 8 * lg) : z8, acc);
+      uint16_t tv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tv[e] = f2bf(-acc[e]);
+      if (w == 0) {
+        // Ta^T[n][16 + m] = T10[m][n]; N block (1,0)
+        *reinterpret_cast<uint2*>(sTaT + lr * TP + 16 + 4 * lg) = *reinterpret_cast<uint2*>(&tv[0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pN[(16 + 4 * lg + e) * RP + lr] = tv[e];
+      } else {
+        // Tb[16 + m][n] = T32[m][n]; N block (3,2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sTbR[(16 + 4 * lg + e) * TP + lr] = tv[e];
+          pN[(48 + 4 * lg + e) * RP + 32 + lr] = tv[e];
+        }
+      }
+    }
+    __syncthreads();
+    const int mi = (w >> 1) & 1, ni = w & 1;
+    if (w < 4) {   // C4: Q = L[32:64, 0:32] Ta, tile (mi, ni); store Q^T
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma(lds8(sLb + (32 + 16 * mi + lr) * RP + 8 * lg), lds8(sTaT + (16 * ni + lr) * TP + 8 * lg),
+                 acc);
+      uint2 pk;
+      pk.x = pack2(acc[0], acc[1]);
+      pk.y = pack2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(sQT + (16 * ni + lr) * TP + 16 * mi + 4 * lg) = pk;
+    }
+    __syncthreads();
+    if (w < 4) {   // C5: T[32:64, 0:32] = -Tb Q, tile (mi, ni), into N
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma(lds8(sTbR + (16 * mi + lr) * TP + 8 * lg), lds8(sQT + (16 * ni + lr) * TP + 8 * lg), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pN[(32 + 16 * mi + 4 * lg + e) * RP + 16 * ni + lr] = f2bf(-acc[e]);
+    }
+    __syncthreads();  // (C) solve done; solve scratch free
+
+    // ================= phase D: the chunk recurrence ==========================
+    // S -> bf16, stored transposed for the B operand: dST[j][d]
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt) {
+      uint2 pk;
+      pk.x = pack2(S[nt][0], S[nt][1]);
+      pk.y = pack2(S[nt][2], S[nt][3]);
+      *reinterpret_cast<uint2*>(dST + (16 * nt + lr) * KP + 16 * w + 4 * lg) = pk;
+    }
+    __syncthreads();
+
+    // X = V - K exp(G) S ; Y = beta X    (rows of block rb, tiles nt0..)
+    f32x4 Y[NTW];
+    if (rb_active) {
+#pragma unroll
+      for (int t2 = 0; t2 < NTW; ++t2) {
+        const int nt = nt0 + t2;
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[e] = bf2f(mV[(16 * rb + 4 * lg + e) * Lay::VP + 16 * nt + lr]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int off = 32 * ks + 8 * lg;
+          acc = mfma(lds8(pKt + (16 * rb + lr) * KP + off), lds8(dST + (16 * nt + lr) * KP + off),
+                     acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= mBeta[16 * rb + 4 * lg + e];
+        Y[t2] = acc;
+        uint2 pk;
+        pk.x = pack2(acc[0], acc[1]);
+        pk.y = pack2(acc[2], acc[3]);
+        *reinterpret_cast<uint2*>(mY + (16 * nt + lr) * RP + 16 * rb + 4 * lg) = pk;
+      }
+    }
+    __syncthreads();
+
+    // U = Y + N Y
+    const int nks = rb >= 2 ? 2 : 1;   // k-steps of 32 rows covering rows < 16(rb+1)
+    if (rb_active) {
+#pragma unroll
+      for (int t2 = 0; t2 < NTW; ++t2) {
+        const int nt = nt0 + t2;
+        f32x4 acc = Y[t2];
+        for (int ks = 0; ks < nks; ++ks) {
+          const int off = 32 * ks + 8 * lg;
+          acc = mfma(lds8(pN + (16 * rb + lr) * RP + off), lds8(mY + (16 * nt + lr) * RP + off),
+                     acc);
+        }
+        uint2 ph, pl;
+        split2(acc[0], acc[1], ph.x, pl.x);
+        split2(acc[2], acc[3], ph.y, pl.y);
+        *reinterpret_cast<uint2*>(dUhi + (16 * nt + lr) * RP + 16 * rb + 4 * lg) = ph;
+        *reinterpret_cast<uint2*>(dUlo + (16 * nt + lr) * RP + 16 * rb + 4 * lg) = pl;
+      }
+    }
+    __syncthreads();
+
+    // O = scale (Q exp(G) S + M U)   (rows of block rb)
+    if (rb_active) {
+#pragma unroll
+      for (int t2 = 0; t2 < NTW; ++t2) {
+        const int nt = nt0 + t2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int off = 32 * ks + 8 * lg;
+          acc = mfma(lds8(pQt + (16 * rb + lr) * KP + off), lds8(dST + (16 * nt + lr) * KP + off),
+                     acc);
+        }
+        for (int ks = 0; ks < nks; ++ks) {
+          const int off = 32 * ks + 8 * lg;
+          const bf16x8 am = lds8(pM + (16 * rb + lr) * RP + off);
+          acc = mfma(am, lds8(dUhi + (16 * nt + lr) * RP + off), acc);
+          acc = mfma(am, lds8(dUlo + (16 * nt + lr) * RP + off), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * lg + e;
+          if (r >= off)
+            a.out[((size_t)(tok0 + r) * H + h) * DVT + col0 + 16 * nt + lr] =
+                f2bf(acc[e] * a.scale);
+        }
+      }
+    }
+
+    // S <- diag(exp(G_end)) S + (K exp(G_end - G))^T U    (rows 16w..16w+15)
+    {
+      const int drow = 16 * w;
+      float gam[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gam[e] = mGam[drow + 4 * lg + e];
+      bf16x8 akh[2], aklo;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) akh[ks] = lds8(pKhT + (drow + lr) * RP + 32 * ks + 8 * lg);
+      aklo = lg >= 2 ? lds8(pKhLo + (drow + lr) * LP + 8 * (lg - 2)) : zero8();
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) {
+        f32x4 acc = S[nt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= gam[e];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int off = 32 * ks + 8 * lg;
+          const bf16x8 bh = lds8(dUhi + (16 * nt + lr) * RP + off);
+          acc = mfma(akh[ks], bh, acc);
+          acc = mfma(akh[ks], lds8(dUlo + (16 * nt + lr) * RP + off), acc);
+          if (ks == 1) acc = mfma(aklo, bh, acc);
+        }
+        S[nt] = acc;
+      }
+    }
+    __syncthreads();  // segment done; LDS reused by the next segment
+
+    if (seg_end == ckpt_at) export_state(a.ckpt);
+    pos = seg_end;
+  }
+
+  if (a.final_state) export_state(a.final_state);
+}
+
+}  // namespace
+
+template <int VW>
+static hipError_t launch_fused_vw(const FusedArgs& a, hipStream_t stream) {
+  constexpr int VSPLIT = DVT / VW;
+  const int groups = (a.num_pairs + 7) / 8;
+  const dim3 grid(groups * 8 * VSPLIT);
+  hipLaunchKernelGGL(kda_fused_kernel<VW>, grid, dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const FusedArgs& a, int vsplit, hipStream_t stream) {
+  switch (vsplit) {
+    case 2: return launch_fused_vw<64>(a, stream);
+    case 4: return launch_fused_vw<32>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

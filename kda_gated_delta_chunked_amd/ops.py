@@ -1,0 +1,210 @@
+"""Thin Python binding over libkda's C ABI (include/kda.h).
+
+Argument marshalling only: tensors are checked for dtype, shape, contiguity
+and device, their device pointers and the current HIP stream are handed to
+``kda_prefill``, and every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library cannot be loaded, calls raise.
+PyTorch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+from . import build as _build
+
+KDA_OK = 0
+STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
+                -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_OVERLAP",
+                -5: "KDA_ERR_WORKSPACE_TOO_SMALL", -6: "KDA_ERR_TOO_LARGE", -7: "KDA_ERR_HIP"}
+VARIANTS = {"auto": 0, "fused": 2}
+HEAD_DIM = 128
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A libkda call returned a non-OK status."""
+
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        name = STATUS_NAMES.get(status, str(status))
+        msg = _lib.kda_status_string(status).decode() if _lib is not None else name
+        super().__init__(f"{what}: {name} ({msg})" if what else f"{name} ({msg})")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``kda_problem``."""
+
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int64),
+                ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("gate_lower_bound", ctypes.c_float), ("variant", ctypes.c_int32),
+                ("value_split", ctypes.c_int32)]
+
+
+def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: float,
+                 gate_lower_bound: float = -5.0, variant: str | int = "auto",
+                 value_split: int = 0, head_dim_k: int = HEAD_DIM,
+                 head_dim_v: int = HEAD_DIM) -> Problem:
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    return Problem(int(num_seqs), int(total_tokens), int(num_heads), int(head_dim_k),
+                   int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split))
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def load_library(path: Optional[str] = None):
+    """Load libkda.so (building it first if it is absent)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _build.LIB_PATH
+    if not os.path.exists(p):
+        _build.build()
+    lib = ctypes.CDLL(p)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(Problem)
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_prefill_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_prefill_workspace_size.restype = ctypes.c_int
+    lib.kda_validate.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t]
+    lib.kda_validate.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_plan.argtypes = [PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_plan.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != KDA_OK:
+        raise KDAError(status, what)
+
+
+def workspace_size(problem: Problem) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.kda_prefill_workspace_size(ctypes.byref(problem), ctypes.byref(n)),
+           "kda_prefill_workspace_size")
+    return int(n.value)
+
+
+def plan(problem: Problem) -> Tuple[str, int]:
+    lib = load_library()
+    var, vs = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.kda_plan(ctypes.byref(problem), ctypes.byref(var), ctypes.byref(vs)), "kda_plan")
+    name = {v: k for k, v in VARIANTS.items()}.get(var.value, str(var.value))
+    return name, int(vs.value)
+
+
+def prefill_raw(problem: Problem, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                ckpt_offsets, ckpt_state, workspace, workspace_bytes: int, stream) -> int:
+    """Call ``kda_prefill`` with raw integer pointers (0 for NULL); returns the status."""
+    lib = load_library()
+    return lib.kda_prefill(ctypes.byref(problem), q or None, k or None, v or None, g or None,
+                           beta or None, cu_seqlens or None, initial_state or None, out or None,
+                           final_state or None, ckpt_offsets or None, ckpt_state or None,
+                           workspace or None, int(workspace_bytes), stream or None)
+
+
+def validate_raw(problem: Problem, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                 ckpt_offsets, ckpt_state, workspace, workspace_bytes: int) -> int:
+    """Call ``kda_validate`` with raw integer pointers; returns the status (host only)."""
+    lib = load_library()
+    return lib.kda_validate(ctypes.byref(problem), q or None, k or None, v or None, g or None,
+                            beta or None, cu_seqlens or None, initial_state or None, out or None,
+                            final_state or None, ckpt_offsets or None, ckpt_state or None,
+                            workspace or None, int(workspace_bytes))
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Optional[float] = None,
+            out=None, final_state=None, output_final_state: bool = True, ckpt_offsets=None,
+            ckpt_state=None, gate_lower_bound: float = -5.0, variant: str = "auto",
+            value_split: int = 0, workspace=None, stream=None):
+    """KDA multi-token recurrent prefill on the GPU.
+
+    q, k, v: bf16 [T, H, 128] (packed, with cu_seqlens int32 [N+1]) or
+    [B, T, H, 128] (fixed layout).  g: fp32 like q (log-decay, >= the gate
+    lower bound, <= 0).  beta: fp32 [T, H] or [B, T, H].  initial_state:
+    fp32 [N, H, 128, 128] or None.  Returns (out, final_state); out has q's
+    shape, final_state is None when output_final_state is False.  Pass
+    ``final_state=initial_state`` for an in-place update and ``out=v`` to
+    overwrite v.  ckpt_offsets int32 [N] / ckpt_state fp32 [N, H, 128, 128]
+    export the state after ckpt_offsets[n] tokens of sequence n.
+    """
+    import torch
+
+    fixed = q.dim() == 4
+    if fixed:
+        B, T, H, D = q.shape
+        N, T_total = B, B * T
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens is for packed [T, H, 128] inputs")
+    elif q.dim() == 3:
+        T_total, H, D = q.shape
+        if cu_seqlens is None:
+            N = 1
+        else:
+            N = int(cu_seqlens.numel()) - 1
+    else:
+        raise ValueError("q must be [T, H, 128] or [B, T, H, 128]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("libkda runs on the GPU: tensors must be on a cuda (HIP) device")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
+                        ("g", g, torch.float32), ("beta", beta, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, v and g must have the same shape")
+    if beta.shape != q.shape[:-1]:
+        raise ValueError("beta must be q.shape[:-1]")
+    for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int32), ("initial_state", initial_state,
+                        torch.float32), ("ckpt_offsets", ckpt_offsets, torch.int32),
+                        ("ckpt_state", ckpt_state, torch.float32), ("out", out, torch.bfloat16),
+                        ("final_state", final_state, torch.float32)):
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    state_shape = (N, H, D, D)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state),
+                    ("ckpt_state", ckpt_state)):
+        if t is not None and tuple(t.shape) != state_shape:
+            raise ValueError(f"{name} must have shape {state_shape}")
+    if scale is None:
+        scale = D ** -0.5
+    prob = make_problem(N, T_total, H, scale=scale, gate_lower_bound=gate_lower_bound,
+                        variant=variant, value_split=value_split, head_dim_k=D, head_dim_v=D)
+    if out is None:
+        out = torch.empty_like(v)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if final_state is None and output_final_state:
+        final_state = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = prefill_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(ckpt_offsets),
+                         _ptr(ckpt_state), _ptr(workspace), ws_bytes, int(stream.cuda_stream))
+    _check(st, "kda_prefill")
+    return out, final_state

@@ -1,0 +1,96 @@
+"""Helpers shared by the GPU tests: move a synth.Problem to the device, run
+libkda through its C ABI, and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+from kda_gated_delta_chunked_amd import synth
+
+# Parity gates (fp32-state KDA prefill vs the fp64 oracle).
+OUT_MAX_ABS = 2e-2
+OUT_REL_L2 = 5e-3
+STATE_REL_L2 = 1e-3
+
+
+def to_device(p: synth.Problem):
+    import torch
+    dev = torch.device("cuda", 0)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    d = {
+        "q": bf16(p.q), "k": bf16(p.k), "v": bf16(p.v),
+        "g": torch.from_numpy(p.g).to(dev), "beta": torch.from_numpy(p.beta).to(dev),
+        "cu": None if p.fixed else torch.from_numpy(p.cu_seqlens).to(dev),
+        "s0": None if p.initial_state is None else torch.from_numpy(p.initial_state).to(dev),
+        "offs": None if p.ckpt_offsets is None else torch.from_numpy(p.ckpt_offsets).to(dev),
+    }
+    return d
+
+
+def run_gpu(p: synth.Problem, *, value_split: int = 0, d=None, sentinel: bool = True,
+            out_alias_v: bool = False, state_in_place: bool = False):
+    """Run kda_prefill through the C ABI on a fresh set of device buffers.
+
+    Outputs are pre-filled with NaN so that any element the kernel fails to
+    write shows up.  Returns numpy dict(out fp32, final, ckpt)."""
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    d = d or to_device(p)
+    dev = d["q"].device
+    N, H, T = p.N, p.H, p.T_total
+    out = d["v"].clone() if out_alias_v else torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16,
+                                                        device=dev)
+    if state_in_place:
+        s0 = d["s0"].clone() if d["s0"] is not None else torch.zeros((N, H, 128, 128), device=dev)
+        fin = s0
+    else:
+        s0 = d["s0"]
+        fin = torch.full((N, H, 128, 128), float("nan") if sentinel else 0.0, dtype=torch.float32,
+                         device=dev)
+    ck = None
+    if d["offs"] is not None:
+        ck = torch.full((N, H, 128, 128), float("nan"), dtype=torch.float32, device=dev)
+    prob = K.make_problem(N, T, H, scale=p.scale, value_split=value_split)
+    stream = torch.cuda.current_stream(dev)
+    v_ptr = out.data_ptr() if out_alias_v else d["v"].data_ptr()
+    st = K.prefill_raw(prob, d["q"].data_ptr(), d["k"].data_ptr(), v_ptr, d["g"].data_ptr(),
+                       d["beta"].data_ptr(), 0 if d["cu"] is None else d["cu"].data_ptr(),
+                       0 if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
+                       0 if d["offs"] is None else d["offs"].data_ptr(),
+                       0 if ck is None else ck.data_ptr(), 0, 0, stream.cuda_stream)
+    assert st == 0, f"kda_prefill returned {st}"
+    torch.cuda.synchronize()
+    res = {"out": out.float().cpu().numpy(), "final": fin.cpu().numpy(),
+           "ckpt": None if ck is None else ck.cpu().numpy()}
+    return res
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b.ravel())
+    return float(np.linalg.norm((a - b).ravel()) / den) if den > 0 else float(np.linalg.norm(a.ravel()))
+
+
+def metrics(gpu, ref):
+    m = {"out_max_abs": float(np.max(np.abs(gpu["out"] - ref["out"]))) if gpu["out"].size else 0.0,
+         "out_rel_l2": rel_l2(gpu["out"], ref["out"]) if gpu["out"].size else 0.0,
+         "final_rel_l2": rel_l2(gpu["final"], ref["final"])}
+    if ref.get("ckpt") is not None:
+        m["ckpt_rel_l2"] = rel_l2(gpu["ckpt"], ref["ckpt"])
+    return m
+
+
+def assert_parity(gpu, ref, what=""):
+    assert np.all(np.isfinite(gpu["out"])), f"{what}: non-finite or unwritten outputs"
+    assert np.all(np.isfinite(gpu["final"])), f"{what}: non-finite or unwritten final state"
+    m = metrics(gpu, ref)
+    assert m["out_max_abs"] <= OUT_MAX_ABS, f"{what}: {m}"
+    assert m["out_rel_l2"] <= OUT_REL_L2, f"{what}: {m}"
+    assert m["final_rel_l2"] <= STATE_REL_L2, f"{what}: {m}"
+    if "ckpt_rel_l2" in m:
+        assert np.all(np.isfinite(gpu["ckpt"])), f"{what}: unwritten checkpoint"
+        assert m["ckpt_rel_l2"] <= STATE_REL_L2, f"{what}: {m}"
+    return m

@@ -1,0 +1,140 @@
+"""GPU parity: libkda (through its C ABI) against the fp64 token-by-token oracle.
+
+Gates: output max-abs <= 2e-2 and relative L2 <= 5e-3; final and checkpoint
+state relative L2 <= 1e-3.  Checkpoint placement and cu_seqlens handling are
+checked exactly (bitwise where the arithmetic allows it: offset 0 exports the
+initial state, a zero-length sequence keeps it, offset L equals the final
+state).  Outputs are NaN-filled before each call so unwritten elements fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_parity, metrics, run_gpu, to_device
+from kda_gated_delta_chunked_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, m):
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.3e}" for k, v in m.items()), flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kda_gated_delta_chunked_amd as K
+    K.load_library()
+
+
+@pytest.mark.parametrize("vsplit", [2, 4])
+def test_one_chunk_h1(vsplit):
+    p = synth.workload("b1_t64_h1")
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, value_split=vsplit)
+    _report(f"b1_t64_h1 vs{vsplit}", assert_parity(gpu, ref, "b1_t64_h1"))
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 33, 63, 64, 65, 129, 200])
+def test_tails_fixed(T):
+    p = synth.make_problem([T, T], 2, seed=100 + T, fixed=True, init_state=True)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p)
+    _report(f"fixed B2 T{T}", assert_parity(gpu, ref, f"T={T}"))
+
+
+@pytest.mark.parametrize("vsplit", [2, 4])
+def test_packed_ragged_with_empty_and_ckpt(vsplit):
+    lens = [130, 0, 64, 1, 257, 0, 33]
+    offs = [77, 0, 64, 1, 128, 0, 5]
+    p = synth.make_problem(lens, 3, seed=7, init_state=True, ckpt=offs)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, value_split=vsplit)
+    _report(f"packed ragged vs{vsplit}", assert_parity(gpu, ref, "packed"))
+    # zero-length sequences keep the initial state bit for bit; offset 0 exports it
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(gpu["final"][n], p.initial_state[n])
+        if offs[n] == 0:
+            assert np.array_equal(gpu["ckpt"][n], p.initial_state[n])
+        if offs[n] == L:
+            assert np.array_equal(gpu["ckpt"][n], gpu["final"][n])
+
+
+def test_checkpoint_offsets_exact():
+    # every offset position class: start, inside first chunk, chunk boundary,
+    # inside a later chunk, end; plus out of range (slot untouched)
+    L = 200
+    offs = [0, 1, 37, 63, 64, 65, 128, 199, 200, 201, -1]
+    p = synth.make_problem([L] * len(offs), 2, seed=9, init_state=True, ckpt=offs)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p)
+    for n, off in enumerate(offs):
+        if 0 <= off <= L:
+            assert np.all(np.isfinite(gpu["ckpt"][n])), f"offset {off} not exported"
+            e = np.linalg.norm(gpu["ckpt"][n] - ref["ckpt"][n]) / np.linalg.norm(ref["ckpt"][n])
+            assert e <= 1e-3, (off, e)
+            # off-by-one detector: closer to S_off than to S_{off +- 1}
+            for other in (off - 1, off + 1):
+                if 0 <= other <= L:
+                    pr = oracle.prefill(p.q[n * L:(n + 1) * L], p.k[n * L:(n + 1) * L],
+                                        p.v[n * L:(n + 1) * L], p.g[n * L:(n + 1) * L],
+                                        p.beta[n * L:(n + 1) * L], scale=p.scale, num_seqs=1,
+                                        initial_state=p.initial_state[n:n + 1],
+                                        ckpt_offsets=np.array([other], np.int32))
+                    e2 = np.linalg.norm(gpu["ckpt"][n] - pr["ckpt"][0]) / np.linalg.norm(pr["ckpt"][0])
+                    assert e2 > 10 * e, (off, other, e, e2)
+        else:
+            assert np.all(np.isnan(gpu["ckpt"][n])), f"offset {off} must export nothing"
+    # exporting a checkpoint does not change the outputs beyond rounding
+    m = metrics(gpu, ref)
+    assert m["out_rel_l2"] <= 5e-3 and m["final_rel_l2"] <= 1e-3
+
+
+def test_gate_extremes_and_beta_zero():
+    # g at the lower bound (-5): everything decays fast, normal gates apply
+    p = synth.make_problem([300, 70], 2, seed=11, init_state=True, gate="min")
+    ref = oracle.prefill_problem(p)
+    _report("gate=min", assert_parity(run_gpu(p), ref, "gate=min"))
+    # g = 0: nothing decays, so the bf16 rounding of the state operand in
+    # V - K exp(G) S, of N and of Y accumulates over all 370 tokens instead of
+    # being forgotten.  The rounding model of the kernel (tests/chunked_model.py,
+    # emulate=True with the kernel's recipe) predicts a final-state relative L2
+    # of 9.85e-4 on this input; the bound for this degenerate gate is 2e-3.
+    p = synth.make_problem([300, 70], 2, seed=11, init_state=True, gate="zero")
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p)
+    m = metrics(gpu, ref)
+    _report("gate=zero", m)
+    assert m["out_rel_l2"] <= 5e-3 and m["out_max_abs"] <= 2e-2 and m["final_rel_l2"] <= 2e-3, m
+    # beta = 0 and g = 0: the state must come back unchanged, bit for bit
+    p = synth.make_problem([150], 2, seed=12, init_state=True, gate="zero", beta_mode="zero")
+    gpu = run_gpu(p)
+    assert np.array_equal(gpu["final"], p.initial_state)
+    ref = oracle.prefill_problem(p)
+    assert_parity(gpu, ref, "beta=0")
+
+
+def test_aliasing_out_v_and_state_in_place():
+    p = synth.make_problem([190, 64], 2, seed=13, init_state=True)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, out_alias_v=True, state_in_place=True)
+    _report("aliased", assert_parity(gpu, ref, "aliased"))
+
+
+def test_deterministic():
+    p = synth.make_problem([333], 2, seed=14, init_state=True)
+    d = to_device(p)
+    a = run_gpu(p, d=d)
+    b = run_gpu(p, d=d)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["final"], b["final"])
+
+
+@pytest.mark.parametrize("name", ["b1_t8192", "b8_t8192", "packed_32_rand", "ckpt_16_rand"])
+def test_full_size_workloads(name):
+    p = synth.workload(name)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p)
+    _report(name, assert_parity(gpu, ref, name))
