@@ -170,9 +170,14 @@ def chunk_step(S, q, k, v, g, beta, scale, C_end=None, *, emulate=False, recipe=
 
 
 def prefill(q, k, v, g, beta, *, scale, cu_seqlens, initial_state=None, ckpt_offsets=None,
-            chunk=64, emulate=False, recipe=None):
+            chunk=64, emulate=False, recipe=None, ckpt_mode="split"):
     """Chunked prefill over a packed batch.  Inputs as for the oracle, but q/k/v
-    already widened to float.  Returns dict(out, final, ckpt)."""
+    already widened to float.  Returns dict(out, final, ckpt).
+
+    ckpt_mode "split" ends a segment at the checkpoint offset (what the HIP
+    kernel does: the chunk containing the offset is processed as two
+    segments); "masked" keeps the chunk whole and forms the checkpoint from a
+    masked partial state update."""
     T, H, K = q.shape
     V = v.shape[2]
     N = len(cu_seqlens) - 1
@@ -184,14 +189,17 @@ def prefill(q, k, v, g, beta, *, scale, cu_seqlens, initial_state=None, ckpt_off
         bos, eos = int(cu_seqlens[n]), int(cu_seqlens[n + 1])
         L = eos - bos
         p = None if ckpt_offsets is None else int(ckpt_offsets[n])
+        # segment boundaries: multiples of `chunk` from the sequence start, plus p
+        cuts = list(range(0, L, chunk)) + [L]
+        if ckpt_mode == "split" and p is not None and 0 < p < L and p not in cuts:
+            cuts = sorted(cuts + [p])
         for h in range(H):
             S = np.zeros((K, V), dt) if initial_state is None else initial_state[n, h].astype(dt)
             if p == 0:
                 ck[n, h] = S
-            for c0 in range(0, L, chunk):
-                c1 = min(c0 + chunk, L)
+            for c0, c1 in zip(cuts[:-1], cuts[1:]):
                 sl = slice(bos + c0, bos + c1)
-                want = p is not None and c0 < p < c1
+                want = ckpt_mode == "masked" and p is not None and c0 < p < c1
                 res = chunk_step(S, q[sl, h], k[sl, h], v[sl, h], g[sl, h], beta[sl, h], scale,
                                  C_end=(p - c0) if want else None, emulate=emulate, recipe=recipe)
                 out[sl, h] = res[0]

@@ -1,0 +1,159 @@
+"""Host-side checks of libkda's C ABI: the library loads without a GPU, exports
+every entry point include/kda.h declares, and kda_validate / kda_prefill reject
+bad arguments on the host before anything reaches the device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import kda_gated_delta_chunked_amd as K
+from kda_gated_delta_chunked_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, OVERLAP, WS, TOO_LARGE = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.load_library()
+    names = declared_functions()
+    assert {"kda_prefill", "kda_prefill_workspace_size", "kda_validate", "kda_status_string",
+            "kda_plan"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_status_strings():
+    lib = K.load_library()
+    for code in range(-7, 1):
+        s = lib.kda_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.kda_status_string(-99) == b"unknown status"
+
+
+class Bufs:
+    """Fake, 16-byte aligned, non-overlapping host addresses (never dereferenced)."""
+
+    def __init__(self, N=2, T=256, H=4):
+        self.N, self.T, self.H = N, T, H
+        base = 1 << 40
+        sizes = {"q": T * H * 256, "k": T * H * 256, "v": T * H * 256, "g": T * H * 512,
+                 "beta": T * H * 4, "cu": (N + 1) * 4, "s0": N * H * 65536, "out": T * H * 256,
+                 "fin": N * H * 65536, "offs": N * 4, "ck": N * H * 65536}
+        self.addr = {}
+        for k_, sz in sizes.items():
+            self.addr[k_] = base
+            base += (sz + 4095) // 4096 * 4096 + 4096
+
+    def args(self, **over):
+        a = dict(self.addr)
+        a.update(over)
+        return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["s0"], a["out"], a["fin"],
+                a["offs"], a["ck"], 0, 0]
+
+
+def validate(prob, b, **over):
+    return K.validate_raw(prob, *b.args(**over))
+
+
+def prob_for(b, **kw):
+    return K.make_problem(b.N, b.T, b.H, scale=kw.pop("scale", 0.088), **kw)
+
+
+def test_validate_accepts_a_well_formed_call():
+    b = Bufs()
+    assert validate(prob_for(b), b) == OK
+    assert validate(prob_for(b), b, cu=0) == OK           # fixed layout, T divisible by N
+    assert validate(prob_for(b), b, s0=0, fin=0) == OK     # no states
+    assert validate(prob_for(b), b, offs=0, ck=0) == OK    # no checkpoints
+
+
+@pytest.mark.parametrize("bound,want", [(-5.0, OK), (0.0, OK), (-2.5, OK), (-5.01, INVALID),
+                                        (0.01, INVALID), (float("nan"), INVALID),
+                                        (float("-inf"), INVALID)])
+def test_gate_lower_bound_range_is_inclusive(bound, want):
+    b = Bufs()
+    assert validate(prob_for(b, gate_lower_bound=bound), b) == want
+
+
+def test_shapes_and_scalars():
+    b = Bufs()
+    assert validate(prob_for(b, head_dim_k=64), b) == UNSUPPORTED
+    assert validate(prob_for(b, head_dim_v=256), b) == UNSUPPORTED
+    assert validate(prob_for(b, scale=float("inf")), b) == INVALID
+    assert validate(prob_for(b, value_split=3), b) == UNSUPPORTED
+    assert validate(prob_for(b, variant=7), b) == UNSUPPORTED
+    assert validate(K.make_problem(0, 256, 4, scale=0.1), b) == INVALID
+    assert validate(K.make_problem(2, 256, 0, scale=0.1), b) == INVALID
+    assert validate(K.make_problem(3, 256, 4, scale=0.1), Bufs(N=3), cu=0) == INVALID  # 256 % 3
+    assert validate(prob_for(b), b, q=0) == INVALID
+
+
+def test_empty_batch_needs_no_token_buffers():
+    b = Bufs(T=0)
+    p = K.make_problem(2, 0, 4, scale=0.1)
+    assert K.validate_raw(p, 0, 0, 0, 0, 0, b.addr["cu"], b.addr["s0"], 0, b.addr["fin"], 0, 0,
+                          0, 0) == OK
+
+
+def test_alignment():
+    b = Bufs()
+    for name in ("q", "k", "v", "g", "beta", "cu", "s0", "out", "fin", "offs", "ck"):
+        assert validate(prob_for(b), b, **{name: b.addr[name] + 8}) == ALIGN, name
+
+
+def test_overlap_rules():
+    b = Bufs()
+    p = prob_for(b)
+    assert validate(p, b, out=b.addr["v"]) == OK                     # exact alias out == v
+    assert validate(p, b, out=b.addr["v"] + 256) == OVERLAP          # partial
+    assert validate(p, b, out=b.addr["q"]) == OVERLAP
+    assert validate(p, b, fin=b.addr["s0"]) == OK                    # in-place state update
+    assert validate(p, b, fin=b.addr["s0"] + 1024) == OVERLAP
+    assert validate(p, b, ck=b.addr["s0"]) == OVERLAP                # checkpoints never alias
+    assert validate(p, b, ck=b.addr["fin"]) == OVERLAP               # nor the final state
+    assert validate(p, b, fin=b.addr["ck"]) == OVERLAP
+    assert validate(p, b, out=b.addr["g"] + 512) == OVERLAP
+
+
+def test_checkpoint_arguments_are_paired():
+    b = Bufs()
+    assert validate(prob_for(b), b, ck=0) == INVALID
+    assert validate(prob_for(b), b, offs=0) == INVALID
+
+
+def test_int32_flat_output_bound():
+    # T_total * H * 128 must fit in int32: at H = 1024, 16383 tokens pass and 16384 do not
+    for T, want in ((16383, OK), (16384, TOO_LARGE)):
+        b = Bufs(N=1, T=T, H=1024)
+        assert validate(K.make_problem(1, T, 1024, scale=0.1), b) == want
+
+
+def test_prefill_rejects_on_the_host_without_a_device():
+    b = Bufs()
+    st = K.prefill_raw(prob_for(b, head_dim_k=64), *b.args()[:-2], 0, 0, 0)
+    assert st == UNSUPPORTED
+    st = K.prefill_raw(prob_for(b), *b.args(out=b.addr["q"])[:-2], 0, 0, 0)
+    assert st == OVERLAP
+
+
+def test_workspace_size_and_plan_arguments():
+    p = K.make_problem(8, 65536, 12, scale=0.088)
+    assert K.workspace_size(p) == 0
+    with pytest.raises(K.KDAError):
+        K.workspace_size(K.make_problem(8, 65536, 12, scale=0.088, head_dim_k=64))
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        K.prefill(q, q, q, torch.zeros(4, 2, 128), torch.zeros(4, 2))
