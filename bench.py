@@ -117,6 +117,9 @@ def main() -> int:
     ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, --steps times "
+                         "(reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this path runs per (sequence, head) on a single "
@@ -126,6 +129,16 @@ def main() -> int:
     import torch
     import kda_gated_delta_chunked_amd as K
     from kda_gated_delta_chunked_amd import synth
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "steps": args.steps}), flush=True)
+        return 0
 
     p = synth.workload(args.workload)
     dev = torch.device("cuda", 0)

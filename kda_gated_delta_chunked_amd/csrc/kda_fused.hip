@@ -69,14 +69,19 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
 __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
+__device__ __forceinline__ float lo_of(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float hi_of(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 // hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const uint16_t ha = f2bf(a), hb = f2bf(b);
-  hi = (uint32_t)ha | ((uint32_t)hb << 16);
-  lo = pack2(a - bf2f(ha), b - bf2f(hb));
+  hi = pack2(a, b);
+  lo = pack2(a - lo_of(hi), b - hi_of(hi));
 }
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
@@ -92,6 +97,7 @@ __device__ __forceinline__ bf16x8 zero8() {
 template <int VW>
 struct Layout {
   static constexpr int NTILE = VW / 16;
+  static constexpr int VP = VW + 8;                    // bf16 pitch of [64][VW] tiles
   // gate-operand phase (rows x KP bf16)
   static constexpr int G_KF = 0;
   static constexpr int G_QF = G_KF + 64 * KP * 2;
@@ -110,31 +116,29 @@ struct Layout {
   static constexpr int P_N = P_M + 64 * RP * 2;        //  N bf16 [64][RP]
   static constexpr int P_END = P_N + 64 * RP * 2;
   // triangular-solve scratch (after the gate products, before the recurrence)
-  static constexpr int S_LDT = P_END;                  // diag blocks of L, transposed, fp32 [4][16][LDP]
-  static constexpr int S_LB = S_LDT + 4 * 16 * LDP * 4;  // L bf16 [64][RP] (off-diagonal blocks)
+  static constexpr int S_LB = P_END;                   // L bf16 [64][RP] (off-diagonal blocks)
   static constexpr int S_TAT = S_LB + 64 * RP * 2;     // [[T00,0],[T10,T11]]^T bf16 [32][TP]
   static constexpr int S_TBR = S_TAT + 32 * TP * 2;    // [[T22,0],[T32,T33]]   bf16 [32][TP]
   static constexpr int S_T22T = S_TBR + 32 * TP * 2;   // T22^T bf16 [16][SP]
   static constexpr int S_T11R = S_T22T + 16 * SP * 2;  // T11   bf16 [16][SP]
-  static constexpr int S_PT = S_T11R + 16 * SP * 2;    // (L10 T00)^T, (L32 T22)^T bf16 [2][16][SP]
-  static constexpr int S_QT = S_PT + 2 * 16 * SP * 2;  // (L[32:64,0:32] Ta)^T bf16 [32][TP]
-  static constexpr int S_END = S_QT + 32 * TP * 2;
+  static constexpr int S_END = S_T11R + 16 * SP * 2;
   // recurrence scratch (after the solve; aliases the solve scratch)
-  static constexpr int D_ST = P_END;                   // S^T bf16 [VW][KP]
-  static constexpr int D_UHI = D_ST + VW * KP * 2;     // U^T hi [VW][RP]
+  static constexpr int D_UHI = P_END;                  // U^T hi [VW][RP]
   static constexpr int D_ULO = D_UHI + VW * RP * 2;    // U^T lo [VW][RP]
-  static constexpr int D_END = D_ULO + VW * RP * 2;
-  static constexpr int M1 = G_END > S_END ? G_END : S_END;
-  static constexpr int REGION = M1 > D_END ? M1 : D_END;
+  static constexpr int D_Y = D_ULO + VW * RP * 2;      // Y^T bf16 [VW][RP]
+  static constexpr int D_END = D_Y + VW * RP * 2;
+  static_assert(S_END <= G_END && D_END <= G_END, "scratch must fit in the gate-operand region");
   // always-live
-  static constexpr int A_V = (REGION + 15) / 16 * 16;  // V slice bf16 [64][VW+8]
-  static constexpr int VP = VW + 8;
+  static constexpr int A_V = G_END;                    // V slice bf16 [64][VP]
   static constexpr int A_BETA = A_V + 64 * VP * 2;     // [64] fp32
   static constexpr int A_GAM = A_BETA + 64 * 4;        // [128] fp32
   static constexpr int A_BD = A_GAM + DK * 4;          // [4][128] fp32
   static constexpr int A_HALF = A_BD + 4 * DK * 4;     // [8][128] fp32 half-block products
-  static constexpr int A_Y = A_HALF + 8 * DK * 4;      // Y^T bf16 [VW][RP]
-  static constexpr int TOTAL = A_Y + VW * RP * 2;
+  static constexpr int A_LDT = A_HALF + 8 * DK * 4;    // diag blocks of L, transposed, fp32 [4][16][LDP]
+  static constexpr int A_OSTG = A_LDT + 4 * 16 * LDP * 4;  // output staging bf16 [64][VP]
+  static constexpr int A_ST = A_OSTG + 64 * VP * 2;    // S^T bf16 [VW][KP]: the state as a B operand
+  static constexpr int TOTAL = A_ST + VW * KP * 2;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
 // Raw inputs of one segment for one thread of the elementwise role (rows
@@ -178,7 +182,6 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // w is wave-uniform
-  const int lr = l & 15, lg = l >> 4;   // MFMA lane row / lane group
   const int col0 = vs * VW;             // first state column owned
 
   uint16_t* gKf = reinterpret_cast<uint16_t*>(smem + Lay::G_KF);
@@ -194,38 +197,46 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
   uint16_t* pKhLo = reinterpret_cast<uint16_t*>(smem + Lay::P_KHLO);
   uint16_t* pM = reinterpret_cast<uint16_t*>(smem + Lay::P_M);
   uint16_t* pN = reinterpret_cast<uint16_t*>(smem + Lay::P_N);
-  float* sLdT = reinterpret_cast<float*>(smem + Lay::S_LDT);
   uint16_t* sLb = reinterpret_cast<uint16_t*>(smem + Lay::S_LB);
   uint16_t* sTaT = reinterpret_cast<uint16_t*>(smem + Lay::S_TAT);
   uint16_t* sTbR = reinterpret_cast<uint16_t*>(smem + Lay::S_TBR);
   uint16_t* sT22T = reinterpret_cast<uint16_t*>(smem + Lay::S_T22T);
   uint16_t* sT11R = reinterpret_cast<uint16_t*>(smem + Lay::S_T11R);
-  uint16_t* sPT = reinterpret_cast<uint16_t*>(smem + Lay::S_PT);
-  uint16_t* sQT = reinterpret_cast<uint16_t*>(smem + Lay::S_QT);
-  uint16_t* dST = reinterpret_cast<uint16_t*>(smem + Lay::D_ST);
   uint16_t* dUhi = reinterpret_cast<uint16_t*>(smem + Lay::D_UHI);
   uint16_t* dUlo = reinterpret_cast<uint16_t*>(smem + Lay::D_ULO);
+  uint16_t* mY = reinterpret_cast<uint16_t*>(smem + Lay::D_Y);
   uint16_t* mV = reinterpret_cast<uint16_t*>(smem + Lay::A_V);
   float* mBeta = reinterpret_cast<float*>(smem + Lay::A_BETA);
   float* mGam = reinterpret_cast<float*>(smem + Lay::A_GAM);
   float* mBd = reinterpret_cast<float*>(smem + Lay::A_BD);
   float* mHalf = reinterpret_cast<float*>(smem + Lay::A_HALF);
-  uint16_t* mY = reinterpret_cast<uint16_t*>(smem + Lay::A_Y);
+  float* sLdT = reinterpret_cast<float*>(smem + Lay::A_LDT);
+  uint16_t* oStg = reinterpret_cast<uint16_t*>(smem + Lay::A_OSTG);
+  uint16_t* dST = reinterpret_cast<uint16_t*>(smem + Lay::A_ST);
 
   // ---- state: wave w owns rows d in [16w, 16w+16), all VW columns ------------
   // S[nt][e] = S[16w + 4lg + e][col0 + 16nt + lr]
   f32x4 S[NTILE];
   const size_t state_base = (size_t)pair * DK * DVT;
+  {
+    const int lr = l & 15, lg = l >> 4;
 #pragma unroll
-  for (int nt = 0; nt < NTILE; ++nt)
+    for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 16 * w + 4 * lg + e;
-      const int j = col0 + 16 * nt + lr;
-      S[nt][e] = a.s0 ? a.s0[state_base + (size_t)d * DVT + j] : 0.f;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * w + 4 * lg + e;
+        const int j = col0 + 16 * nt + lr;
+        S[nt][e] = a.s0 ? a.s0[state_base + (size_t)d * DVT + j] : 0.f;
+      }
+    // bf16 copy of the state, transposed, as the B operand of the next segment
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt)
+      *reinterpret_cast<uint2*>(dST + (16 * nt + lr) * KP + 16 * w + 4 * lg) =
+          make_uint2(pack2(S[nt][0], S[nt][1]), pack2(S[nt][2], S[nt][3]));
+  }
 
   auto export_state = [&](float* dst) {
+    const int lr = l & 15, lg = l >> 4;
 #pragma unroll
     for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
@@ -241,13 +252,10 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
   // elementwise role: block ib, rows 16ib + 8hb .. +7, channels d0, d0+1
   const int ib = w >> 1;
   const int hb = w & 1;
-  const int d0 = 2 * l;
   // row-block role in the recurrence: block rb, column tiles [nt0, nt0 + NTW)
   const int rb = w & 3;
   const int nt0 = NTILE >= 2 ? (w >> 2) * NTW : 0;
   const bool rb_active = NTILE >= 2 || w < 4;
-  // V-slice piece of this thread
-  const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
   const bool v_thread = tid < 64 * PER_ROW;
 
   // Segment geometry: at most 64 tokens, never crossing a multiple of 64 from
@@ -260,17 +268,22 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     const int64_t ce = (p0 / CH + 1) * CH < len ? (p0 / CH + 1) * CH : len;
     return (ckpt_at > p0 && ckpt_at < ce) ? ckpt_at : ce;
   };
+  const size_t row_stride = (size_t)H * DK;   // elements between consecutive tokens
   auto load_segment = [&](int64_t p0, SegmentLoads& L) {
+    const int d0 = 2 * l;
+    const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
     const int off = CH - (int)(seg_end_of(p0) - p0);
     const int64_t t0 = bos + p0 - off;
+    const int r0 = 16 * ib + 8 * hb;
+    // rows before `off` belong to the previous segment or sequence: zero
+    const size_t e0 = ((size_t)(t0 + r0) * H + h) * DK + d0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int r = 16 * ib + 8 * hb + e;
-      if (r >= off) {
-        const size_t base = ((size_t)(t0 + r) * H + h) * DK + d0;
-        L.g[e] = *reinterpret_cast<const float2*>(a.g + base);
-        L.k[e] = *reinterpret_cast<const uint32_t*>(a.k + base);
-        L.q[e] = *reinterpret_cast<const uint32_t*>(a.q + base);
+      if (r0 + e >= off) {
+        const size_t o = e0 + (size_t)e * row_stride;
+        L.g[e] = *reinterpret_cast<const float2*>(a.g + o);
+        L.k[e] = *reinterpret_cast<const uint32_t*>(a.k + o);
+        L.q[e] = *reinterpret_cast<const uint32_t*>(a.q + o);
       } else {
         L.g[e] = make_float2(0.f, 0.f);
         L.k[e] = 0u;
@@ -282,38 +295,19 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       L.v = *reinterpret_cast<const uint4*>(a.v + ((size_t)(t0 + vr) * H + h) * DVT + col0 + 8 * vc8);
     L.beta = (tid < 64 && tid >= off) ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
   };
-
-  SegmentLoads ld;
-  int64_t pos = 0;
-  if (pos < len) load_segment(pos, ld);
-  while (pos < len) {
-    const int64_t seg_end = seg_end_of(pos);
-    const int c = (int)(seg_end - pos);
-    const int off = CH - c;
-    const int64_t tok0 = bos + pos - off;
-    // per-iteration copies of the lane coordinates: keeps the compiler from
-    // hoisting every derived LDS address out of the segment loop
-    int lane_it = l;
-    asm volatile("" : "+v"(lane_it));
-    const int lr = lane_it & 15, lg = lane_it >> 4, d0 = 2 * lane_it;
-    const int vr = (64 * w + lane_it) / PER_ROW, vc8 = (64 * w + lane_it) % PER_ROW;
-
-    // ================= phase A: gate factors and gate-product operands ========
-    if (v_thread) *reinterpret_cast<uint4*>(mV + vr * Lay::VP + 8 * vc8) = ld.v;
-    if (tid < 64) mBeta[tid] = ld.beta;
-    float kk[8][2], qq[8][2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kk[e][0] = __uint_as_float(ld.k[e] << 16); kk[e][1] = __uint_as_float(ld.k[e] & 0xffff0000u);
-      qq[e][0] = __uint_as_float(ld.q[e] << 16); qq[e][1] = __uint_as_float(ld.q[e] & 0xffff0000u);
-    }
-    // exp(g); prefix (Ef) and suffix (Eb) products within this half block
-    float Ef[8][2], Eb[8][2];
+  // Gate factors of a segment, first half: exp(g), prefix (Ef) and suffix (Eb)
+  // products inside this thread's half block, the half-block product to LDS,
+  // and the segment's V slice and beta to LDS.  Second half (after a barrier):
+  // combine with the other half block and publish the block decays.
+  float Ef[8][2], Eb[8][2];
+  auto gate_factors_1 = [&](const SegmentLoads& L) {
+    const int d0 = 2 * l;
+    const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
       float ex[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ex[e] = __expf(ch ? ld.g[e].y : ld.g[e].x);
+      for (int e = 0; e < 8; ++e) ex[e] = __expf(ch ? L.g[e].y : L.g[e].x);
       float run = 1.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) { run *= ex[e]; Ef[e][ch] = run; }
@@ -322,21 +316,62 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       for (int e = 7; e >= 0; --e) { Eb[e][ch] = run; run *= ex[e]; }
     }
     *reinterpret_cast<float2*>(mHalf + (2 * ib + hb) * DK + d0) = make_float2(Ef[7][0], Ef[7][1]);
-    __syncthreads();  // (1) half-block products visible
-    {
-      const float2 other = *reinterpret_cast<const float2*>(mHalf + (2 * ib + (1 - hb)) * DK + d0);
-      if (hb == 0)
-        *reinterpret_cast<float2*>(mBd + ib * DK + d0) =
-            make_float2(Ef[7][0] * other.x, Ef[7][1] * other.y);
-      // complete the in-block products: Ef_r = exp(G_r - G_{16ib-1}), Eb_r = exp(G_{16ib+15} - G_r)
+    (void)vr; (void)vc8;
+  };
+  auto stage_v_beta = [&](const SegmentLoads& L) {
+    const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
+    if (v_thread) *reinterpret_cast<uint4*>(mV + vr * Lay::VP + 8 * vc8) = L.v;
+    if (tid < 64) mBeta[tid] = L.beta;
+  };
+  auto gate_factors_2 = [&]() {
+    const int d0 = 2 * l;
+    const float2 other = *reinterpret_cast<const float2*>(mHalf + (2 * ib + (1 - hb)) * DK + d0);
+    if (hb == 0)
+      *reinterpret_cast<float2*>(mBd + ib * DK + d0) =
+          make_float2(Ef[7][0] * other.x, Ef[7][1] * other.y);
+    // Ef_r = exp(G_r - G_{16ib-1}), Eb_r = exp(G_{16ib+15} - G_r)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (hb == 1) { Ef[e][0] *= other.x; Ef[e][1] *= other.y; }
-        else { Eb[e][0] *= other.x; Eb[e][1] *= other.y; }
-      }
+    for (int e = 0; e < 8; ++e) {
+      if (hb == 1) { Ef[e][0] *= other.x; Ef[e][1] *= other.y; }
+      else { Eb[e][0] *= other.x; Eb[e][1] *= other.y; }
     }
-    __syncthreads();  // (2) block decays visible
+  };
+  // store the staged output tile of a finished segment (rows >= off_prev,
+  // token tok0_prev + row) with 16-byte stores
+  auto flush_out = [&](int off_prev, int64_t tok0_prev) {
+    const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
+    if (v_thread && vr >= off_prev)
+      *reinterpret_cast<uint4*>(a.out + ((size_t)(tok0_prev + vr) * H + h) * DVT + col0 + 8 * vc8) =
+          *reinterpret_cast<const uint4*>(oStg + vr * Lay::VP + 8 * vc8);
+  };
+  int pending_off = -1;        // staged output of the previous segment, if any
+  int64_t pending_tok0 = 0;
 
+  SegmentLoads ld;
+  int64_t pos = 0;
+  if (pos < len) {
+    load_segment(pos, ld);
+    gate_factors_1(ld);
+    stage_v_beta(ld);
+    __syncthreads();
+    gate_factors_2();
+    __syncthreads();
+  }
+  while (pos < len) {
+    const int64_t seg_end = seg_end_of(pos);
+    const int c = (int)(seg_end - pos);
+    const int off = CH - c;
+    const int64_t tok0 = bos + pos - off;
+    const bool has_next = seg_end < len;
+    // per-iteration copies of the lane coordinates: keeps the compiler from
+    // hoisting every derived LDS address out of the segment loop
+    int lane_it = l;
+    asm volatile("" : "+v"(lane_it));
+    const int lr = lane_it & 15, lg = lane_it >> 4, d0 = 2 * lane_it;
+
+    // ================= phase A: gate-product operands =========================
+    // (this segment's Ef, Eb, block decays, V and beta were prepared during the
+    // previous segment's recurrence)
     float cref[2], Pend[2], rbd[2], W1[2], W2[2];
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
@@ -350,13 +385,12 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         if (m > ib) pe *= bd[m];
       }
       cref[ch] = cr; Pend[ch] = pe;
-      rbd[ch] = 1.f / bd[ib];
+      rbd[ch] = __builtin_amdgcn_rcpf(bd[ib]);   // ~1 ulp; feeds hi+lo operands
       // block 0 rows feed blocks 2 and 3 (factors bd1 and bd1*bd2); block 1 rows feed block 3 (bd2)
       W1[ch] = ib == 0 ? bd[1] : bd[2];
       W2[ch] = bd[1] * bd[2];
       if (ib == 0 && hb == 0) mGam[d0 + ch] = bd[0] * bd[1] * bd[2] * bd[3];
     }
-    // gate-product operands; keep the fp32 pieces for the prepared operands
     // kept for the prepared operands after the gate products: K exp(G) and
     // Q exp(G) as bf16 pairs (their block-start factor is applied later and
     // they only feed bf16 operands), K exp(G_end - G) in fp32 (its last rows
@@ -367,12 +401,16 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     for (int e = 0; e < 8; ++e) {
       const int rl = 8 * hb + e;        // row within the block
       const int r = 16 * ib + rl;
+      // k, q of this segment are still in the prefetch registers (the next
+      // prefetch is issued only after this phase)
+      const float kk[2] = {lo_of(ld.k[e]), hi_of(ld.k[e])};
+      const float qq[2] = {lo_of(ld.q[e]), hi_of(ld.q[e])};
       float kf[2], qf[2];
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        kf[ch] = kk[e][ch] * Ef[e][ch];
-        qf[ch] = qq[e][ch] * Ef[e][ch];
-        kb[e][ch] = kk[e][ch] * Eb[e][ch];
+        kf[ch] = kk[ch] * Ef[e][ch];
+        qf[ch] = qq[ch] * Ef[e][ch];
+        kb[e][ch] = kk[ch] * Eb[e][ch];
       }
       kfp[e] = pack2(kf[0], kf[1]);
       *reinterpret_cast<uint32_t*>(gKf + r * KP + d0) = kfp[e];
@@ -396,18 +434,30 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       }
     }
     __syncthreads();  // (3) gate operands ready
+    if (pending_off >= 0) flush_out(pending_off, pending_tok0);
 
     // ================= phase B: gated K K^T and Q K^T blocks ==================
-    // units (i, j <= i), u = i(i+1)/2 + j, dealt to waves u % 8
-    auto unit_i = [](int u) { return u >= 6 ? 3 : (u >= 3 ? 2 : (u >= 1 ? 1 : 0)); };
+    // Waves 0-3 take the diagonal block (w, w) and invert it right away (C1);
+    // waves 4-7 take the off-diagonal blocks.
+    float tcol[16];                      // column lr of T_ww = (I + L_ww)^-1 (waves 0-3)
     f32x4 accA[2], accM[2];
+    int ui[2], uj[2], nunits = 0;
+    if (w < 4) {
+      ui[0] = w; uj[0] = w; nunits = 1;
+    } else {
+      // (1,0),(3,2) | (2,0),(3,1) | (2,1) | (3,0)
+      const int i0 = w == 4 ? 1 : (w == 5 ? 2 : (w == 6 ? 2 : 3));
+      const int j0 = w == 4 ? 0 : (w == 5 ? 0 : (w == 6 ? 1 : 0));
+      ui[0] = i0; uj[0] = j0; nunits = 1;
+      if (w == 4) { ui[1] = 3; uj[1] = 2; nunits = 2; }
+      if (w == 5) { ui[1] = 3; uj[1] = 1; nunits = 2; }
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int u = w + 8 * s;
       accA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
       accM[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < 10) {
-        const int i = unit_i(u), j = u - i * (i + 1) / 2;
+      if (s < nunits) {
+        const int i = ui[s], j = uj[s];
         const uint16_t* left_k = gKf + (16 * i + lr) * KP;
         const uint16_t* left_q = gQf + (16 * i + lr) * KP;
         const uint16_t* right;
@@ -427,73 +477,25 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         }
       }
     }
-    __syncthreads();  // (4) gate operands consumed; region reused below
-
-    // L = diag(beta) A (strictly lower): diagonal blocks fp32 transposed for the
-    // 16x16 inversions, off-diagonal blocks bf16 for the matrix-core merges.
-    // M (lower incl. diagonal) bf16.
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int u = w + 8 * s;
-      if (u < 10) {
-        const int i = unit_i(u), j = u - i * (i + 1) / 2;
-        const int sc = 16 * j + lr;
+    if (w < 4) {
+      // C1: L_ww = diag(beta) A_ww (strictly lower), transposed to LDS (this
+      // wave's own block), then T_ww by column-wise forward substitution in
+      // fp32, lane column lr (all four lane groups compute the same column)
+      {
         float lv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * i + 4 * lg + e;
-          lv[e] = sc < r ? mBeta[r] * accA[s][e] : 0.f;
-          pM[r * RP + sc] = f2bf(sc <= r ? accM[s][e] : 0.f);
-          if (i != j) sLb[r * RP + sc] = f2bf(lv[e]);
+          const int r = 16 * w + 4 * lg + e;
+          lv[e] = lr < 4 * lg + e ? mBeta[r] * accA[0][e] : 0.f;
         }
-        if (i == j)
-          *reinterpret_cast<float4*>(sLdT + (16 * i + lr) * LDP + 4 * lg) =
-              make_float4(lv[0], lv[1], lv[2], lv[3]);
+        *reinterpret_cast<float4*>(sLdT + (16 * w + lr) * LDP + 4 * lg) =
+            make_float4(lv[0], lv[1], lv[2], lv[3]);
       }
-    }
-    // zero the upper blocks of M and N that the M U and N Y products read: (0,1), (2,3)
-    {
-      const int blk = tid >> 8, rr = (tid >> 4) & 15, cc = tid & 15;
-      const int r = blk == 0 ? rr : 32 + rr, sc = blk == 0 ? 16 + cc : 48 + cc;
-      pM[r * RP + sc] = 0;
-      pN[r * RP + sc] = 0;
-    }
-    // prepared operands: -K exp(G), Q exp(G), K exp(G_end - G) (transposed)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = 16 * ib + 8 * hb + e;
-      *reinterpret_cast<uint32_t*>(pKt + r * KP + d0) =
-          pack2(-__uint_as_float(kfp[e] << 16) * cref[0], -__uint_as_float(kfp[e] & 0xffff0000u) * cref[1]);
-      *reinterpret_cast<uint32_t*>(pQt + r * KP + d0) =
-          pack2(__uint_as_float(qfp[e] << 16) * cref[0], __uint_as_float(qfp[e] & 0xffff0000u) * cref[1]);
-    }
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      uint16_t hv[8], lv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = kb[e][ch] * Pend[ch];
-        hv[e] = f2bf(x);
-        lv[e] = f2bf(x - bf2f(hv[e]));
-      }
-      *reinterpret_cast<uint4*>(pKhT + (d0 + ch) * RP + 16 * ib + 8 * hb) =
-          *reinterpret_cast<uint4*>(&hv[0]);
-      if (ib == 3)
-        *reinterpret_cast<uint4*>(pKhLo + (d0 + ch) * LP + 8 * hb) =
-            *reinterpret_cast<uint4*>(&lv[0]);
-    }
-    // prefetch the next segment's inputs; they land during phases C and D
-    if (seg_end < len) load_segment(seg_end, ld);
-    __syncthreads();  // (5) L, M and prepared operands ready
-
-    // ================= phase C: N = (I + L)^-1 - I ============================
-    // C1: the four 16x16 diagonal blocks T_ii = (I + L_ii)^-1 by column-wise
-    // forward substitution in fp32; wave w < 4 inverts block w, lane column lr.
-    if (w < 4) {
-      const int cc = lr;
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = r == cc ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) tcol[r] = r == lr ? 1.f : 0.f;
       const float* LT = sLdT + (16 * w) * LDP;   // LT[s][r] = L[r][s]
 #pragma unroll
       for (int s2 = 0; s2 < 15; ++s2) {
@@ -504,67 +506,136 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
           lcol[4 * q4] = v4.x; lcol[4 * q4 + 1] = v4.y; lcol[4 * q4 + 2] = v4.z; lcol[4 * q4 + 3] = v4.w;
         }
 #pragma unroll
-        for (int r = s2 + 1; r < 16; ++r) t[r] = fmaf(-lcol[r], t[s2], t[r]);
+        for (int r = s2 + 1; r < 16; ++r) tcol[r] = fmaf(-lcol[r], tcol[s2], tcol[r]);
       }
-      if (lg == 0) {
-        // N diagonal block: T_ii - I (strictly lower)
+    }
+    __syncthreads();  // (4) gate operands consumed; region reused below
+
+    // L off-diagonal blocks (bf16, for the matrix-core merges) and M (bf16,
+    // lower incl. diagonal)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pN[(16 * w + r) * RP + 16 * w + cc] = f2bf(r > cc ? t[r] : 0.f);
-        uint16_t tv[16];
+    for (int s = 0; s < 2; ++s) {
+      if (s < nunits) {
+        const int i = ui[s], j = uj[s];
+        const int sc = 16 * j + lr;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tv[r] = f2bf(t[r]);
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        if (w == 0) {          // T00^T into Ta^T[0:16][0:16]
-          *reinterpret_cast<uint4*>(sTaT + cc * TP) = *reinterpret_cast<uint4*>(&tv[0]);
-          *reinterpret_cast<uint4*>(sTaT + cc * TP + 8) = *reinterpret_cast<uint4*>(&tv[8]);
-        } else if (w == 1) {   // T11^T into Ta^T[16:32][16:32], zero Ta^T[16:32][0:16]; T11 row-major
-          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 16) = *reinterpret_cast<uint4*>(&tv[0]);
-          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 24) = *reinterpret_cast<uint4*>(&tv[8]);
-          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP) = z;
-          *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 8) = z;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sT11R[r * SP + cc] = tv[r];
-        } else if (w == 2) {   // T22^T; T22 row-major into Tb[0:16][0:16], zero Tb[0:16][16:32]
-          *reinterpret_cast<uint4*>(sT22T + cc * SP) = *reinterpret_cast<uint4*>(&tv[0]);
-          *reinterpret_cast<uint4*>(sT22T + cc * SP + 8) = *reinterpret_cast<uint4*>(&tv[8]);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            sTbR[r * TP + cc] = tv[r];
-            sTbR[r * TP + 16 + cc] = 0;
-          }
-        } else {               // T33 row-major into Tb[16:32][16:32]
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sTbR[(16 + r) * TP + 16 + cc] = tv[r];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * lg + e;
+          pM[r * RP + sc] = f2bf(sc <= r ? accM[s][e] : 0.f);
+          if (i != j) sLb[r * RP + sc] = f2bf(mBeta[r] * accA[s][e]);
         }
       }
     }
-    __syncthreads();
-    // Merges on the matrix cores.  With Ta = T[0:32,0:32], Tb = T[32:64,32:64]:
-    //   T10 = -T11 (L10 T00),  T32 = -T33 (L32 T22),  T[32:64,0:32] = -Tb (L[32:64,0:32] Ta).
-    // 16-deep products use the 32-deep instruction with lane groups 2, 3 zero.
-    const bf16x8 z8 = zero8();
-    if (w < 2) {   // C2: P10 = L10 T00 (w 0), P32 = L32 T22 (w 1); store P^T
-      const uint16_t* A = w == 0 ? sLb + (16 + lr) * RP : sLb + (48 + lr) * RP + 32;
-      const uint16_t* B = w == 0 ? sTaT + lr * TP : sT22T + lr * SP;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(lg < 2 ? lds8(A + 8 * lg) : z8, lg < 2 ? lds8(B + 8 * lg) : z8, acc);
-      uint2 pk;
-      pk.x = pack2(acc[0], acc[1]);
-      pk.y = pack2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(sPT + (16 * w + lr) * SP + 4 * lg) = pk;
+    // zero the upper blocks of M and N that the M U and N Y products read: (0,1), (2,3)
+    {
+      const int blk = tid >> 8, rr = (tid >> 4) & 15, cc = tid & 15;
+      const int r = blk == 0 ? rr : 32 + rr, sc = blk == 0 ? 16 + cc : 48 + cc;
+      pM[r * RP + sc] = 0;
+      pN[r * RP + sc] = 0;
     }
-    __syncthreads();
-    if (w < 2) {   // C3: T10 = -T11 P10 (w 0), T32 = -T33 P32 (w 1)
-      const uint16_t* A = w == 0 ? sT11R + lr * SP : sTbR + (16 + lr) * TP + 16;
-      const uint16_t* B = sPT + (16 * w + lr) * SP;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(lg < 2 ? lds8(A + 8 * lg) : z8, lg < 2 ? lds8(B + 8 * lg) : z8, acc);
+    // T_ww outputs of the diagonal inversions
+    if (w < 4 && lg == 0) {
+      const int cc = lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pN[(16 * w + r) * RP + 16 * w + cc] = f2bf(r > cc ? tcol[r] : 0.f);
+      uint32_t tp[8];
+#pragma unroll
+      for (int r2 = 0; r2 < 8; ++r2) tp[r2] = pack2(tcol[2 * r2], tcol[2 * r2 + 1]);
+      const uint4 t_lo = make_uint4(tp[0], tp[1], tp[2], tp[3]);
+      const uint4 t_hi = make_uint4(tp[4], tp[5], tp[6], tp[7]);
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      if (w == 0) {          // Ta^T[0:16][0:16] = T00^T
+        *reinterpret_cast<uint4*>(sTaT + cc * TP) = t_lo;
+        *reinterpret_cast<uint4*>(sTaT + cc * TP + 8) = t_hi;
+      } else if (w == 1) {   // Ta^T[16:32][16:32] = T11^T, Ta^T[16:32][0:16] = 0; T11 row-major
+        *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 16) = t_lo;
+        *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 24) = t_hi;
+        *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP) = z;
+        *reinterpret_cast<uint4*>(sTaT + (16 + cc) * TP + 8) = z;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT11R[r * SP + cc] = (uint16_t)(tp[r >> 1] >> (16 * (r & 1)));
+      } else if (w == 2) {   // T22^T; Tb[0:16][0:16] = T22 row-major, Tb[0:16][16:32] = 0
+        *reinterpret_cast<uint4*>(sT22T + cc * SP) = t_lo;
+        *reinterpret_cast<uint4*>(sT22T + cc * SP + 8) = t_hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sTbR[r * TP + cc] = (uint16_t)(tp[r >> 1] >> (16 * (r & 1)));
+          sTbR[r * TP + 16 + cc] = 0;
+        }
+      } else {               // Tb[16:32][16:32] = T33 row-major
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sTbR[(16 + r) * TP + 16 + cc] = (uint16_t)(tp[r >> 1] >> (16 * (r & 1)));
+      }
+    }
+    // prepared operands: -K exp(G), Q exp(G), K exp(G_end - G) (transposed)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 16 * ib + 8 * hb + e;
+      *reinterpret_cast<uint32_t*>(pKt + r * KP + d0) =
+          pack2(-lo_of(kfp[e]) * cref[0], -hi_of(kfp[e]) * cref[1]);
+      *reinterpret_cast<uint32_t*>(pQt + r * KP + d0) =
+          pack2(lo_of(qfp[e]) * cref[0], hi_of(qfp[e]) * cref[1]);
+    }
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      uint32_t hp[4], lp[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        split2(kb[2 * e2][ch] * Pend[ch], kb[2 * e2 + 1][ch] * Pend[ch], hp[e2], lp[e2]);
+      *reinterpret_cast<uint4*>(pKhT + (d0 + ch) * RP + 16 * ib + 8 * hb) =
+          make_uint4(hp[0], hp[1], hp[2], hp[3]);
+      if (ib == 3)
+        *reinterpret_cast<uint4*>(pKhLo + (d0 + ch) * LP + 8 * hb) =
+            make_uint4(lp[0], lp[1], lp[2], lp[3]);
+    }
+    // prefetch the next segment's inputs; they land during phases C and D
+    if (has_next) load_segment(seg_end, ld);
+    __syncthreads();  // (5) L, M, T_ii and prepared operands ready
+
+    // ================= phase C: merges of N = (I + L)^-1 - I ==================
+    // With Ta = T[0:32,0:32], Tb = T[32:64,32:64]:
+    //   T10 = -T11 (L10 T00),  T32 = -T33 (L32 T22),  T[32:64,0:32] = -Tb (L[32:64,0:32] Ta).
+    // A product's fp32 accumulator feeds the next product as its B operand
+    // directly: lane group lg holds rows 4lg..4lg+3 of each 16-row tile, so
+    // the reduction index of the second product is permuted the same way in
+    // its A operand (the order of terms in a matrix product is free).
+    const bf16x8 z8 = zero8();
+    auto acc_to_b4 = [&](const f32x4& c4) {   // 4 rows -> k-slots 0..3, zeros 4..7
+      const uint4 u = make_uint4(pack2(c4[0], c4[1]), pack2(c4[2], c4[3]), 0u, 0u);
+      return __builtin_bit_cast(bf16x8, u);
+    };
+    auto acc_to_b8 = [&](const f32x4& c0, const f32x4& c1) {   // two tiles -> 8 k-slots
+      const uint4 u = make_uint4(pack2(c0[0], c0[1]), pack2(c0[2], c0[3]), pack2(c1[0], c1[1]),
+                                 pack2(c1[2], c1[3]));
+      return __builtin_bit_cast(bf16x8, u);
+    };
+    auto lds4_z4 = [&](const uint16_t* p) {   // 4 bf16 from LDS, then 4 zeros
+      const uint2 v2 = *reinterpret_cast<const uint2*>(p);
+      return __builtin_bit_cast(bf16x8, make_uint4(v2.x, v2.y, 0u, 0u));
+    };
+    auto lds4_4 = [&](const uint16_t* p, const uint16_t* q2) {   // 4 + 4 bf16 from two places
+      const uint2 v0 = *reinterpret_cast<const uint2*>(p);
+      const uint2 v1 = *reinterpret_cast<const uint2*>(q2);
+      return __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+    };
+    if (w < 2) {
+      // w 0: T10 = -T11 (L10 T00);  w 1: T32 = -T33 (L32 T22)   (16-deep products:
+      // lane groups 2, 3 feed zeros to the first)
+      const uint16_t* A1 = w == 0 ? sLb + (16 + lr) * RP : sLb + (48 + lr) * RP + 32;
+      const uint16_t* B1 = w == 0 ? sTaT + lr * TP : sT22T + lr * SP;
+      f32x4 P = {0.f, 0.f, 0.f, 0.f};
+      P = mfma(lg < 2 ? lds8(A1 + 8 * lg) : z8, lg < 2 ? lds8(B1 + 8 * lg) : z8, P);
+      const uint16_t* A2 = w == 0 ? sT11R + lr * SP + 4 * lg : sTbR + (16 + lr) * TP + 16 + 4 * lg;
+      f32x4 Tn = {0.f, 0.f, 0.f, 0.f};
+      Tn = mfma(lds4_z4(A2), acc_to_b4(P), Tn);
       uint16_t tv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tv[e] = f2bf(-acc[e]);
+      for (int e = 0; e < 4; ++e) tv[e] = f2bf(-Tn[e]);
       if (w == 0) {
         // Ta^T[n][16 + m] = T10[m][n]; N block (1,0)
-        *reinterpret_cast<uint2*>(sTaT + lr * TP + 16 + 4 * lg) = *reinterpret_cast<uint2*>(&tv[0]);
+        *reinterpret_cast<uint2*>(sTaT + lr * TP + 16 + 4 * lg) =
+            make_uint2(pack2(-Tn[0], -Tn[1]), pack2(-Tn[2], -Tn[3]));
 #pragma unroll
         for (int e = 0; e < 4; ++e) pN[(16 + 4 * lg + e) * RP + lr] = tv[e];
       } else {
@@ -577,62 +648,56 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       }
     }
     __syncthreads();
-    const int mi = (w >> 1) & 1, ni = w & 1;
-    if (w < 4) {   // C4: Q = L[32:64, 0:32] Ta, tile (mi, ni); store Q^T
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(lds8(sLb + (32 + 16 * mi + lr) * RP + 8 * lg), lds8(sTaT + (16 * ni + lr) * TP + 8 * lg),
-                 acc);
-      uint2 pk;
-      pk.x = pack2(acc[0], acc[1]);
-      pk.y = pack2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(sQT + (16 * ni + lr) * TP + 16 * mi + 4 * lg) = pk;
-    }
-    __syncthreads();
-    if (w < 4) {   // C5: T[32:64, 0:32] = -Tb Q, tile (mi, ni), into N
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(lds8(sTbR + (16 * mi + lr) * TP + 8 * lg), lds8(sQT + (16 * ni + lr) * TP + 8 * lg), acc);
+    if (w < 2) {
+      // column block ni = w of T[32:64, 0:32]: Q = L[32:64,0:32] Ta[:, ni] (two
+      // 16-row tiles), then -Tb Q
+      const int ni = w;
+      f32x4 Q0 = {0.f, 0.f, 0.f, 0.f}, Q1 = {0.f, 0.f, 0.f, 0.f};
+      const bf16x8 bta = lds8(sTaT + (16 * ni + lr) * TP + 8 * lg);
+      Q0 = mfma(lds8(sLb + (32 + lr) * RP + 8 * lg), bta, Q0);
+      Q1 = mfma(lds8(sLb + (48 + lr) * RP + 8 * lg), bta, Q1);
+      const bf16x8 bq = acc_to_b8(Q0, Q1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pN[(32 + 16 * mi + 4 * lg + e) * RP + 16 * ni + lr] = f2bf(-acc[e]);
+      for (int mi = 0; mi < 2; ++mi) {
+        const uint16_t* Ar = sTbR + (16 * mi + lr) * TP;
+        f32x4 Tn = {0.f, 0.f, 0.f, 0.f};
+        Tn = mfma(lds4_4(Ar + 4 * lg, Ar + 16 + 4 * lg), bq, Tn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pN[(32 + 16 * mi + 4 * lg + e) * RP + 16 * ni + lr] = f2bf(-Tn[e]);
+      }
     }
     __syncthreads();  // (C) solve done; solve scratch free
 
     // ================= phase D: the chunk recurrence ==========================
-    // S -> bf16, stored transposed for the B operand: dST[j][d]
-#pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt) {
-      uint2 pk;
-      pk.x = pack2(S[nt][0], S[nt][1]);
-      pk.y = pack2(S[nt][2], S[nt][3]);
-      *reinterpret_cast<uint2*>(dST + (16 * nt + lr) * KP + 16 * w + 4 * lg) = pk;
-    }
-    __syncthreads();
-
-    // X = V - K exp(G) S ; Y = beta X    (rows of block rb, tiles nt0..)
-    f32x4 Y[NTW];
+    // dST holds the incoming state in bf16.  X = V - K exp(G) S, Y = beta X and
+    // P = Q exp(G) S for the rows of block rb.
+    f32x4 Y[NTW], PO[NTW];
     if (rb_active) {
 #pragma unroll
       for (int t2 = 0; t2 < NTW; ++t2) {
         const int nt = nt0 + t2;
-        f32x4 acc;
+        f32x4 acc, po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           acc[e] = bf2f(mV[(16 * rb + 4 * lg + e) * Lay::VP + 16 * nt + lr]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int off = 32 * ks + 8 * lg;
-          acc = mfma(lds8(pKt + (16 * rb + lr) * KP + off), lds8(dST + (16 * nt + lr) * KP + off),
-                     acc);
+          const int o8 = 32 * ks + 8 * lg;
+          const bf16x8 bs = lds8(dST + (16 * nt + lr) * KP + o8);
+          acc = mfma(lds8(pKt + (16 * rb + lr) * KP + o8), bs, acc);
+          po = mfma(lds8(pQt + (16 * rb + lr) * KP + o8), bs, po);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] *= mBeta[16 * rb + 4 * lg + e];
         Y[t2] = acc;
-        uint2 pk;
-        pk.x = pack2(acc[0], acc[1]);
-        pk.y = pack2(acc[2], acc[3]);
-        *reinterpret_cast<uint2*>(mY + (16 * nt + lr) * RP + 16 * rb + 4 * lg) = pk;
+        PO[t2] = po;
+        *reinterpret_cast<uint2*>(mY + (16 * nt + lr) * RP + 16 * rb + 4 * lg) =
+            make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
       }
     }
-    __syncthreads();
+    // next segment's gate factors, first half (its inputs were prefetched)
+    if (has_next) gate_factors_1(ld);
+    __syncthreads();  // (D1) Y and the next segment's half-block products ready
 
     // U = Y + N Y
     const int nks = rb >= 2 ? 2 : 1;   // k-steps of 32 rows covering rows < 16(rb+1)
@@ -642,9 +707,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         const int nt = nt0 + t2;
         f32x4 acc = Y[t2];
         for (int ks = 0; ks < nks; ++ks) {
-          const int off = 32 * ks + 8 * lg;
-          acc = mfma(lds8(pN + (16 * rb + lr) * RP + off), lds8(mY + (16 * nt + lr) * RP + off),
-                     acc);
+          const int o8 = 32 * ks + 8 * lg;
+          acc = mfma(lds8(pN + (16 * rb + lr) * RP + o8), lds8(mY + (16 * nt + lr) * RP + o8), acc);
         }
         uint2 ph, pl;
         split2(acc[0], acc[1], ph.x, pl.x);
@@ -653,37 +717,33 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         *reinterpret_cast<uint2*>(dUlo + (16 * nt + lr) * RP + 16 * rb + 4 * lg) = pl;
       }
     }
-    __syncthreads();
+    // next segment: second half of the gate factors; its V slice and beta
+    if (has_next) {
+      gate_factors_2();
+      stage_v_beta(ld);
+    }
+    __syncthreads();  // (D2) U ready; nobody reads dST, mV, mBeta again in this segment
 
-    // O = scale (Q exp(G) S + M U)   (rows of block rb)
+    // O = scale (P + M U)   (rows of block rb), staged for 16-byte stores
     if (rb_active) {
 #pragma unroll
       for (int t2 = 0; t2 < NTW; ++t2) {
         const int nt = nt0 + t2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int off = 32 * ks + 8 * lg;
-          acc = mfma(lds8(pQt + (16 * rb + lr) * KP + off), lds8(dST + (16 * nt + lr) * KP + off),
-                     acc);
-        }
+        f32x4 acc = PO[t2];
         for (int ks = 0; ks < nks; ++ks) {
-          const int off = 32 * ks + 8 * lg;
-          const bf16x8 am = lds8(pM + (16 * rb + lr) * RP + off);
-          acc = mfma(am, lds8(dUhi + (16 * nt + lr) * RP + off), acc);
-          acc = mfma(am, lds8(dUlo + (16 * nt + lr) * RP + off), acc);
+          const int o8 = 32 * ks + 8 * lg;
+          const bf16x8 am = lds8(pM + (16 * rb + lr) * RP + o8);
+          acc = mfma(am, lds8(dUhi + (16 * nt + lr) * RP + o8), acc);
+          acc = mfma(am, lds8(dUlo + (16 * nt + lr) * RP + o8), acc);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * lg + e;
-          if (r >= off)
-            a.out[((size_t)(tok0 + r) * H + h) * DVT + col0 + 16 * nt + lr] =
-                f2bf(acc[e] * a.scale);
-        }
+        for (int e = 0; e < 4; ++e)
+          oStg[(16 * rb + 4 * lg + e) * Lay::VP + 16 * nt + lr] = f2bf(acc[e] * a.scale);
       }
     }
 
-    // S <- diag(exp(G_end)) S + (K exp(G_end - G))^T U    (rows 16w..16w+15)
+    // S <- diag(exp(G_end)) S + (K exp(G_end - G))^T U    (rows 16w..16w+15),
+    // then its bf16 copy for the next segment's B operand
     {
       const int drow = 16 * w;
       float gam[4];
@@ -700,21 +760,26 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         for (int e = 0; e < 4; ++e) acc[e] *= gam[e];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int off = 32 * ks + 8 * lg;
-          const bf16x8 bh = lds8(dUhi + (16 * nt + lr) * RP + off);
+          const int o8 = 32 * ks + 8 * lg;
+          const bf16x8 bh = lds8(dUhi + (16 * nt + lr) * RP + o8);
           acc = mfma(akh[ks], bh, acc);
-          acc = mfma(akh[ks], lds8(dUlo + (16 * nt + lr) * RP + off), acc);
+          acc = mfma(akh[ks], lds8(dUlo + (16 * nt + lr) * RP + o8), acc);
           if (ks == 1) acc = mfma(aklo, bh, acc);
         }
         S[nt] = acc;
+        *reinterpret_cast<uint2*>(dST + (16 * nt + lr) * KP + 16 * w + 4 * lg) =
+            make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
       }
     }
-    __syncthreads();  // segment done; LDS reused by the next segment
+    __syncthreads();  // (E) segment done: the gate-operand region is free again
 
+    pending_off = off;
+    pending_tok0 = tok0;
     if (seg_end == ckpt_at) export_state(a.ckpt);
     pos = seg_end;
   }
 
+  if (pending_off >= 0) flush_out(pending_off, pending_tok0);
   if (a.final_state) export_state(a.final_state);
 }
 
