@@ -115,6 +115,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b8_t8192")
     ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--variant", default="auto", choices=["auto", "decomp", "fused"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -156,8 +157,11 @@ def main() -> int:
     out = torch.empty_like(v)
     fin = torch.empty((p.N, p.H, 128, 128), dtype=torch.float32, device=dev)
     ck = None if offs is None else torch.empty_like(fin)
-    prob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, value_split=args.value_split)
+    prob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, variant=args.variant,
+                          value_split=args.value_split)
     variant, vsplit = K.plan(prob)
+    ws_bytes = K.workspace_size(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream(dev)
 
     def ptr(t):
@@ -165,7 +169,7 @@ def main() -> int:
 
     def step():
         st = K.prefill_raw(prob, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), ptr(s0),
-                           ptr(out), ptr(fin), ptr(offs), ptr(ck), 0, 0, stream.cuda_stream)
+                           ptr(out), ptr(fin), ptr(offs), ptr(ck), ptr(ws), ws_bytes, stream.cuda_stream)
         if st != 0:
             raise K.KDAError(st, "kda_prefill")
 

@@ -75,8 +75,13 @@ typedef enum {
 } kda_status;
 
 typedef enum {
-  KDA_VARIANT_AUTO = 0,          /* pick the schedule from the problem shape and CU count */
-  KDA_VARIANT_FUSED = 2          /* one launch: chunk preparation and recurrence per workgroup */
+  KDA_VARIANT_AUTO = 0,          /* pick the schedule from the problem shape and the CU count;
+                                    the two-launch schedule only when the workspace holds it */
+  KDA_VARIANT_DECOMP = 1,        /* two launches through the workspace: a chunk-parallel
+                                    prepare, then the recurrence (FlashInfer PR #4633,
+                                    Description: the "decomp" variant) */
+  KDA_VARIANT_FUSED = 2          /* one launch: chunk preparation and recurrence per workgroup
+                                    (same page: the "fused" variant); needs no workspace */
 } kda_variant;
 
 typedef struct {
@@ -88,13 +93,19 @@ typedef struct {
   float scale;               /* read-out scale, finite (typically 1/sqrt(128)) */
   float gate_lower_bound;    /* caller's promise g >= bound; must lie in [-5, 0] */
   int32_t variant;           /* kda_variant */
-  int32_t value_split;       /* 0 = automatic, else 2 or 4: workgroups per (sequence, head),
-                                each owning 128/value_split columns of the state */
+  int32_t value_split;       /* 0 = automatic, else workgroups per (sequence, head), each
+                                owning 128/value_split columns of the state: 2 or 4 for
+                                FUSED, 1, 2, 4 or 8 for DECOMP (FlashInfer PR #4262,
+                                Physical schedules: value rows split over CTAs) */
 } kda_problem;
 
 /* Bytes of caller workspace kda_prefill needs for this problem (host only, no
- * device access).  The current schedules need none, so this reports 0; a
- * caller may still pass a buffer. */
+ * device access).  FUSED needs none (0).  DECOMP, and AUTO so that it may
+ * pick DECOMP, need a header of (N + 1) int32 rounded up to 256 bytes plus
+ * 66,560 bytes per (segment slot, head), with floor(T_total / 64) + 2 N
+ * segment slots: about 1.04 KiB per token-head.  The workspace is scratch:
+ * it carries nothing between calls, may be reused by any later call on the
+ * same stream, and must not be used by two calls in flight at once. */
 kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes);
 
 /* Host-side argument checks of kda_prefill without launching anything: sizes,
@@ -122,8 +133,9 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
 /* Static string for a status code. */
 const char* kda_status_string(kda_status s);
 
-/* Number of workgroups per (sequence, head) kda_prefill would use for this
- * problem on the current device (host only; reads the device's CU count). */
+/* Schedule and workgroups per (sequence, head) kda_prefill would use for this
+ * problem on the current device, given a workspace of at least
+ * kda_prefill_workspace_size bytes (host only; reads the device's CU count). */
 kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split);
 
 #ifdef __cplusplus

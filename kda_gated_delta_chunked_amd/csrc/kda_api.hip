@@ -45,8 +45,12 @@ kda_status check_problem(const kda_problem* p) {
   if (!std::isfinite(p->gate_lower_bound) || p->gate_lower_bound < -5.0f ||
       p->gate_lower_bound > 0.0f)
     return KDA_ERR_INVALID_ARG;
-  if (p->variant != KDA_VARIANT_AUTO && p->variant != KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;
-  if (p->value_split != 0 && p->value_split != 2 && p->value_split != 4) return KDA_ERR_UNSUPPORTED;
+  if (p->variant != KDA_VARIANT_AUTO && p->variant != KDA_VARIANT_FUSED &&
+      p->variant != KDA_VARIANT_DECOMP)
+    return KDA_ERR_UNSUPPORTED;
+  const int vs = p->value_split;
+  if (vs != 0 && vs != 1 && vs != 2 && vs != 4 && vs != 8) return KDA_ERR_UNSUPPORTED;
+  if (p->variant == KDA_VARIANT_FUSED && (vs == 1 || vs == 8)) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if ((int64_t)p->num_seqs * p->num_heads > kInt32Max / 8) return KDA_ERR_TOO_LARGE;
@@ -67,18 +71,38 @@ int device_cu_count() {
   return cus;
 }
 
-// Schedule choice.  Each workgroup carries one (sequence, head) pair and a
-// slice of the state's columns; the chunk preparation is repeated by every
-// workgroup of a pair, the recurrence is split.  Two workgroups per pair is
-// the default; four when there are too few pairs to occupy half the CUs.
-void choose(const kda_problem* p, int cus, int32_t* variant, int32_t* vsplit) {
-  *variant = KDA_VARIANT_FUSED;
+size_t decomp_bytes(const kda_problem* p) {
+  size_t header = 0, bytes = 0;
+  int64_t slots = 0;
+  kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, &header, &slots, &bytes);
+  return bytes;
+}
+
+// Schedule choice.  FUSED: each workgroup carries one (sequence, head) pair
+// and a slice of the state's columns, and repeats the chunk preparation; two
+// workgroups per pair, four when there are too few pairs to occupy half the
+// CUs.  DECOMP: the recurrence workgroup holds two slot buffers in LDS, so one
+// runs per CU; split the columns as far as the CUs allow.  AUTO takes DECOMP
+// whenever the workspace holds it (value_split of 1/8 are DECOMP-only, 2 and
+// 4 exist in both).
+void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
+  int32_t var = p->variant;
+  if (var == KDA_VARIANT_AUTO) {
+    var = ws_bytes >= decomp_bytes(p) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
+    if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
+      var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
+  }
+  *variant = var;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
   if (p->value_split) {
     *vsplit = p->value_split;
-    return;
+  } else if (var == KDA_VARIANT_FUSED) {
+    *vsplit = (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
+  } else {
+    int v = 1;
+    while (v < 8 && cus > 0 && pairs * v * 2 <= cus) v *= 2;
+    *vsplit = v;
   }
-  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
-  *vsplit = (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
 }
 
 }  // namespace
@@ -103,7 +127,7 @@ kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes) {
   if (!bytes) return KDA_ERR_INVALID_ARG;
   const kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
-  *bytes = 0;
+  *bytes = p->variant == KDA_VARIANT_FUSED ? 0 : decomp_bytes(p);
   return KDA_OK;
 }
 
@@ -123,10 +147,12 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
                         ckpt_offsets, ckpt_state, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
-  size_t need = 0;
-  st = kda_prefill_workspace_size(p, &need);
-  if (st != KDA_OK) return st;
-  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // DECOMP (named, or implied by a DECOMP-only value_split) needs its
+  // workspace; AUTO falls back to FUSED when the workspace is smaller
+  int32_t var = 0, vs = 0;
+  choose(p, 0, workspace ? workspace_bytes : 0, &var, &vs);
+  if (var == KDA_VARIANT_DECOMP && (!workspace || workspace_bytes < decomp_bytes(p)))
+    return KDA_ERR_WORKSPACE_TOO_SMALL;
 
   const uint64_t tok_bf16 = (uint64_t)T * H * kHeadDim * 2;
   const uint64_t tok_f32 = (uint64_t)T * H * kHeadDim * 4;
@@ -151,6 +177,9 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
   // checkpoint buffer: no overlap with anything
   for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff, rws})
     if (overlaps(rck, r)) return KDA_ERR_OVERLAP;
+  // workspace: written by the call, so it overlaps no other buffer either
+  for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff})
+    if (overlaps(rws, r)) return KDA_ERR_OVERLAP;
   return KDA_OK;
 }
 
@@ -158,7 +187,7 @@ kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split
   if (!variant || !value_split) return KDA_ERR_INVALID_ARG;
   const kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
-  choose(p, device_cu_count(), variant, value_split);
+  choose(p, device_cu_count(), decomp_bytes(p), variant, value_split);
   return KDA_OK;
 }
 
@@ -172,26 +201,56 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
                                      workspace_bytes);
   if (st != KDA_OK) return st;
   int32_t variant = 0, vsplit = 0;
-  choose(p, device_cu_count(), &variant, &vsplit);
-
-  kda::FusedArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = g;
-  a.beta = beta;
-  a.cu_seqlens = cu_seqlens;
-  a.s0 = initial_state;
-  a.out = out;
-  a.final_state = final_state;
-  a.ckpt_off = ckpt_offsets;
-  a.ckpt = ckpt_state;
-  a.N = p->num_seqs;
-  a.H = p->num_heads;
-  a.num_pairs = p->num_seqs * p->num_heads;
-  a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
-  a.scale = p->scale;
-  const hipError_t err = kda::launch_fused(a, vsplit, static_cast<hipStream_t>(stream));
+  choose(p, device_cu_count(), workspace ? workspace_bytes : 0, &variant, &vsplit);
+  const hipStream_t st_ = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (variant == KDA_VARIANT_DECOMP) {
+    size_t header = 0, bytes = 0;
+    int64_t slots = 0;
+    kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, &header, &slots, &bytes);
+    kda::DecompArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.s0 = initial_state;
+    a.out = out;
+    a.final_state = final_state;
+    a.ckpt_off = ckpt_offsets;
+    a.ckpt = ckpt_state;
+    a.seg_base = static_cast<int32_t*>(workspace);
+    a.slots = static_cast<unsigned char*>(workspace) + header;
+    a.N = p->num_seqs;
+    a.H = p->num_heads;
+    a.T_total = p->total_tokens;
+    a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
+    a.slots_per_seq = cu_seqlens ? 0 : (a.T_fixed + 63) / 64 + (ckpt_offsets ? 1 : 0);
+    a.slot_bound = slots;
+    a.scale = p->scale;
+    const int64_t prepare_slots = cu_seqlens ? slots : (int64_t)p->num_seqs * a.slots_per_seq;
+    err = kda::launch_decomp(a, vsplit, prepare_slots, st_);
+  } else {
+    kda::FusedArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.s0 = initial_state;
+    a.out = out;
+    a.final_state = final_state;
+    a.ckpt_off = ckpt_offsets;
+    a.ckpt = ckpt_state;
+    a.N = p->num_seqs;
+    a.H = p->num_heads;
+    a.num_pairs = p->num_seqs * p->num_heads;
+    a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
+    a.scale = p->scale;
+    err = kda::launch_fused(a, vsplit, st_);
+  }
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

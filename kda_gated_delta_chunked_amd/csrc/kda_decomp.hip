@@ -1,0 +1,780 @@
+// kda_decomp.hip -- two-launch chunked KDA prefill for gfx950 (MI355X).
+//
+// The chunk-parallel / recurrent split of the prefill: a prepare launch that
+// runs over every (segment, head) at once, and a recurrence launch that carries
+// the state across a sequence's segments (FlashInfer PR #4633, Description:
+// the "decomp" variant, two launches sharing one scratch arena).
+//
+// Segments are the 64-token chunks of each sequence, aligned to its start,
+// with the chunk that holds a checkpoint offset cut in two at that offset.  A
+// segment of c <= 64 rows sits in the last c rows of a 64-row tile; the rows
+// before it are zero and contribute nothing.  With G_r = g_0 + ... + g_r per
+// key channel (reset at every segment):
+//   A[r,s] = sum_d k_rd k_sd exp(G_rd - G_sd)   s < r      (gated K K^T)
+//   M[r,s] = sum_d q_rd k_sd exp(G_rd - G_sd)   s <= r     (gated Q K^T)
+//   T = (I + diag(beta) A)^-1,  N = T - I
+//   K~ = K exp(G),  Q~ = Q exp(G),  K^ = K exp(G_end - G),  Gam = exp(G_end)
+// are state independent (prepare).  The recurrence then does, per segment,
+//   X = V - K~ S,  Y = diag(beta) X,  U = Y + N Y
+//   O = scale (Q~ S + M U),   S <- diag(Gam) S + K^^T U
+// which regroups the token recurrence (decay, delta-rule correction, read-out
+// of the updated state) by segments.
+//
+// Prepare stores its results in the caller's workspace already in the lane
+// order of the v_mfma_f32_16x16x32_bf16 operands the recurrence feeds, so the
+// recurrence copies a slot straight into LDS (global_load_lds) and reads each
+// operand fragment with one 16-byte LDS load per lane.
+//
+// Fragment conventions (lane l = 16 g + q, g = 0..3, q = 0..15).  Within a
+// 32-wide contraction block b, element e = 0..7 of lane l stands for index
+//   kidx(b, g, e) = 32 b + 16 (e / 4) + 4 g + (e % 4).
+// An A operand of row tile t holds X[16 t + q][kidx]; a B operand of column
+// tile t holds Y[kidx][16 t + q]; an accumulator holds C[4 g + i][q].  With
+// this order, the accumulators of row tiles 2b and 2b+1 of a matrix Z, taken
+// side by side, are exactly the B operand of Z for block b (and the A operand
+// of Z^T), so state and U feed the next product without any data movement.
+//
+// Exponent range (prepare): rows form 16-row blocks i with local cumulative
+// sums Gl_r = G_r - G_{16i-1} <= 0 and block sums bt_i.  With g >= -5 (the gate
+// lower bound of lmdeploy PR #5050, Modification) every factor used below lies
+// in [exp(-80), exp(80)] or is a product of factors <= 1:
+//   block (i,i):   exp(G_r - G_s) = exp(Gl_r) * exp(-Gl_s)
+//   block (i,j<i): exp(G_r - G_s) = exp(Gl_r) * exp(bt_j - Gl_s) * prod_{j<m<i} exp(bt_m)
+//
+// Precision: bf16 operands with fp32 accumulation, except the diagonal blocks
+// of M (hi + lo operands), U (hi + lo into M U and the state update), the last
+// 16 rows of K^ (hi + lo) and the identity part of T (U = Y + N Y in fp32); the
+// triangular solve is done in fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_kernels.h"
+
+namespace kda {
+namespace {
+
+constexpr int CH = 64;    // chunk rows
+constexpr int DK = 128;   // key channels = value channels
+
+// Slot layout (bytes).  Fragments are 64 lanes x 16 bytes = 1 KiB.
+constexpr int SL_KT = 0;        // K~  : row tile t (4) x key block b (4), A of K~ S
+constexpr int SL_QT = 16384;    // Q~  : token tile t (4) x key block b (4), B of S^T Q~^T
+constexpr int SL_KH = 32768;    // K^ hi: key tile m (8) x token block b (2), A of K^^T U
+constexpr int SL_KL = 49152;    // K^ lo, tokens 48..63: key tile m (8), 8 bytes per lane
+constexpr int SL_M = 53248;     // M  : token tile t x token block b <= t/2 (6 fragments)
+constexpr int SL_N = 59392;     // N  : same tiling as M
+constexpr int SL_GAM = 65536;   // exp(G_end), 128 fp32
+constexpr int SL_BETA = 66048;  // beta per tile row, 64 fp32 (0 on empty rows)
+constexpr int SLOT_UNITS = 65;  // 1 KiB copy units per slot
+static_assert(SLOT_UNITS * 1024 == kDecompSlotBytes, "slot size");
+static_assert(SL_BETA + 256 <= kDecompSlotBytes, "slot layout");
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ float lo_of(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float hi_of(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// eight floats -> bf16x8 (hi), and optionally the rounding remainder (lo)
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
+  uint4 u;
+  u.x = pack2(x[0], x[1]);
+  u.y = pack2(x[2], x[3]);
+  u.z = pack2(x[4], x[5]);
+  u.w = pack2(x[6], x[7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack2(x[2 * e], x[2 * e + 1]);
+    l[e] = pack2(x[2 * e] - lo_of(h[e]), x[2 * e + 1] - hi_of(h[e]));
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+// two accumulators (row tiles 2b, 2b+1) -> the B operand of block b
+__device__ __forceinline__ bf16x8 acc_pair(const f32x4& a, const f32x4& b) {
+  uint4 u;
+  u.x = pack2(a[0], a[1]);
+  u.y = pack2(a[2], a[3]);
+  u.z = pack2(b[0], b[1]);
+  u.w = pack2(b[2], b[3]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void acc_pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  split8(x, hi, lo);
+}
+// M / N fragment index of (token tile t, token block b <= t / 2)
+__host__ __device__ constexpr int tri_frag(int t, int b) { return t < 2 ? t : 2 * t - 2 + b; }
+
+// ---------------------------------------------------------------------------
+// Sequence and segment geometry (shared by both launches).
+
+struct SeqInfo {
+  int64_t bos;   // first token of the sequence
+  int len;       // tokens
+  int p;         // checkpoint offset (-1 when none)
+  int nseg;      // segments
+  bool split;    // the chunk holding p is cut at p
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const DecompArgs& a, int n) {
+  SeqInfo s;
+  int64_t b, e;
+  if (a.cu_seqlens) {
+    b = a.cu_seqlens[n];
+    e = a.cu_seqlens[n + 1];
+  } else {
+    b = (int64_t)n * a.T_fixed;
+    e = b + a.T_fixed;
+  }
+  // keep every access inside [0, T_total) even for offsets that break the contract
+  b = b < 0 ? 0 : (b > a.T_total ? a.T_total : b);
+  e = e < b ? b : (e > a.T_total ? a.T_total : e);
+  s.bos = b;
+  s.len = (int)(e - b);
+  s.p = a.ckpt_off ? a.ckpt_off[n] : -1;
+  s.split = s.p > 0 && s.p < s.len && (s.p & (CH - 1)) != 0;
+  s.nseg = (s.len + CH - 1) / CH + (s.split ? 1 : 0);
+  return s;
+}
+
+// token range [lo, hi) of segment j, relative to the sequence start
+__device__ __forceinline__ void seg_range(const SeqInfo& s, int j, int& lo, int& hi) {
+  const int pc = s.split ? (s.p >> 6) : 0x7fffffff;
+  if (j < pc) {
+    lo = CH * j;
+    hi = min(lo + CH, s.len);
+  } else if (j == pc) {
+    lo = CH * j;
+    hi = s.p;
+  } else {
+    const int jj = j - 1;
+    lo = (j == pc + 1) ? s.p : CH * jj;
+    hi = min(CH * jj + CH, s.len);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 0 (packed layout only): first slot of every sequence.  Sequence n
+// owns ceil(L_n / 64) slots, plus one when checkpoints are requested (the
+// chunk cut at the offset).  base[N] is the total.
+
+__global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int extra = a.ckpt_off ? 1 : 0;
+  int64_t carry = 0;
+  for (int n0 = 0; n0 < a.N; n0 += 1024) {
+    const int n = n0 + t;
+    int cnt = 0;
+    if (n < a.N) {
+      int64_t b = a.cu_seqlens[n], e = a.cu_seqlens[n + 1];
+      b = b < 0 ? 0 : (b > a.T_total ? a.T_total : b);
+      e = e < b ? b : (e > a.T_total ? a.T_total : e);
+      cnt = (int)((e - b + CH - 1) / CH) + extra;
+    }
+    int x = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      woff += i < w ? wsum[i] : 0;
+      tot += wsum[i];
+    }
+    if (n < a.N) a.seg_base[n] = (int32_t)(carry + woff + x - cnt);
+    __syncthreads();
+    carry += tot;
+  }
+  if (t == 0) a.seg_base[a.N] = (int32_t)carry;
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: prepare.  One workgroup of 4 waves per (slot, head); wave i owns
+// the 16-row block i of the tile.
+
+constexpr int P_GP = DK + 4;    // fp32 pitch of the cumulative-sum tile
+constexpr int P_LP = CH + 4;    // fp32 pitch of L and T
+// per-channel factor rows
+constexpr int F_BT = 0;         // bt_0..3 (block sums of g)
+constexpr int F_P = 4;          // P_1..3 = exp(bt_0 + ... + bt_{i-1})  (row F_P + i - 1)
+constexpr int F_R = 7;          // R_0..2 = exp(bt_{i+1} + ... + bt_3)  (row F_R + i)
+constexpr int F_IBD = 10;       // exp(-bt_i)
+constexpr int F_W20 = 14;       // exp(bt_1)
+constexpr int F_W31 = 15;       // exp(bt_2)
+constexpr int F_W30 = 16;       // exp(bt_1 + bt_2)
+constexpr int F_ROWS = 17;
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void load8_f32(const float* p, float (&x)[8], int off) {
+  const float4 a = *reinterpret_cast<const float4*>(p + off);
+  const float4 b = *reinterpret_cast<const float4*>(p + off + 16);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void unpack8(const uint2 (&u)[2], float (&x)[8]) {
+  x[0] = lo_of(u[0].x); x[1] = hi_of(u[0].x); x[2] = lo_of(u[0].y); x[3] = hi_of(u[0].y);
+  x[4] = lo_of(u[1].x); x[5] = hi_of(u[1].x); x[6] = lo_of(u[1].y); x[7] = hi_of(u[1].y);
+}
+
+__global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
+  __shared__ __attribute__((aligned(16))) float sG[CH * P_GP];        // Gl; later T (pitch P_LP)
+  __shared__ __attribute__((aligned(16))) float sF[F_ROWS * DK];
+  __shared__ __attribute__((aligned(16))) float sL[CH * P_LP];        // beta_r A[r,s]
+  __shared__ __attribute__((aligned(16))) float sB[CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[(16 + 4) * 512]; // K^ fragments, then scratch
+
+  const int H = a.H;
+  const int64_t bid = blockIdx.x;
+  const int64_t s = bid / H;
+  const int h = (int)(bid - s * H);
+  if (s >= a.slot_bound) return;
+
+  // slot -> (sequence, segment)
+  int n, j;
+  if (a.cu_seqlens) {
+    if (s >= a.seg_base[a.N]) return;
+    int lo = 0, hi = a.N;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.seg_base[mid] <= s) lo = mid; else hi = mid;
+    }
+    n = lo;
+    j = (int)(s - a.seg_base[n]);
+  } else {
+    n = (int)(s / a.slots_per_seq);
+    j = (int)(s - (int64_t)n * a.slots_per_seq);
+  }
+  const SeqInfo si = seq_info(a, n);
+  if (j >= si.nseg) return;
+  int lo_t, hi_t;
+  seg_range(si, j, lo_t, hi_t);
+  const int off = CH - (hi_t - lo_t);
+  const int64_t tok0 = si.bos + lo_t - off;        // token of tile row 0
+  unsigned char* slot = a.slots + (size_t)bid * kDecompSlotBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
+
+  // A-side rows of this wave: r = 16 w + q; prefetch k and q (8 channels per block)
+  const int r = 16 * w + q;
+  const bool rv = r >= off;
+  const size_t erow = ((size_t)(tok0 + r) * H + h) * DK;
+  uint2 kA[4][2], qA[4][2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ch = 32 * b + 16 * hh + 4 * g4;
+      kA[b][hh] = rv ? *reinterpret_cast<const uint2*>(a.k + erow + ch) : make_uint2(0, 0);
+      qA[b][hh] = rv ? *reinterpret_cast<const uint2*>(a.q + erow + ch) : make_uint2(0, 0);
+    }
+
+  // (1) cumulative gate sums inside 16-row blocks: thread -> channel d, rows 32 hb ..
+  {
+    const int d = tid & (DK - 1), hb = tid >> 7;
+    float gv[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int row = 32 * hb + e;
+      gv[e] = row >= off ? a.g[((size_t)(tok0 + row) * H + h) * DK + d] : 0.f;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        acc += gv[16 * blk + e];
+        sG[(32 * hb + 16 * blk + e) * P_GP + d] = acc;
+      }
+      sF[(F_BT + 2 * hb + blk) * DK + d] = acc;
+    }
+    if (tid < CH) sB[tid] = tid >= off ? a.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+  }
+  __syncthreads();
+
+  // (2) per-channel block factors; Gam and beta go straight to the slot
+  if (tid < DK) {
+    const int d = tid;
+    const float b0 = sF[F_BT * DK + d], b1 = sF[(F_BT + 1) * DK + d];
+    const float b2 = sF[(F_BT + 2) * DK + d], b3 = sF[(F_BT + 3) * DK + d];
+    sF[(F_P + 0) * DK + d] = __expf(b0);
+    sF[(F_P + 1) * DK + d] = __expf(b0 + b1);
+    sF[(F_P + 2) * DK + d] = __expf(b0 + b1 + b2);
+    sF[(F_R + 0) * DK + d] = __expf(b1 + b2 + b3);
+    sF[(F_R + 1) * DK + d] = __expf(b2 + b3);
+    sF[(F_R + 2) * DK + d] = __expf(b3);
+    sF[(F_IBD + 0) * DK + d] = __expf(-b0);
+    sF[(F_IBD + 1) * DK + d] = __expf(-b1);
+    sF[(F_IBD + 2) * DK + d] = __expf(-b2);
+    sF[(F_IBD + 3) * DK + d] = __expf(-b3);
+    sF[F_W20 * DK + d] = __expf(b1);
+    sF[F_W31 * DK + d] = __expf(b2);
+    sF[F_W30 * DK + d] = __expf(b1 + b2);
+    reinterpret_cast<float*>(slot + SL_GAM)[d] = __expf(b0 + b1 + b2 + b3);
+  } else if (tid < DK + CH) {
+    reinterpret_cast<float*>(slot + SL_BETA)[tid - DK] = sB[tid - DK];
+  }
+  __syncthreads();
+
+  // (3) wave i = w: operands of row block i, gated products of blocks (i, j <= i)
+  const int i = w;
+  const float beta_r = sB[r];
+  bf16x8 aK[4], aQ[4], aQl[4], bD[4], bDl[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int ch0 = 32 * b + 4 * g4;
+    float kf[8], qf[8], gl[8], bt[8], fac[8];
+    unpack8(kA[b], kf);
+    unpack8(qA[b], qf);
+    load8_f32(sG, gl, r * P_GP + ch0);
+    load8_f32(sF, bt, (F_BT + i) * DK + ch0);
+    float ef[8], eb[8], Kf[8], Qf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ef[e] = __expf(gl[e]);
+      eb[e] = __expf(bt[e] - gl[e]);
+      Kf[e] = kf[e] * ef[e];
+      Qf[e] = qf[e] * ef[e];
+    }
+    aK[b] = to_bf16x8(Kf);
+    split8(Qf, aQ[b], aQl[b]);
+    // K~ and Q~ fragments (row tile i, key block b)
+    float kt[8], qt[8];
+    if (i > 0) {
+      load8_f32(sF, fac, (F_P + i - 1) * DK + ch0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kt[e] = Kf[e] * fac[e];
+        qt[e] = Qf[e] * fac[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kt[e] = Kf[e];
+        qt[e] = Qf[e];
+      }
+    }
+    *reinterpret_cast<bf16x8*>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(kt);
+    *reinterpret_cast<bf16x8*>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(qt);
+    // diagonal-block right operand k exp(-Gl) = k Eb / bd_i, hi + lo
+    load8_f32(sF, fac, (F_IBD + i) * DK + ch0);
+    float kr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kr[e] = kf[e] * eb[e] * fac[e];
+    split8(kr, bD[b], bDl[b]);
+    // K^ = k exp(G_end - G_r) = k Eb R_i, scattered into the K^^T fragments
+    float kh[8];
+    if (i < 3) {
+      load8_f32(sF, fac, (F_R + i) * DK + ch0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kh[e] = kf[e] * eb[e] * fac[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kh[e] = kf[e] * eb[e];
+    }
+    const int tb = i >> 1, ep = 4 * (i & 1) + (q & 3), lg = (q >> 2) * 16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = ch0 + 16 * (e >> 2) + (e & 3);
+      const int m = ch >> 4, lp = lg + (ch & 15);
+      const uint32_t hb16 = pack2(kh[e], 0.f) & 0xffffu;
+      sK[((m * 2 + tb) * 64 + lp) * 8 + ep] = (uint16_t)hb16;
+      if (i == 3) sK[8192 + (m * 64 + lp) * 4 + (q & 3)] = (uint16_t)(pack2(kh[e] - bf2f(hb16), 0.f) & 0xffffu);
+    }
+  }
+
+  // diagonal block: A_ii^T (bf16) and M_ii^T (hi + lo), lane holds row r, s = 16 i + 4 g4 + e
+  f32x4 macc[4];
+  {
+    f32x4 aacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 m0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      aacc = mfma(bD[b], aK[b], aacc);
+      m0 = mfma(bD[b], aQ[b], m0);
+      m0 = mfma(bDl[b], aQ[b], m0);
+      m0 = mfma(bD[b], aQl[b], m0);
+    }
+    float4 lv;
+    float* lp = &lv.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sidx = 16 * i + 4 * g4 + e;
+      lp[e] = sidx < r ? beta_r * aacc[e] : 0.f;
+      m0[e] = sidx <= r ? m0[e] : 0.f;
+    }
+    *reinterpret_cast<float4*>(&sL[r * P_LP + 16 * i + 4 * g4]) = lv;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) macc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (jj == i) macc[jj] = m0;
+  }
+  // off-diagonal blocks (i, jb < i)
+#pragma unroll
+  for (int jb = 0; jb < 3; ++jb) {
+    if (jb >= i) continue;
+    const int srow = 16 * jb + q;
+    const bool sv = srow >= off;
+    const size_t es = ((size_t)(tok0 + srow) * H + h) * DK;
+    f32x4 aacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 m1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int ch0 = 32 * b + 4 * g4;
+      uint2 ku[2];
+      ku[0] = sv ? *reinterpret_cast<const uint2*>(a.k + es + ch0) : make_uint2(0, 0);
+      ku[1] = sv ? *reinterpret_cast<const uint2*>(a.k + es + ch0 + 16) : make_uint2(0, 0);
+      float ks[8], gl[8], bt[8], wf[8];
+      unpack8(ku, ks);
+      load8_f32(sG, gl, srow * P_GP + ch0);
+      load8_f32(sF, bt, (F_BT + jb) * DK + ch0);
+      const int wrow = (jb == i - 1) ? -1 : (i == 2 ? F_W20 : (jb == 1 ? F_W31 : F_W30));
+      if (wrow >= 0) {
+        load8_f32(sF, wf, wrow * DK + ch0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wf[e] = 1.f;
+      }
+      float kb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kb[e] = ks[e] * __expf(bt[e] - gl[e]) * wf[e];
+      const bf16x8 bb = to_bf16x8(kb);
+      aacc = mfma(bb, aK[b], aacc);
+      m1 = mfma(bb, aQ[b], m1);
+    }
+    float4 lv = make_float4(beta_r * aacc[0], beta_r * aacc[1], beta_r * aacc[2], beta_r * aacc[3]);
+    *reinterpret_cast<float4*>(&sL[r * P_LP + 16 * jb + 4 * g4]) = lv;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (jj == jb) macc[jj] = m1;
+  }
+  // M fragments of token tile i (B operand of O^T += U^T M^T)
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    if (2 * tb > i) continue;
+    const f32x4 lo4 = macc[2 * tb];
+    const f32x4 hi4 = (2 * tb + 1 <= i) ? macc[2 * tb + 1] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<bf16x8*>(slot + SL_M + (tri_frag(i, tb) * 64 + lane) * 16) = acc_pair(lo4, hi4);
+  }
+  __syncthreads();
+
+  // (4) wave 0: T_bb = (I + L_bb)^-1 by forward substitution, lane = (block, column);
+  //     waves 1-3: K^ fragments to the slot
+  float* sT = sG;
+  if (w == 0) {
+    const int bb = lane >> 4, col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float acc = rr == col ? 1.f : 0.f;
+      const float* lrow = &sL[(16 * bb + rr) * P_LP + 16 * bb];
+#pragma unroll
+      for (int ss = 0; ss < rr; ++ss) acc -= lrow[ss] * x[ss];
+      x[rr] = acc;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sT[(16 * bb + rr) * P_LP + 16 * bb + col] = x[rr];
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(sK);
+    uint4* dst = reinterpret_cast<uint4*>(slot + SL_KH);
+    for (int u = tid - 64; u < 1280; u += 192) dst[u] = src[u];
+  }
+  __syncthreads();
+
+  // (5) off-diagonal blocks of T: T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj
+  float* sZ = reinterpret_cast<float*>(sK) + 256 * w;
+  auto offdiag = [&](int ib, int jb) {
+    const int rr = lane >> 2, c4 = 4 * (lane & 3);
+    float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
+    for (int m = jb; m < ib; ++m) {
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const float lv = sL[(16 * ib + rr) * P_LP + 16 * m + kk];
+        const float4 tv = *reinterpret_cast<const float4*>(&sT[(16 * m + kk) * P_LP + 16 * jb + c4]);
+        z0 += lv * tv.x; z1 += lv * tv.y; z2 += lv * tv.z; z3 += lv * tv.w;
+      }
+    }
+    *reinterpret_cast<float4*>(&sZ[rr * 16 + c4]) = make_float4(z0, z1, z2, z3);
+    wave_sync();
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float tv = sT[(16 * ib + rr) * P_LP + 16 * ib + kk];
+      const float4 zv = *reinterpret_cast<const float4*>(&sZ[kk * 16 + c4]);
+      o0 += tv * zv.x; o1 += tv * zv.y; o2 += tv * zv.z; o3 += tv * zv.w;
+    }
+    *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o0, -o1, -o2, -o3);
+  };
+  if (w < 3) offdiag(w + 1, w);
+  __syncthreads();
+  if (w < 2) offdiag(w + 2, w);
+  __syncthreads();
+  if (w == 0) offdiag(3, 0);
+  __syncthreads();
+
+  // (6) N = T - I fragments of token tile w (A operand of N Y)
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    if (2 * tb > w) continue;
+    const int s0 = 32 * tb + 4 * g4;
+    const float4 v0 = *reinterpret_cast<const float4*>(&sT[r * P_LP + s0]);
+    const float4 v1 = *reinterpret_cast<const float4*>(&sT[r * P_LP + s0 + 16]);
+    const float x[8] = {s0 + 0 < r ? v0.x : 0.f, s0 + 1 < r ? v0.y : 0.f,
+                        s0 + 2 < r ? v0.z : 0.f, s0 + 3 < r ? v0.w : 0.f,
+                        s0 + 16 < r ? v1.x : 0.f, s0 + 17 < r ? v1.y : 0.f,
+                        s0 + 18 < r ? v1.z : 0.f, s0 + 19 < r ? v1.w : 0.f};
+    *reinterpret_cast<bf16x8*>(slot + SL_N + (tri_frag(w, tb) * 64 + lane) * 16) = to_bf16x8(x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: recurrence.  One workgroup of WAVES waves per (sequence, head,
+// column group); wave w owns 16 columns of the state (all 128 rows, 8
+// accumulator tiles in registers).  The slot of the next segment is copied
+// into the other LDS buffer while the current one is consumed.
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArgs a) {
+  __shared__ __attribute__((aligned(16))) uint4 opsA[SLOT_UNITS * 64];
+  __shared__ __attribute__((aligned(16))) uint4 opsB[SLOT_UNITS * 64];
+  constexpr int PARTS = 8 / WAVES;
+  const int H = a.H;
+  // workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8): keep
+  // the column groups of a (sequence, head) on one XCD so they share L2
+  const int bx = blockIdx.x, xcd = bx & 7, rest = bx >> 3;
+  const int pair = (rest / PARTS) * 8 + xcd, part = rest % PARTS;
+  if (pair >= a.N * H) return;
+  const int n = pair / H, h = pair - n * H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
+  const int col0 = 16 * (part * WAVES + w);
+
+  const SeqInfo si = seq_info(a, n);
+  const int64_t base = a.cu_seqlens ? (int64_t)a.seg_base[n] : (int64_t)n * a.slots_per_seq;
+  int nseg = si.nseg;
+  if (base + nseg > a.slot_bound) nseg = base >= a.slot_bound ? 0 : (int)(a.slot_bound - base);
+  const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q;
+
+  f32x4 S[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[m][e] = a.s0 ? a.s0[sbase + (size_t)(16 * m + 4 * g4 + e) * DK] : 0.f;
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[sbase + (size_t)(16 * m + 4 * g4 + e) * DK] = S[m][e];
+  };
+  if (a.ckpt_off && si.p == 0) store_state(a.ckpt);
+
+  auto issue_ops = [&](int jseg, uint4* dst) {
+    const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
+    for (int u = w; u < SLOT_UNITS; u += WAVES)
+      __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
+  };
+  auto geometry = [&](int jseg, int& off, int64_t& tok0) {
+    int lo, hi;
+    seg_range(si, jseg, lo, hi);
+    off = CH - (hi - lo);
+    tok0 = si.bos + lo - off;
+  };
+  // V of a segment in accumulator order: rows 16 t + 4 g4 + e, column col0 + q.
+  // Rows before the segment load row `off` instead (always inside the
+  // sequence) and are zeroed where they are used, so no load waits on a branch.
+  auto load_v = [&](int jseg, uint32_t (&vv)[16]) {
+    int off;
+    int64_t tok0;
+    geometry(jseg, off, tok0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r0 = max(16 * t + 4 * g4 + e, off);
+        vv[4 * t + e] = a.v[((size_t)(tok0 + r0) * H + h) * DK + col0 + q];
+      }
+  };
+
+  const float scale = a.scale;
+  uint32_t vcur[16], vnxt[16], opk[8];
+  int poff = CH;
+  int64_t ptok = 0;
+  bool pend = false;
+  auto store_out = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = 16 * t + q;
+      if (row >= poff)
+        *reinterpret_cast<uint2*>(a.out + ((size_t)(ptok + row) * H + h) * DK + col0 + 4 * g4) =
+            make_uint2(opk[2 * t], opk[2 * t + 1]);
+    }
+  };
+
+  auto step = [&](int jseg, const uint4* cur, uint4* nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies and V loads landed
+    __syncthreads();                     // ... and every other wave's
+    if (pend) store_out();
+    if (jseg + 1 < nseg) {
+      issue_ops(jseg + 1, nxt);
+      load_v(jseg + 1, vnxt);
+    }
+    auto frag = [&](int byte_off) { return __builtin_bit_cast(bf16x8, cur[(byte_off >> 4) + lane]); };
+    auto f4 = [&](int byte_off) { return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off); };
+
+    bf16x8 Sb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Sb[b] = acc_pair(S[2 * b], S[2 * b + 1]);
+    f32x4 X[4], O[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      X[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) X[t] = mfma(frag(SL_KT + (t * 4 + b) * 1024), Sb[b], X[t]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[b], frag(SL_QT + (t * 4 + b) * 1024), O[t]);
+    // Y = beta (V - X), kept in U; U = Y + N Y
+    int off;
+    int64_t tok0;
+    geometry(jseg, off, tok0);
+    f32x4 U[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 bt = f4(SL_BETA + (16 * t + 4 * g4) * 4);
+      const float bv[4] = {bt.x, bt.y, bt.z, bt.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vx = (16 * t + 4 * g4 + e >= off) ? bf2f(vcur[4 * t + e]) : 0.f;
+        U[t][e] = bv[e] * (vx - X[t][e]);
+      }
+    }
+    const bf16x8 Y0 = acc_pair(U[0], U[1]), Y1 = acc_pair(U[2], U[3]);
+    U[0] = mfma(frag(SL_N + tri_frag(0, 0) * 1024), Y0, U[0]);
+    U[1] = mfma(frag(SL_N + tri_frag(1, 0) * 1024), Y0, U[1]);
+    U[2] = mfma(frag(SL_N + tri_frag(2, 0) * 1024), Y0, U[2]);
+    U[2] = mfma(frag(SL_N + tri_frag(2, 1) * 1024), Y1, U[2]);
+    U[3] = mfma(frag(SL_N + tri_frag(3, 0) * 1024), Y0, U[3]);
+    U[3] = mfma(frag(SL_N + tri_frag(3, 1) * 1024), Y1, U[3]);
+    bf16x8 Uh[2], Ul[2];
+    acc_pair_split(U[0], U[1], Uh[0], Ul[0]);
+    acc_pair_split(U[2], U[3], Uh[1], Ul[1]);
+    // O^T += U^T M^T
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (2 * b > t) continue;
+        const bf16x8 mf = frag(SL_M + tri_frag(t, b) * 1024);
+        O[t] = mfma(Uh[b], mf, O[t]);
+        O[t] = mfma(Ul[b], mf, O[t]);
+      }
+    // S <- diag(Gam) S + K^^T U
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float4 gm = f4(SL_GAM + (16 * m + 4 * g4) * 4);
+      S[m][0] *= gm.x;
+      S[m][1] *= gm.y;
+      S[m][2] *= gm.z;
+      S[m][3] *= gm.w;
+      const bf16x8 k0 = frag(SL_KH + (m * 2 + 0) * 1024);
+      const bf16x8 k1 = frag(SL_KH + (m * 2 + 1) * 1024);
+      const uint2 kl = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_KL + m * 512 + lane * 8);
+      const bf16x8 klf = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, kl.x, kl.y));
+      S[m] = mfma(k0, Uh[0], S[m]);
+      S[m] = mfma(k0, Ul[0], S[m]);
+      S[m] = mfma(k1, Uh[1], S[m]);
+      S[m] = mfma(k1, Ul[1], S[m]);
+      S[m] = mfma(klf, Uh[1], S[m]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      opk[2 * t] = pack2(scale * O[t][0], scale * O[t][1]);
+      opk[2 * t + 1] = pack2(scale * O[t][2], scale * O[t][3]);
+    }
+    poff = off;
+    ptok = tok0;
+    pend = true;
+    if (a.ckpt_off && si.p > 0) {
+      int lo, hi;
+      seg_range(si, jseg, lo, hi);
+      if (hi == si.p) store_state(a.ckpt);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vcur[e] = vnxt[e];
+  };
+
+  if (nseg > 0) {
+    issue_ops(0, opsA);
+    load_v(0, vcur);
+  }
+  for (int jseg = 0; jseg < nseg; jseg += 2) {
+    step(jseg, opsA, opsB);
+    if (jseg + 1 < nseg) step(jseg + 1, opsB, opsA);
+  }
+  if (pend) store_out();
+  if (a.final_state) store_state(a.final_state);
+}
+
+template <int WAVES>
+hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
+  constexpr int PARTS = 8 / WAVES;
+  const int64_t pairs = (int64_t)a.N * a.H;
+  const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * PARTS));
+  hipLaunchKernelGGL(kda_recurrence_kernel<WAVES>, grid, dim3(64 * WAVES), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, hipStream_t stream) {
+  hipError_t err;
+  if (a.cu_seqlens) {
+    hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  const int64_t blocks = prepare_slots * a.H;
+  if (blocks > 0) {
+    hipLaunchKernelGGL(kda_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  switch (vsplit) {
+    case 1: return launch_recurrence<8>(a, stream);
+    case 2: return launch_recurrence<4>(a, stream);
+    case 4: return launch_recurrence<2>(a, stream);
+    case 8: return launch_recurrence<1>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

@@ -30,4 +30,47 @@ struct FusedArgs {
 // vsplit = workgroups per (sequence, head): 2 or 4.
 hipError_t launch_fused(const FusedArgs& a, int vsplit, hipStream_t stream);
 
+// Two-launch schedule.  The workspace holds a header of (N + 1) int32 slot
+// offsets (packed layout) followed by one slot of kDecompSlotBytes per
+// (segment, head).
+constexpr int kDecompSlotBytes = 66560;
+
+struct DecompArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;  // NULL: N sequences of T_fixed tokens
+  const float* s0;            // NULL: zero initial state
+  uint16_t* out;
+  float* final_state;         // may be NULL
+  const int32_t* ckpt_off;    // NULL: no export
+  float* ckpt;
+  unsigned char* slots;       // workspace slot area
+  int32_t* seg_base;          // workspace header: first slot of each sequence (packed layout)
+  int N;
+  int H;
+  int64_t T_total;
+  int64_t T_fixed;
+  int64_t slots_per_seq;      // fixed layout: slots owned by each sequence
+  int64_t slot_bound;         // slots the workspace holds
+  float scale;
+};
+
+// Workspace layout for (N, T_total, H): header bytes and slot capacity.
+inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, size_t* header,
+                                    int64_t* slots, size_t* bytes) {
+  *header = (size_t)(((N + 1) * 4 + 255) / 256 * 256);
+  // ceil(L/64) summed over sequences is at most floor(T/64) + N; one more per
+  // sequence for the chunk cut at a checkpoint offset
+  *slots = T_total / 64 + 2 * N;
+  *bytes = *header + (size_t)(*slots) * (size_t)H * kDecompSlotBytes;
+}
+
+// vsplit = workgroups per (sequence, head): 1, 2, 4 or 8.  prepare_slots =
+// slots the prepare launch covers (fixed layout: N * slots_per_seq; packed:
+// slot_bound).
+hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, hipStream_t stream);
+
 }  // namespace kda

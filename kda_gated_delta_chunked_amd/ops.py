@@ -18,7 +18,7 @@ KDA_OK = 0
 STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
                 -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_OVERLAP",
                 -5: "KDA_ERR_WORKSPACE_TOO_SMALL", -6: "KDA_ERR_TOO_LARGE", -7: "KDA_ERR_HIP"}
-VARIANTS = {"auto": 0, "fused": 2}
+VARIANTS = {"auto": 0, "decomp": 1, "fused": 2}
 HEAD_DIM = 128
 
 _lib = None
@@ -142,6 +142,8 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
     ``final_state=initial_state`` for an in-place update and ``out=v`` to
     overwrite v.  ckpt_offsets int32 [N] / ckpt_state fp32 [N, H, 128, 128]
     export the state after ckpt_offsets[n] tokens of sequence n.
+    workspace: a device buffer of at least ``workspace_size`` bytes; when None
+    and the schedule may use one, a buffer is taken from torch's allocator.
     """
     import torch
 
@@ -199,6 +201,10 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         raise ValueError("out must have q's shape")
     if final_state is None and output_final_state:
         final_state = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = workspace_size(prob)
+        if need and variant != "fused":
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev)

@@ -29,12 +29,14 @@ def to_device(p: synth.Problem):
     return d
 
 
-def run_gpu(p: synth.Problem, *, value_split: int = 0, d=None, sentinel: bool = True,
-            out_alias_v: bool = False, state_in_place: bool = False):
+def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=None,
+            sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False):
     """Run kda_prefill through the C ABI on a fresh set of device buffers.
 
     Outputs are pre-filled with NaN so that any element the kernel fails to
-    write shows up.  Returns numpy dict(out fp32, final, ckpt)."""
+    write shows up; the workspace (sized by kda_prefill_workspace_size) is
+    filled with 0xFF bytes (NaN as fp32) so nothing depends on its contents.
+    Returns numpy dict(out fp32, final, ckpt)."""
     import torch
     import kda_gated_delta_chunked_amd as K
     d = d or to_device(p)
@@ -52,14 +54,17 @@ def run_gpu(p: synth.Problem, *, value_split: int = 0, d=None, sentinel: bool = 
     ck = None
     if d["offs"] is not None:
         ck = torch.full((N, H, 128, 128), float("nan"), dtype=torch.float32, device=dev)
-    prob = K.make_problem(N, T, H, scale=p.scale, value_split=value_split)
+    prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split)
+    need = K.workspace_size(prob)
+    ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev) if need else None
     stream = torch.cuda.current_stream(dev)
     v_ptr = out.data_ptr() if out_alias_v else d["v"].data_ptr()
     st = K.prefill_raw(prob, d["q"].data_ptr(), d["k"].data_ptr(), v_ptr, d["g"].data_ptr(),
                        d["beta"].data_ptr(), 0 if d["cu"] is None else d["cu"].data_ptr(),
                        0 if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
                        0 if d["offs"] is None else d["offs"].data_ptr(),
-                       0 if ck is None else ck.data_ptr(), 0, 0, stream.cuda_stream)
+                       0 if ck is None else ck.data_ptr(), 0 if ws is None else ws.data_ptr(), need,
+                       stream.cuda_stream)
     assert st == 0, f"kda_prefill returned {st}"
     torch.cuda.synchronize()
     res = {"out": out.float().cpu().numpy(), "final": fin.cpu().numpy(),

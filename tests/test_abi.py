@@ -145,11 +145,56 @@ def test_prefill_rejects_on_the_host_without_a_device():
     assert st == OVERLAP
 
 
+def decomp_bytes(N, T, H):
+    """The documented workspace formula: (N + 1) int32 rounded up to 256 bytes,
+    then 66,560 bytes per (segment slot, head) for floor(T / 64) + 2 N slots."""
+    return ((N + 1) * 4 + 255) // 256 * 256 + (T // 64 + 2 * N) * H * 66560
+
+
 def test_workspace_size_and_plan_arguments():
-    p = K.make_problem(8, 65536, 12, scale=0.088)
-    assert K.workspace_size(p) == 0
+    assert K.workspace_size(K.make_problem(8, 65536, 12, scale=0.088, variant="fused")) == 0
+    for var in ("auto", "decomp"):
+        p = K.make_problem(8, 65536, 12, scale=0.088, variant=var)
+        assert K.workspace_size(p) == decomp_bytes(8, 65536, 12)
+    assert K.workspace_size(K.make_problem(3, 100, 2, scale=0.1)) == decomp_bytes(3, 100, 2)
     with pytest.raises(K.KDAError):
         K.workspace_size(K.make_problem(8, 65536, 12, scale=0.088, head_dim_k=64))
+
+
+def test_workspace_rules():
+    b = Bufs()
+    need = decomp_bytes(b.N, b.T, b.H)
+    ws = 1 << 44
+    args = b.args()[:-2]
+
+    def val(p, wsp, wsb, **over):
+        return K.validate_raw(p, *b.args(**over)[:-2], wsp, wsb)
+
+    dec = prob_for(b, variant="decomp")
+    assert val(dec, 0, 0) == WS                        # DECOMP needs its workspace
+    assert val(dec, ws, need - 1) == WS
+    assert val(dec, ws, need) == OK
+    assert val(prob_for(b), 0, 0) == OK                # AUTO falls back to FUSED
+    assert val(prob_for(b), ws, need) == OK
+    assert val(prob_for(b, value_split=8), 0, 0) == WS  # split 1 / 8 exist only in DECOMP
+    assert val(prob_for(b, variant="fused", value_split=8), 0, 0) == UNSUPPORTED
+    assert val(prob_for(b, variant="fused", value_split=1), ws, need) == UNSUPPORTED
+    for vs in (1, 2, 4, 8):
+        assert val(prob_for(b, variant="decomp", value_split=vs), ws, need) == OK
+    assert val(dec, ws + 8, need) == ALIGN
+    # the workspace overlaps nothing the call reads or writes
+    assert val(dec, b.addr["out"], need) == OVERLAP
+    assert val(dec, b.addr["fin"] - 4096, need) == OVERLAP
+    assert val(dec, b.addr["ck"], need) == OVERLAP
+    assert val(dec, b.addr["q"], need) == OVERLAP
+
+
+def test_plan_picks_a_schedule_without_a_device():
+    # no GPU here: the CU count reads as 0, and the choice is still valid
+    var, vs = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="fused"))
+    assert var == "fused" and vs in (2, 4)
+    var, vs = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="decomp", value_split=4))
+    assert (var, vs) == ("decomp", 4)
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -1,11 +1,17 @@
 """GPU parity: libkda (through its C ABI) against the fp64 token-by-token oracle.
 
+Both schedules are covered: FUSED (one launch) and DECOMP (prepare launch,
+then recurrence, through a caller workspace), at every value split each one
+supports.
+
 Gates: output max-abs <= 2e-2 and relative L2 <= 5e-3; final and checkpoint
 state relative L2 <= 1e-3.  Checkpoint placement and cu_seqlens handling are
 checked exactly (bitwise where the arithmetic allows it: offset 0 exports the
 initial state, a zero-length sequence keeps it, offset L equals the final
 state).  Outputs are NaN-filled before each call so unwritten elements fail.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -29,30 +35,40 @@ def _gpu():
     K.load_library()
 
 
-@pytest.mark.parametrize("vsplit", [2, 4])
-def test_one_chunk_h1(vsplit):
-    p = synth.workload("b1_t64_h1")
-    ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p, value_split=vsplit)
-    _report(f"b1_t64_h1 vs{vsplit}", assert_parity(gpu, ref, "b1_t64_h1"))
+SPLITS = [("fused", 2), ("fused", 4), ("decomp", 1), ("decomp", 2), ("decomp", 4), ("decomp", 8)]
+VARIANTS = ["fused", "decomp"]
 
 
+@functools.lru_cache(maxsize=None)
+def _workload_ref(name):
+    p = synth.workload(name)
+    return p, oracle.prefill_problem(p)
+
+
+@pytest.mark.parametrize("variant,vsplit", SPLITS)
+def test_one_chunk_h1(variant, vsplit):
+    p, ref = _workload_ref("b1_t64_h1")
+    gpu = run_gpu(p, variant=variant, value_split=vsplit)
+    _report(f"b1_t64_h1 {variant} vs{vsplit}", assert_parity(gpu, ref, "b1_t64_h1"))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 33, 63, 64, 65, 129, 200])
-def test_tails_fixed(T):
+def test_tails_fixed(T, variant):
     p = synth.make_problem([T, T], 2, seed=100 + T, fixed=True, init_state=True)
     ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p)
-    _report(f"fixed B2 T{T}", assert_parity(gpu, ref, f"T={T}"))
+    gpu = run_gpu(p, variant=variant)
+    _report(f"fixed B2 T{T} {variant}", assert_parity(gpu, ref, f"T={T}"))
 
 
-@pytest.mark.parametrize("vsplit", [2, 4])
-def test_packed_ragged_with_empty_and_ckpt(vsplit):
+@pytest.mark.parametrize("variant,vsplit", SPLITS)
+def test_packed_ragged_with_empty_and_ckpt(variant, vsplit):
     lens = [130, 0, 64, 1, 257, 0, 33]
     offs = [77, 0, 64, 1, 128, 0, 5]
     p = synth.make_problem(lens, 3, seed=7, init_state=True, ckpt=offs)
     ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p, value_split=vsplit)
-    _report(f"packed ragged vs{vsplit}", assert_parity(gpu, ref, "packed"))
+    gpu = run_gpu(p, variant=variant, value_split=vsplit)
+    _report(f"packed ragged {variant} vs{vsplit}", assert_parity(gpu, ref, "packed"))
     # zero-length sequences keep the initial state bit for bit; offset 0 exports it
     for n, L in enumerate(lens):
         if L == 0:
@@ -63,14 +79,15 @@ def test_packed_ragged_with_empty_and_ckpt(vsplit):
             assert np.array_equal(gpu["ckpt"][n], gpu["final"][n])
 
 
-def test_checkpoint_offsets_exact():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_checkpoint_offsets_exact(variant):
     # every offset position class: start, inside first chunk, chunk boundary,
     # inside a later chunk, end; plus out of range (slot untouched)
     L = 200
     offs = [0, 1, 37, 63, 64, 65, 128, 199, 200, 201, -1]
     p = synth.make_problem([L] * len(offs), 2, seed=9, init_state=True, ckpt=offs)
     ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p)
+    gpu = run_gpu(p, variant=variant)
     for n, off in enumerate(offs):
         if 0 <= off <= L:
             assert np.all(np.isfinite(gpu["ckpt"][n])), f"offset {off} not exported"
@@ -93,11 +110,12 @@ def test_checkpoint_offsets_exact():
     assert m["out_rel_l2"] <= 5e-3 and m["final_rel_l2"] <= 1e-3
 
 
-def test_gate_extremes_and_beta_zero():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_gate_extremes_and_beta_zero(variant):
     # g at the lower bound (-5): everything decays fast, normal gates apply
     p = synth.make_problem([300, 70], 2, seed=11, init_state=True, gate="min")
     ref = oracle.prefill_problem(p)
-    _report("gate=min", assert_parity(run_gpu(p), ref, "gate=min"))
+    _report(f"gate=min {variant}", assert_parity(run_gpu(p, variant=variant), ref, "gate=min"))
     # g = 0: nothing decays, so the bf16 rounding of the state operand in
     # V - K exp(G) S, of N and of Y accumulates over all 370 tokens instead of
     # being forgotten.  The rounding model of the kernel (tests/chunked_model.py,
@@ -105,36 +123,57 @@ def test_gate_extremes_and_beta_zero():
     # of 9.85e-4 on this input; the bound for this degenerate gate is 2e-3.
     p = synth.make_problem([300, 70], 2, seed=11, init_state=True, gate="zero")
     ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p)
+    gpu = run_gpu(p, variant=variant)
     m = metrics(gpu, ref)
-    _report("gate=zero", m)
+    _report(f"gate=zero {variant}", m)
     assert m["out_rel_l2"] <= 5e-3 and m["out_max_abs"] <= 2e-2 and m["final_rel_l2"] <= 2e-3, m
     # beta = 0 and g = 0: the state must come back unchanged, bit for bit
     p = synth.make_problem([150], 2, seed=12, init_state=True, gate="zero", beta_mode="zero")
-    gpu = run_gpu(p)
+    gpu = run_gpu(p, variant=variant)
     assert np.array_equal(gpu["final"], p.initial_state)
     ref = oracle.prefill_problem(p)
     assert_parity(gpu, ref, "beta=0")
 
 
-def test_aliasing_out_v_and_state_in_place():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_aliasing_out_v_and_state_in_place(variant):
     p = synth.make_problem([190, 64], 2, seed=13, init_state=True)
     ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p, out_alias_v=True, state_in_place=True)
+    gpu = run_gpu(p, variant=variant, out_alias_v=True, state_in_place=True)
     _report("aliased", assert_parity(gpu, ref, "aliased"))
 
 
-def test_deterministic():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_deterministic(variant):
     p = synth.make_problem([333], 2, seed=14, init_state=True)
     d = to_device(p)
-    a = run_gpu(p, d=d)
-    b = run_gpu(p, d=d)
+    a = run_gpu(p, variant=variant, d=d)
+    b = run_gpu(p, variant=variant, d=d)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["final"], b["final"])
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("name", ["b1_t8192", "b8_t8192", "packed_32_rand", "ckpt_16_rand"])
-def test_full_size_workloads(name):
-    p = synth.workload(name)
-    ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p)
-    _report(name, assert_parity(gpu, ref, name))
+def test_full_size_workloads(name, variant):
+    p, ref = _workload_ref(name)
+    gpu = run_gpu(p, variant=variant)
+    _report(f"{name} {variant}", assert_parity(gpu, ref, name))
+
+
+def test_decomp_matches_fused_on_packed_layout_as_separate_runs():
+    # packed sequences are independent: the packed call equals per-sequence
+    # fixed calls bit for bit (chunks align to each sequence start)
+    lens = [70, 129, 1, 64]
+    p = synth.make_problem(lens, 2, seed=15, init_state=True)
+    whole = run_gpu(p, variant="decomp")
+    t0 = 0
+    for n, L in enumerate(lens):
+        sl = slice(t0, t0 + L)
+        pn = synth.Problem(name="one", seq_lens=[L], H=p.H, q=p.q[sl], k=p.k[sl], v=p.v[sl],
+                           g=p.g[sl], beta=p.beta[sl], cu_seqlens=np.array([0, L], np.int32),
+                           fixed=True, initial_state=p.initial_state[n:n + 1], ckpt_offsets=None,
+                           scale=p.scale, seed=p.seed)
+        one = run_gpu(pn, variant="decomp")
+        assert np.array_equal(one["out"], whole["out"][sl]), n
+        assert np.array_equal(one["final"][0], whole["final"][n]), n
+        t0 += L
