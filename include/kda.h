@@ -95,7 +95,7 @@ typedef struct {
   int32_t variant;           /* kda_variant */
   int32_t value_split;       /* 0 = automatic, else workgroups per (sequence, head), each
                                 owning 128/value_split columns of the state: 2 or 4 for
-                                FUSED, 1, 2, 4 or 8 for DECOMP (FlashInfer PR #4262,
+                                FUSED, 2, 4 or 8 for DECOMP (FlashInfer PR #4262,
                                 Physical schedules: value rows split over CTAs) */
 } kda_problem;
 

@@ -49,8 +49,8 @@ kda_status check_problem(const kda_problem* p) {
       p->variant != KDA_VARIANT_DECOMP)
     return KDA_ERR_UNSUPPORTED;
   const int vs = p->value_split;
-  if (vs != 0 && vs != 1 && vs != 2 && vs != 4 && vs != 8) return KDA_ERR_UNSUPPORTED;
-  if (p->variant == KDA_VARIANT_FUSED && (vs == 1 || vs == 8)) return KDA_ERR_UNSUPPORTED;
+  if (vs != 0 && vs != 2 && vs != 4 && vs != 8) return KDA_ERR_UNSUPPORTED;
+  if (p->variant == KDA_VARIANT_FUSED && vs == 8) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if ((int64_t)p->num_seqs * p->num_heads > kInt32Max / 8) return KDA_ERR_TOO_LARGE;
@@ -83,13 +83,13 @@ size_t decomp_bytes(const kda_problem* p) {
 // workgroups per pair, four when there are too few pairs to occupy half the
 // CUs.  DECOMP: the recurrence workgroup holds two slot buffers in LDS, so one
 // runs per CU; split the columns as far as the CUs allow.  AUTO takes DECOMP
-// whenever the workspace holds it (value_split of 1/8 are DECOMP-only, 2 and
-// 4 exist in both).
+// whenever the workspace holds it (value_split 8 is DECOMP-only, 2 and 4 exist
+// in both).
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
   int32_t var = p->variant;
   if (var == KDA_VARIANT_AUTO) {
     var = ws_bytes >= decomp_bytes(p) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
-    if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
+    if (var == KDA_VARIANT_FUSED && p->value_split == 8)
       var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
   }
   *variant = var;
@@ -99,7 +99,7 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
   } else if (var == KDA_VARIANT_FUSED) {
     *vsplit = (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
   } else {
-    int v = 1;
+    int v = 2;
     while (v < 8 && cus > 0 && pairs * v * 2 <= cus) v *= 2;
     *vsplit = v;
   }

@@ -280,40 +280,76 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
 
+  // All global loads below are unconditional: a row before the segment
+  // (r < off) reads row `off` instead, which is always inside it, and the
+  // value is zeroed where it is used.  (A load under a per-lane condition would
+  // make the compiler wait for it before the branch joins.)
+  //
   // A-side rows of this wave: r = 16 w + q; prefetch k and q (8 channels per block)
   const int r = 16 * w + q;
   const bool rv = r >= off;
-  const size_t erow = ((size_t)(tok0 + r) * H + h) * DK;
+  const size_t erow = ((size_t)(tok0 + max(r, off)) * H + h) * DK;
   uint2 kA[4][2], qA[4][2];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int ch = 32 * b + 16 * hh + 4 * g4;
-      kA[b][hh] = rv ? *reinterpret_cast<const uint2*>(a.k + erow + ch) : make_uint2(0, 0);
-      qA[b][hh] = rv ? *reinterpret_cast<const uint2*>(a.q + erow + ch) : make_uint2(0, 0);
+      kA[b][hh] = *reinterpret_cast<const uint2*>(a.k + erow + ch);
+      qA[b][hh] = *reinterpret_cast<const uint2*>(a.q + erow + ch);
     }
+  const float beta_ld = a.beta[(size_t)(tok0 + max(tid & (CH - 1), off)) * H + h];
+  // B-side rows of the earlier blocks jb < w: s = 16 jb + q
+  uint2 kB[3][4][2];
+#pragma unroll
+  for (int jb = 0; jb < 3; ++jb) {
+    if (jb >= w) continue;
+    const size_t es = ((size_t)(tok0 + max(16 * jb + q, off)) * H + h) * DK;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        kB[jb][b][hh] = *reinterpret_cast<const uint2*>(a.k + es + 32 * b + 16 * hh + 4 * g4);
+  }
 
-  // (1) cumulative gate sums inside 16-row blocks: thread -> channel d, rows 32 hb ..
+  // (1) cumulative gate sums inside 16-row blocks.  Thread -> 4 channels
+  // (4 cg ..) and 8 rows (8 rg ..); the odd half of a block adds the even
+  // half's total, taken from lane - 32 of the same wave.
   {
-    const int d = tid & (DK - 1), hb = tid >> 7;
-    float gv[32];
+    const int cg = tid & 31, rg = tid >> 5;
+    float4 gv[8];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int row = 32 * hb + e;
-      gv[e] = row >= off ? a.g[((size_t)(tok0 + row) * H + h) * DK + d] : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * rg + e;
+      gv[e] = *reinterpret_cast<const float4*>(a.g + ((size_t)(tok0 + max(row, off)) * H + h) * DK + 4 * cg);
     }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float acc = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = 8 * rg + e >= off;
+      acc.x += ok ? gv[e].x : 0.f;
+      acc.y += ok ? gv[e].y : 0.f;
+      acc.z += ok ? gv[e].z : 0.f;
+      acc.w += ok ? gv[e].w : 0.f;
+      gv[e] = acc;
+    }
+    // totals of the even half (lanes 0..31 of this wave) to the odd half (lanes 32..63)
+    const float px = __shfl(acc.x, lane & 31, 64), py = __shfl(acc.y, lane & 31, 64);
+    const float pz = __shfl(acc.z, lane & 31, 64), pw = __shfl(acc.w, lane & 31, 64);
+    const bool odd = rg & 1;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        acc += gv[16 * blk + e];
-        sG[(32 * hb + 16 * blk + e) * P_GP + d] = acc;
+    for (int e = 0; e < 8; ++e) {
+      float4 v = gv[e];
+      if (odd) {
+        v.x += px;
+        v.y += py;
+        v.z += pz;
+        v.w += pw;
       }
-      sF[(F_BT + 2 * hb + blk) * DK + d] = acc;
+      *reinterpret_cast<float4*>(&sG[(8 * rg + e) * P_GP + 4 * cg]) = v;
+      if (odd && e == 7) *reinterpret_cast<float4*>(&sF[(F_BT + (rg >> 1)) * DK + 4 * cg]) = v;
     }
-    if (tid < CH) sB[tid] = tid >= off ? a.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+    if (tid < CH) sB[tid] = tid >= off ? beta_ld : 0.f;
   }
   __syncthreads();
 
@@ -351,6 +387,11 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     float kf[8], qf[8], gl[8], bt[8], fac[8];
     unpack8(kA[b], kf);
     unpack8(qA[b], qf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = rv ? kf[e] : 0.f;
+      qf[e] = rv ? qf[e] : 0.f;
+    }
     load8_f32(sG, gl, r * P_GP + ch0);
     load8_f32(sF, bt, (F_BT + i) * DK + ch0);
     float ef[8], eb[8], Kf[8], Qf[8];
@@ -441,17 +482,15 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     if (jb >= i) continue;
     const int srow = 16 * jb + q;
     const bool sv = srow >= off;
-    const size_t es = ((size_t)(tok0 + srow) * H + h) * DK;
     f32x4 aacc = {0.f, 0.f, 0.f, 0.f};
     f32x4 m1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int ch0 = 32 * b + 4 * g4;
-      uint2 ku[2];
-      ku[0] = sv ? *reinterpret_cast<const uint2*>(a.k + es + ch0) : make_uint2(0, 0);
-      ku[1] = sv ? *reinterpret_cast<const uint2*>(a.k + es + ch0 + 16) : make_uint2(0, 0);
       float ks[8], gl[8], bt[8], wf[8];
-      unpack8(ku, ks);
+      unpack8(kB[jb][b], ks);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ks[e] = sv ? ks[e] : 0.f;
       load8_f32(sG, gl, srow * P_GP + ch0);
       load8_f32(sF, bt, (F_BT + jb) * DK + ch0);
       const int wrow = (jb == i - 1) ? -1 : (i == 2 ? F_W20 : (jb == 1 ? F_W31 : F_W30));
@@ -507,35 +546,55 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
   }
   __syncthreads();
 
-  // (5) off-diagonal blocks of T: T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj
-  float* sZ = reinterpret_cast<float*>(sK) + 256 * w;
-  auto offdiag = [&](int ib, int jb) {
-    const int rr = lane >> 2, c4 = 4 * (lane & 3);
-    float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
-    for (int m = jb; m < ib; ++m) {
+  // (5) off-diagonal blocks of T in two levels.  First the 32 x 32 halves:
+  // T_10 = -T_11 L_10 T_00 and T_32 = -T_33 L_32 T_22.  Then the lower-left
+  // quarter of the block inverse, -T_hh L_hl T_ll with hh = rows 32..63 and
+  // ll = columns 0..31: wave w writes block (2 + w / 2, w % 2) as
+  //   T_ij = -sum_{p=2}^{i} T_ip Z_pj,   Z_pj = sum_{m=j}^{1} L_pm T_mj.
+  const int rr = lane >> 2, c4 = 4 * (lane & 3);
+  float* sZ = reinterpret_cast<float*>(sK) + 512 * w;
+  // Z = sum_{m=m0}^{m1-1} L[pb, m] T[m, jb] for this lane's row rr and columns c4..c4+3
+  auto lt_prod = [&](int pb, int m0, int m1, int jb) {
+    float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int m = m0; m < m1; ++m) {
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
-        const float lv = sL[(16 * ib + rr) * P_LP + 16 * m + kk];
+        const float lv = sL[(16 * pb + rr) * P_LP + 16 * m + kk];
         const float4 tv = *reinterpret_cast<const float4*>(&sT[(16 * m + kk) * P_LP + 16 * jb + c4]);
-        z0 += lv * tv.x; z1 += lv * tv.y; z2 += lv * tv.z; z3 += lv * tv.w;
+        z.x += lv * tv.x; z.y += lv * tv.y; z.z += lv * tv.z; z.w += lv * tv.w;
       }
     }
-    *reinterpret_cast<float4*>(&sZ[rr * 16 + c4]) = make_float4(z0, z1, z2, z3);
-    wave_sync();
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float tv = sT[(16 * ib + rr) * P_LP + 16 * ib + kk];
-      const float4 zv = *reinterpret_cast<const float4*>(&sZ[kk * 16 + c4]);
-      o0 += tv * zv.x; o1 += tv * zv.y; o2 += tv * zv.z; o3 += tv * zv.w;
-    }
-    *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o0, -o1, -o2, -o3);
+    return z;
   };
-  if (w < 3) offdiag(w + 1, w);
+  // sum_{p=p0}^{p1} T[ib, p] Zs[p - p0], Zs in this wave's scratch
+  auto tz_prod = [&](int ib, int p0, int p1) {
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int pb = p0; pb <= p1; ++pb) {
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const float tv = sT[(16 * ib + rr) * P_LP + 16 * pb + kk];
+        const float4 zv = *reinterpret_cast<const float4*>(&sZ[(pb - p0) * 256 + kk * 16 + c4]);
+        o.x += tv * zv.x; o.y += tv * zv.y; o.z += tv * zv.z; o.w += tv * zv.w;
+      }
+    }
+    return o;
+  };
+  if (w < 2) {
+    const int ib = 2 * w + 1, jb = 2 * w;
+    *reinterpret_cast<float4*>(&sZ[rr * 16 + c4]) = lt_prod(ib, jb, ib, jb);
+    wave_sync();
+    const float4 o = tz_prod(ib, ib, ib);
+    *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o.x, -o.y, -o.z, -o.w);
+  }
   __syncthreads();
-  if (w < 2) offdiag(w + 2, w);
-  __syncthreads();
-  if (w == 0) offdiag(3, 0);
+  {
+    const int ib = 2 + (w >> 1), jb = w & 1;
+    for (int pb = 2; pb <= ib; ++pb)
+      *reinterpret_cast<float4*>(&sZ[(pb - 2) * 256 + rr * 16 + c4]) = lt_prod(pb, jb, 2, jb);
+    wave_sync();
+    const float4 o = tz_prod(ib, 2, ib);
+    *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o.x, -o.y, -o.z, -o.w);
+  }
   __syncthreads();
 
   // (6) N = T - I fragments of token tile w (A operand of N Y)
@@ -554,15 +613,23 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Launch 2: recurrence.  One workgroup of WAVES waves per (sequence, head,
-// column group); wave w owns 16 columns of the state (all 128 rows, 8
-// accumulator tiles in registers).  The slot of the next segment is copied
-// into the other LDS buffer while the current one is consumed.
+// Launch 2: recurrence.  One workgroup per (sequence, head, column group) with
+// WAVES compute waves and WAVES copy waves.  Compute wave w owns 16 columns
+// of the state (all 128 rows: 8 accumulator tiles in registers).  The copy
+// waves bring the next segment's slot and V block into the idle one of two
+// LDS buffers with global_load_lds while the compute waves consume the other;
+// a copy wave may stall on a full memory queue, a compute wave never issues a
+// load.  One barrier per segment hands the buffers over.
 
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArgs a) {
-  __shared__ __attribute__((aligned(16))) uint4 opsA[SLOT_UNITS * 64];
-  __shared__ __attribute__((aligned(16))) uint4 opsB[SLOT_UNITS * 64];
+__global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompArgs a) {
+  constexpr int VW = 16 * WAVES;                  // columns per workgroup
+  constexpr int VUNITS = CH * VW * 2 / 1024;      // 1 KiB units of the V block
+  constexpr int UNITS = SLOT_UNITS + VUNITS;
+  // two buffers as separate arrays, so the compiler sees that reads of one do
+  // not wait for copies into the other
+  __shared__ __attribute__((aligned(16))) uint4 opsA[UNITS * 64];
+  __shared__ __attribute__((aligned(16))) uint4 opsB[UNITS * 64];
   constexpr int PARTS = 8 / WAVES;
   const int H = a.H;
   // workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8): keep
@@ -572,20 +639,63 @@ __global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArg
   if (pair >= a.N * H) return;
   const int n = pair / H, h = pair - n * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
-  const int col0 = 16 * (part * WAVES + w);
 
   const SeqInfo si = seq_info(a, n);
   const int64_t base = a.cu_seqlens ? (int64_t)a.seg_base[n] : (int64_t)n * a.slots_per_seq;
   int nseg = si.nseg;
   if (base + nseg > a.slot_bound) nseg = base >= a.slot_bound ? 0 : (int)(a.slot_bound - base);
-  const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q;
+  auto geometry = [&](int jseg, int& off, int64_t& tok0) {
+    int lo, hi;
+    seg_range(si, jseg, lo, hi);
+    off = CH - (hi - lo);
+    tok0 = si.bos + lo - off;
+  };
 
+  if (w >= WAVES) {
+    // ---- copy waves: unit u of the slot (or of the V block) goes to copy wave u % WAVES
+    const int cw = w - WAVES;
+    auto copy = [&](int jseg, uint4* dst) {
+      const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
+      for (int u = cw; u < SLOT_UNITS; u += WAVES)
+        __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
+      // V rows 0..63 (rows before the segment read row `off`, zeroed on use)
+      int off;
+      int64_t tok0;
+      geometry(jseg, off, tok0);
+      constexpr int LPR = VW / 8, RPI = 64 / LPR;  // lanes per row, rows per unit
+      for (int k = cw; k < VUNITS; k += WAVES) {
+        const int row = max(k * RPI + lane / LPR, off);
+        const uint16_t* vsrc = a.v + ((size_t)(tok0 + row) * H + h) * DK + VW * part + 8 * (lane % LPR);
+        __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS + k) * 64, 16, 0, 0);
+      }
+    };
+    if (nseg > 0) copy(0, opsA);
+    for (int jseg = 0; jseg < nseg; jseg += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+      __syncthreads();
+      if (jseg + 1 < nseg) copy(jseg + 1, opsB);
+      if (jseg + 1 < nseg) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (jseg + 2 < nseg) copy(jseg + 2, opsA);
+      }
+    }
+    return;
+  }
+
+  // ---- compute waves
+  const int col0 = 16 * (part * WAVES + w);
+  const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q;
   f32x4 S[8];
+  if (a.s0) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[m][e] = a.s0 ? a.s0[sbase + (size_t)(16 * m + 4 * g4 + e) * DK] : 0.f;
+      for (int e = 0; e < 4; ++e) S[m][e] = a.s0[sbase + (size_t)(16 * m + 4 * g4 + e) * DK];
+  } else {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
   auto store_state = [&](float* dst) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -594,38 +704,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArg
   };
   if (a.ckpt_off && si.p == 0) store_state(a.ckpt);
 
-  auto issue_ops = [&](int jseg, uint4* dst) {
-    const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
-    for (int u = w; u < SLOT_UNITS; u += WAVES)
-      __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
-  };
-  auto geometry = [&](int jseg, int& off, int64_t& tok0) {
-    int lo, hi;
-    seg_range(si, jseg, lo, hi);
-    off = CH - (hi - lo);
-    tok0 = si.bos + lo - off;
-  };
-  // V of a segment in accumulator order: rows 16 t + 4 g4 + e, column col0 + q.
-  // Rows before the segment load row `off` instead (always inside the
-  // sequence) and are zeroed where they are used, so no load waits on a branch.
-  auto load_v = [&](int jseg, uint32_t (&vv)[16]) {
-    int off;
-    int64_t tok0;
-    geometry(jseg, off, tok0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = max(16 * t + 4 * g4 + e, off);
-        vv[4 * t + e] = a.v[((size_t)(tok0 + r0) * H + h) * DK + col0 + q];
-      }
-  };
-
   const float scale = a.scale;
-  uint32_t vcur[16], vnxt[16], opk[8];
+  uint32_t opk[8];
   int poff = CH;
   int64_t ptok = 0;
   bool pend = false;
+  // O^T tile t of the previous segment: lane holds token 16 t + q, columns
+  // col0 + 4 g4 .. + 3 (one 8-byte store per tile)
   auto store_out = [&]() {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -636,20 +721,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArg
     }
   };
 
-  auto step = [&](int jseg, const uint4* cur, uint4* nxt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies and V loads landed
-    __syncthreads();                     // ... and every other wave's
+  auto step = [&](int jseg, const uint4* cur) {
+    __syncthreads();  // the copy waves have filled `cur`
     if (pend) store_out();
-    if (jseg + 1 < nseg) {
-      issue_ops(jseg + 1, nxt);
-      load_v(jseg + 1, vnxt);
-    }
     auto frag = [&](int byte_off) { return __builtin_bit_cast(bf16x8, cur[(byte_off >> 4) + lane]); };
-    auto f4 = [&](int byte_off) { return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off); };
+    auto f4 = [&](int byte_off) {
+      return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off);
+    };
+    const uint16_t* vblk = reinterpret_cast<const uint16_t*>(cur + SLOT_UNITS * 64);
 
     bf16x8 Sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) Sb[b] = acc_pair(S[2 * b], S[2 * b + 1]);
+    // X = K~ S and O^T = S^T Q~^T
     f32x4 X[4], O[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -675,7 +759,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArg
       const float bv[4] = {bt.x, bt.y, bt.z, bt.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float vx = (16 * t + 4 * g4 + e >= off) ? bf2f(vcur[4 * t + e]) : 0.f;
+        const int row = 16 * t + 4 * g4 + e;
+        // unconditional LDS read, masked (a conditional read would branch)
+        const uint32_t keep = row >= off ? 0xffffffffu : 0u;
+        const float vx = __uint_as_float(((uint32_t)vblk[row * VW + 16 * w + q] << 16) & keep);
         U[t][e] = bv[e] * (vx - X[t][e]);
       }
     }
@@ -730,17 +817,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void kda_recurrence_kernel(DecompArg
       seg_range(si, jseg, lo, hi);
       if (hi == si.p) store_state(a.ckpt);
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) vcur[e] = vnxt[e];
   };
 
-  if (nseg > 0) {
-    issue_ops(0, opsA);
-    load_v(0, vcur);
-  }
   for (int jseg = 0; jseg < nseg; jseg += 2) {
-    step(jseg, opsA, opsB);
-    if (jseg + 1 < nseg) step(jseg + 1, opsB, opsA);
+    step(jseg, opsA);
+    if (jseg + 1 < nseg) step(jseg + 1, opsB);
   }
   if (pend) store_out();
   if (a.final_state) store_state(a.final_state);
@@ -751,7 +832,7 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
   constexpr int PARTS = 8 / WAVES;
   const int64_t pairs = (int64_t)a.N * a.H;
   const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * PARTS));
-  hipLaunchKernelGGL(kda_recurrence_kernel<WAVES>, grid, dim3(64 * WAVES), 0, stream, a);
+  hipLaunchKernelGGL(kda_recurrence_kernel<WAVES>, grid, dim3(128 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -769,7 +850,6 @@ hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots,
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   switch (vsplit) {
-    case 1: return launch_recurrence<8>(a, stream);
     case 2: return launch_recurrence<4>(a, stream);
     case 4: return launch_recurrence<2>(a, stream);
     case 8: return launch_recurrence<1>(a, stream);

@@ -176,10 +176,10 @@ def test_workspace_rules():
     assert val(dec, ws, need) == OK
     assert val(prob_for(b), 0, 0) == OK                # AUTO falls back to FUSED
     assert val(prob_for(b), ws, need) == OK
-    assert val(prob_for(b, value_split=8), 0, 0) == WS  # split 1 / 8 exist only in DECOMP
+    assert val(prob_for(b, value_split=8), 0, 0) == WS  # split 8 exists only in DECOMP
     assert val(prob_for(b, variant="fused", value_split=8), 0, 0) == UNSUPPORTED
-    assert val(prob_for(b, variant="fused", value_split=1), ws, need) == UNSUPPORTED
-    for vs in (1, 2, 4, 8):
+    assert val(prob_for(b, variant="decomp", value_split=1), ws, need) == UNSUPPORTED
+    for vs in (2, 4, 8):
         assert val(prob_for(b, variant="decomp", value_split=vs), ws, need) == OK
     assert val(dec, ws + 8, need) == ALIGN
     # the workspace overlaps nothing the call reads or writes
