@@ -697,10 +697,14 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
     for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   auto store_state = [&](float* dst) {
+    // the row pointer is made opaque so the 32 store addresses are formed
+    // here, not kept live in registers across the segment loop
+    float* rowp = dst + sbase + (size_t)(4 * g4) * DK;
+    asm volatile("" : "+v"(rowp));
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[sbase + (size_t)(16 * m + 4 * g4 + e) * DK] = S[m][e];
+      for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = S[m][e];
   };
   if (a.ckpt_off && si.p == 0) store_state(a.ckpt);
 
@@ -724,55 +728,105 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
   auto step = [&](int jseg, const uint4* cur) {
     __syncthreads();  // the copy waves have filled `cur`
     if (pend) store_out();
-    auto frag = [&](int byte_off) { return __builtin_bit_cast(bf16x8, cur[(byte_off >> 4) + lane]); };
+    // An opaque copy of the lane index, renewed every segment: LDS addresses
+    // become one register plus an immediate offset instead of dozens of
+    // precomputed addresses kept live across the loop.
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    const int qq = lq & 15, gg = lq >> 4;
+    auto frag = [&](int byte_off) { return __builtin_bit_cast(bf16x8, cur[(byte_off >> 4) + lq]); };
     auto f4 = [&](int byte_off) {
       return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off);
     };
     const uint16_t* vblk = reinterpret_cast<const uint16_t*>(cur + SLOT_UNITS * 64);
 
+    // The segment runs as load batches and matrix batches separated by
+    // scheduling fences: fragment reads go out together and are consumed while
+    // the next batch is in flight (without the fences the reads are issued one
+    // at a time, each waited for before its product).
+#define KDA_FENCE() __builtin_amdgcn_sched_barrier(0)
+    bf16x8 fk[16], fq[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        fk[t * 4 + b] = frag(SL_KT + (t * 4 + b) * 1024);
+        fq[t * 4 + b] = frag(SL_QT + (t * 4 + b) * 1024);
+      }
+    float4 bt4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bt4[t] = f4(SL_BETA + (16 * t + 4 * gg) * 4);
     bf16x8 Sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) Sb[b] = acc_pair(S[2 * b], S[2 * b + 1]);
-    // X = K~ S and O^T = S^T Q~^T
+    KDA_FENCE();
+    // X = K~ S, key blocks 0-1; the rest of K~ is read meanwhile
     f32x4 X[4], O[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      X[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4], Sb[0], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) X[t] = mfma(frag(SL_KT + (t * 4 + b) * 1024), Sb[b], X[t]);
+      for (int b = 2; b < 4; ++b) fk[t * 4 + b] = frag(SL_KT + (t * 4 + b) * 1024);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4 + 1], Sb[1], X[t]);
+    KDA_FENCE();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[b], frag(SL_QT + (t * 4 + b) * 1024), O[t]);
-    // Y = beta (V - X), kept in U; U = Y + N Y
+    for (int b = 2; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4 + b], Sb[b], X[t]);
+    KDA_FENCE();
+    // the rest of Q~, the V block and N, read while O^T = S^T Q~^T starts
     int off;
     int64_t tok0;
     geometry(jseg, off, tok0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 2; b < 4; ++b) fq[t * 4 + b] = frag(SL_QT + (t * 4 + b) * 1024);
+    uint16_t vv[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[4 * t + e] = vblk[(16 * t + 4 * gg + e) * VW + 16 * w + qq];
+    bf16x8 fn[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) fn[i] = frag(SL_N + i * 1024);
+    KDA_FENCE();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[0], fq[t * 4], (f32x4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int b = 1; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[b], fq[t * 4 + b], O[t]);
+    KDA_FENCE();
+    // Y = beta (V - X), kept in U; U = Y + N Y.  Rows before the segment are
+    // masked to zero (the read above is unconditional).
     f32x4 U[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float4 bt = f4(SL_BETA + (16 * t + 4 * g4) * 4);
-      const float bv[4] = {bt.x, bt.y, bt.z, bt.w};
+      const float bv[4] = {bt4[t].x, bt4[t].y, bt4[t].z, bt4[t].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 16 * t + 4 * g4 + e;
-        // unconditional LDS read, masked (a conditional read would branch)
-        const uint32_t keep = row >= off ? 0xffffffffu : 0u;
-        const float vx = __uint_as_float(((uint32_t)vblk[row * VW + 16 * w + q] << 16) & keep);
+        const uint32_t keep = 16 * t + 4 * g4 + e >= off ? 0xffffffffu : 0u;
+        const float vx = __uint_as_float(((uint32_t)vv[4 * t + e] << 16) & keep);
         U[t][e] = bv[e] * (vx - X[t][e]);
       }
     }
     const bf16x8 Y0 = acc_pair(U[0], U[1]), Y1 = acc_pair(U[2], U[3]);
-    U[0] = mfma(frag(SL_N + tri_frag(0, 0) * 1024), Y0, U[0]);
-    U[1] = mfma(frag(SL_N + tri_frag(1, 0) * 1024), Y0, U[1]);
-    U[2] = mfma(frag(SL_N + tri_frag(2, 0) * 1024), Y0, U[2]);
-    U[2] = mfma(frag(SL_N + tri_frag(2, 1) * 1024), Y1, U[2]);
-    U[3] = mfma(frag(SL_N + tri_frag(3, 0) * 1024), Y0, U[3]);
-    U[3] = mfma(frag(SL_N + tri_frag(3, 1) * 1024), Y1, U[3]);
+    U[0] = mfma(fn[tri_frag(0, 0)], Y0, U[0]);
+    U[1] = mfma(fn[tri_frag(1, 0)], Y0, U[1]);
+    U[2] = mfma(fn[tri_frag(2, 0)], Y0, U[2]);
+    U[3] = mfma(fn[tri_frag(3, 0)], Y0, U[3]);
+    U[2] = mfma(fn[tri_frag(2, 1)], Y1, U[2]);
+    U[3] = mfma(fn[tri_frag(3, 1)], Y1, U[3]);
+    // M and the first half of K^, read while N Y runs
+    bf16x8 fm[6], fh[16];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) fm[i] = frag(SL_M + i * 1024);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fh[i] = frag(SL_KH + i * 1024);
+    KDA_FENCE();
     bf16x8 Uh[2], Ul[2];
     acc_pair_split(U[0], U[1], Uh[0], Ul[0]);
     acc_pair_split(U[2], U[3], Uh[1], Ul[1]);
@@ -782,28 +836,35 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         if (2 * b > t) continue;
-        const bf16x8 mf = frag(SL_M + tri_frag(t, b) * 1024);
-        O[t] = mfma(Uh[b], mf, O[t]);
-        O[t] = mfma(Ul[b], mf, O[t]);
+        O[t] = mfma(Uh[b], fm[tri_frag(t, b)], O[t]);
+        O[t] = mfma(Ul[b], fm[tri_frag(t, b)], O[t]);
       }
+    // second half of K^, the K^ lo fragments and Gam, read while M U runs
+#pragma unroll
+    for (int i = 8; i < 16; ++i) fh[i] = frag(SL_KH + i * 1024);
+    uint2 kl[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      kl[m] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_KL + m * 512 + lq * 8);
+    float4 gm[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
+    KDA_FENCE();
     // S <- diag(Gam) S + K^^T U
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float4 gm = f4(SL_GAM + (16 * m + 4 * g4) * 4);
-      S[m][0] *= gm.x;
-      S[m][1] *= gm.y;
-      S[m][2] *= gm.z;
-      S[m][3] *= gm.w;
-      const bf16x8 k0 = frag(SL_KH + (m * 2 + 0) * 1024);
-      const bf16x8 k1 = frag(SL_KH + (m * 2 + 1) * 1024);
-      const uint2 kl = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_KL + m * 512 + lane * 8);
-      const bf16x8 klf = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, kl.x, kl.y));
-      S[m] = mfma(k0, Uh[0], S[m]);
-      S[m] = mfma(k0, Ul[0], S[m]);
-      S[m] = mfma(k1, Uh[1], S[m]);
-      S[m] = mfma(k1, Ul[1], S[m]);
+      S[m][0] *= gm[m].x;
+      S[m][1] *= gm[m].y;
+      S[m][2] *= gm[m].z;
+      S[m][3] *= gm[m].w;
+      const bf16x8 klf = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, kl[m].x, kl[m].y));
+      S[m] = mfma(fh[2 * m], Uh[0], S[m]);
+      S[m] = mfma(fh[2 * m], Ul[0], S[m]);
+      S[m] = mfma(fh[2 * m + 1], Uh[1], S[m]);
+      S[m] = mfma(fh[2 * m + 1], Ul[1], S[m]);
       S[m] = mfma(klf, Uh[1], S[m]);
     }
+#undef KDA_FENCE
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       opk[2 * t] = pack2(scale * O[t][0], scale * O[t][1]);
