@@ -82,7 +82,7 @@ size_t decomp_bytes(const kda_problem* p) {
 // and a slice of the state's columns, and repeats the chunk preparation; two
 // workgroups per pair, four when there are too few pairs to occupy half the
 // CUs.  DECOMP: the recurrence workgroup holds two slot buffers in LDS, so one
-// runs per CU; split the columns as far as the CUs allow.  AUTO takes DECOMP
+// runs per CU; two workgroups per pair.  AUTO takes DECOMP
 // whenever the workspace holds it (value_split 8 is DECOMP-only, 2 and 4 exist
 // in both).
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
@@ -99,9 +99,10 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
   } else if (var == KDA_VARIANT_FUSED) {
     *vsplit = (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
   } else {
-    int v = 2;
-    while (v < 8 && cus > 0 && pairs * v * 2 <= cus) v *= 2;
-    *vsplit = v;
+    // measured on MI355X (256 CUs): two workgroups per pair is best from 12 to
+    // 384 pairs (B1 and B8 at T = 8192, B32 at T = 512); more splits add slot
+    // copies faster than they remove work per workgroup
+    *vsplit = 2;
   }
 }
 

@@ -210,10 +210,11 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Launch 1: prepare.  One workgroup of 4 waves per (slot, head); wave i owns
-// the 16-row block i of the tile.
+// Launch 1: prepare.  One workgroup of 4 waves per (slot, head).  Wave i owns
+// the 16-row block i of the tile and works in the lane order of the matrix
+// fragments throughout: lane l = 16 g + q holds row 16 i + q and, for key
+// block b, the 8 channels kidx(b, g, 0..7).
 
-constexpr int P_GP = DK + 4;    // fp32 pitch of the cumulative-sum tile
 constexpr int P_LP = CH + 4;    // fp32 pitch of L and T
 // per-channel factor rows
 constexpr int F_BT = 0;         // bt_0..3 (block sums of g)
@@ -224,6 +225,10 @@ constexpr int F_W20 = 14;       // exp(bt_1)
 constexpr int F_W31 = 15;       // exp(bt_2)
 constexpr int F_W30 = 16;       // exp(bt_1 + bt_2)
 constexpr int F_ROWS = 17;
+// k exp(bt_j - Gl_s) of row blocks 0..2 (fp32 [block][row][channel]); after
+// the gated products the same space holds T (pitch P_LP) and solve scratch
+constexpr int P_E_FLOATS = CH * P_LP + 4 * 512;
+static_assert(P_E_FLOATS >= 3 * 16 * DK, "prepare LDS layout");
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -231,23 +236,32 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// the 8 channels of key block b of this lane: two runs of 4 at p + off, p + off + 16
 __device__ __forceinline__ void load8_f32(const float* p, float (&x)[8], int off) {
   const float4 a = *reinterpret_cast<const float4*>(p + off);
   const float4 b = *reinterpret_cast<const float4*>(p + off + 16);
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
+__device__ __forceinline__ void store8_f32(float* p, const float (&x)[8], int off) {
+  *reinterpret_cast<float4*>(p + off) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + off + 16) = make_float4(x[4], x[5], x[6], x[7]);
+}
 __device__ __forceinline__ void unpack8(const uint2 (&u)[2], float (&x)[8]) {
   x[0] = lo_of(u[0].x); x[1] = hi_of(u[0].x); x[2] = lo_of(u[0].y); x[3] = hi_of(u[0].y);
   x[4] = lo_of(u[1].x); x[5] = hi_of(u[1].x); x[6] = lo_of(u[1].y); x[7] = hi_of(u[1].y);
 }
+// value of lane q - n of this 16-lane row (0 for q < n)
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
 
 __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
-  __shared__ __attribute__((aligned(16))) float sG[CH * P_GP];        // Gl; later T (pitch P_LP)
   __shared__ __attribute__((aligned(16))) float sF[F_ROWS * DK];
+  __shared__ __attribute__((aligned(16))) float sE[P_E_FLOATS];
   __shared__ __attribute__((aligned(16))) float sL[CH * P_LP];        // beta_r A[r,s]
   __shared__ __attribute__((aligned(16))) float sB[CH];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[(16 + 4) * 512]; // K^ fragments, then scratch
 
   const int H = a.H;
   const int64_t bid = blockIdx.x;
@@ -279,17 +293,16 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
   unsigned char* slot = a.slots + (size_t)bid * kDecompSlotBytes;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
+  const int i = w;
+  const int r = 16 * i + q;
 
-  // All global loads below are unconditional: a row before the segment
-  // (r < off) reads row `off` instead, which is always inside it, and the
-  // value is zeroed where it is used.  (A load under a per-lane condition would
-  // make the compiler wait for it before the branch joins.)
-  //
-  // A-side rows of this wave: r = 16 w + q; prefetch k and q (8 channels per block)
-  const int r = 16 * w + q;
+  // (0) Loads.  All are unconditional: a row before the segment (r < off)
+  // reads row `off` instead, which is inside it, and is zeroed where used (a
+  // load under a per-lane condition makes the compiler wait before the join).
   const bool rv = r >= off;
   const size_t erow = ((size_t)(tok0 + max(r, off)) * H + h) * DK;
   uint2 kA[4][2], qA[4][2];
+  float4 gA[4][2];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -297,63 +310,36 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
       const int ch = 32 * b + 16 * hh + 4 * g4;
       kA[b][hh] = *reinterpret_cast<const uint2*>(a.k + erow + ch);
       qA[b][hh] = *reinterpret_cast<const uint2*>(a.q + erow + ch);
+      gA[b][hh] = *reinterpret_cast<const float4*>(a.g + erow + ch);
     }
   const float beta_ld = a.beta[(size_t)(tok0 + max(tid & (CH - 1), off)) * H + h];
-  // B-side rows of the earlier blocks jb < w: s = 16 jb + q
-  uint2 kB[3][4][2];
-#pragma unroll
-  for (int jb = 0; jb < 3; ++jb) {
-    if (jb >= w) continue;
-    const size_t es = ((size_t)(tok0 + max(16 * jb + q, off)) * H + h) * DK;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        kB[jb][b][hh] = *reinterpret_cast<const uint2*>(a.k + es + 32 * b + 16 * hh + 4 * g4);
-  }
 
-  // (1) cumulative gate sums inside 16-row blocks.  Thread -> 4 channels
-  // (4 cg ..) and 8 rows (8 rg ..); the odd half of a block adds the even
-  // half's total, taken from lane - 32 of the same wave.
-  {
-    const int cg = tid & 31, rg = tid >> 5;
-    float4 gv[8];
+  // Gl: cumulative sum of g over the rows of the block, for this lane's 32
+  // channels -- an inclusive scan over the 16 lanes of a DPP row (lane q = row q)
+  float gl[4][8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float4 u = gA[b][0], v = gA[b][1];
+    const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int row = 8 * rg + e;
-      gv[e] = *reinterpret_cast<const float4*>(a.g + ((size_t)(tok0 + max(row, off)) * H + h) * DK + 4 * cg);
+      float y = rv ? x[e] : 0.f;
+      y += row_shr<1>(y);
+      y += row_shr<2>(y);
+      y += row_shr<4>(y);
+      y += row_shr<8>(y);
+      gl[b][e] = y;
     }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = 8 * rg + e >= off;
-      acc.x += ok ? gv[e].x : 0.f;
-      acc.y += ok ? gv[e].y : 0.f;
-      acc.z += ok ? gv[e].z : 0.f;
-      acc.w += ok ? gv[e].w : 0.f;
-      gv[e] = acc;
-    }
-    // totals of the even half (lanes 0..31 of this wave) to the odd half (lanes 32..63)
-    const float px = __shfl(acc.x, lane & 31, 64), py = __shfl(acc.y, lane & 31, 64);
-    const float pz = __shfl(acc.z, lane & 31, 64), pw = __shfl(acc.w, lane & 31, 64);
-    const bool odd = rg & 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float4 v = gv[e];
-      if (odd) {
-        v.x += px;
-        v.y += py;
-        v.z += pz;
-        v.w += pw;
-      }
-      *reinterpret_cast<float4*>(&sG[(8 * rg + e) * P_GP + 4 * cg]) = v;
-      if (odd && e == 7) *reinterpret_cast<float4*>(&sF[(F_BT + (rg >> 1)) * DK + 4 * cg]) = v;
-    }
-    if (tid < CH) sB[tid] = tid >= off ? beta_ld : 0.f;
   }
+  // block sums (row 15 of the block) and beta to LDS
+  if (q == 15) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) store8_f32(sF, gl[b], (F_BT + i) * DK + 32 * b + 4 * g4);
+  }
+  if (tid < CH) sB[tid] = tid >= off ? beta_ld : 0.f;
   __syncthreads();
 
-  // (2) per-channel block factors; Gam and beta go straight to the slot
+  // (1) per-channel block factors; Gam and beta go straight to the slot
   if (tid < DK) {
     const int d = tid;
     const float b0 = sF[F_BT * DK + d], b1 = sF[(F_BT + 1) * DK + d];
@@ -377,14 +363,26 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
   }
   __syncthreads();
 
-  // (3) wave i = w: operands of row block i, gated products of blocks (i, j <= i)
-  const int i = w;
+  // (2) wave i: operands of row block i and the diagonal block (i, i).
+  // Identity slices that transpose a K^ tile with one exact matrix product:
+  // lane 16 g + n holds 1.0 at element 4 h + n % 4 when n / 4 == g.
+  bf16x8 eye[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+    const int el = 4 * hh + (q & 3);
+    const bool on = (q >> 2) == g4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (on && el == e) wv[e >> 1] |= 0x3f80u << (16 * (e & 1));
+    eye[hh] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+  }
   const float beta_r = sB[r];
   bf16x8 aK[4], aQ[4], aQl[4], bD[4], bDl[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int ch0 = 32 * b + 4 * g4;
-    float kf[8], qf[8], gl[8], bt[8], fac[8];
+    float kf[8], qf[8], bt[8], fac[8];
     unpack8(kA[b], kf);
     unpack8(qA[b], qf);
 #pragma unroll
@@ -392,15 +390,14 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
       kf[e] = rv ? kf[e] : 0.f;
       qf[e] = rv ? qf[e] : 0.f;
     }
-    load8_f32(sG, gl, r * P_GP + ch0);
     load8_f32(sF, bt, (F_BT + i) * DK + ch0);
-    float ef[8], eb[8], Kf[8], Qf[8];
+    float Kf[8], Qf[8], kb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ef[e] = __expf(gl[e]);
-      eb[e] = __expf(bt[e] - gl[e]);
-      Kf[e] = kf[e] * ef[e];
-      Qf[e] = qf[e] * ef[e];
+      const float ef = __expf(gl[b][e]);             // exp(G_r - G_{16i-1}) <= 1
+      kb[e] = kf[e] * __expf(bt[e] - gl[b][e]);      // k exp(G_{16i+15} - G_r), <= |k|
+      Kf[e] = kf[e] * ef;
+      Qf[e] = qf[e] * ef;
     }
     aK[b] = to_bf16x8(Kf);
     split8(Qf, aQ[b], aQl[b]);
@@ -422,30 +419,41 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     }
     *reinterpret_cast<bf16x8*>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(kt);
     *reinterpret_cast<bf16x8*>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(qt);
-    // diagonal-block right operand k exp(-Gl) = k Eb / bd_i, hi + lo
+    // k exp(bt - Gl) of this block for the later waves' off-diagonal products
+    if (i < 3) store8_f32(sE, kb, (i * 16 + q) * DK + ch0);
+    // diagonal-block right operand k exp(-Gl) = k exp(bt - Gl) exp(-bt), hi + lo
     load8_f32(sF, fac, (F_IBD + i) * DK + ch0);
     float kr[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kr[e] = kf[e] * eb[e] * fac[e];
+    for (int e = 0; e < 8; ++e) kr[e] = kb[e] * fac[e];
     split8(kr, bD[b], bDl[b]);
-    // K^ = k exp(G_end - G_r) = k Eb R_i, scattered into the K^^T fragments
+    // K^ = k exp(G_end - G_r) = k exp(bt_i - Gl) R_i; transposed into K^^T
+    // fragments by products with the identity slices (exact: one nonzero
+    // bf16 term per output), stored as the half of each fragment that token
+    // tile i fills
     float kh[8];
     if (i < 3) {
       load8_f32(sF, fac, (F_R + i) * DK + ch0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kh[e] = kf[e] * eb[e] * fac[e];
+      for (int e = 0; e < 8; ++e) kh[e] = kb[e] * fac[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kh[e] = kf[e] * eb[e];
+      for (int e = 0; e < 8; ++e) kh[e] = kb[e];
     }
-    const int tb = i >> 1, ep = 4 * (i & 1) + (q & 3), lg = (q >> 2) * 16;
+    bf16x8 khi, klo;
+    split8(kh, khi, klo);
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ch = ch0 + 16 * (e >> 2) + (e & 3);
-      const int m = ch >> 4, lp = lg + (ch & 15);
-      const uint32_t hb16 = pack2(kh[e], 0.f) & 0xffffu;
-      sK[((m * 2 + tb) * 64 + lp) * 8 + ep] = (uint16_t)hb16;
-      if (i == 3) sK[8192 + (m * 64 + lp) * 4 + (q & 3)] = (uint16_t)(pack2(kh[e] - bf2f(hb16), 0.f) & 0xffffu);
+    for (int hh = 0; hh < 2; ++hh) {
+      const int m = 2 * b + hh;
+      const f32x4 th = mfma(khi, eye[hh], z4);
+      *reinterpret_cast<uint2*>(slot + SL_KH + ((m * 2 + (i >> 1)) * 64 + lane) * 16 + 8 * (i & 1)) =
+          make_uint2(pack2(th[0], th[1]), pack2(th[2], th[3]));
+      if (i == 3) {
+        const f32x4 tl = mfma(klo, eye[hh], z4);
+        *reinterpret_cast<uint2*>(slot + SL_KL + m * 512 + lane * 8) =
+            make_uint2(pack2(tl[0], tl[1]), pack2(tl[2], tl[3]));
+      }
     }
   }
 
@@ -476,39 +484,32 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     for (int jj = 0; jj < 4; ++jj)
       if (jj == i) macc[jj] = m0;
   }
-  // off-diagonal blocks (i, jb < i)
+  __syncthreads();
+
+  // (3) off-diagonal blocks (i, jb < i): right operand k exp(bt_jb - Gl_s) W_{i,jb}
+  // from LDS, W = prod_{jb<m<i} exp(bt_m)
 #pragma unroll
   for (int jb = 0; jb < 3; ++jb) {
     if (jb >= i) continue;
-    const int srow = 16 * jb + q;
-    const bool sv = srow >= off;
     f32x4 aacc = {0.f, 0.f, 0.f, 0.f};
     f32x4 m1 = {0.f, 0.f, 0.f, 0.f};
+    const int wrow = (jb == i - 1) ? -1 : (i == 2 ? F_W20 : (jb == 1 ? F_W31 : F_W30));
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int ch0 = 32 * b + 4 * g4;
-      float ks[8], gl[8], bt[8], wf[8];
-      unpack8(kB[jb][b], ks);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ks[e] = sv ? ks[e] : 0.f;
-      load8_f32(sG, gl, srow * P_GP + ch0);
-      load8_f32(sF, bt, (F_BT + jb) * DK + ch0);
-      const int wrow = (jb == i - 1) ? -1 : (i == 2 ? F_W20 : (jb == 1 ? F_W31 : F_W30));
+      float ks[8], wf[8];
+      load8_f32(sE, ks, (jb * 16 + q) * DK + ch0);
       if (wrow >= 0) {
         load8_f32(sF, wf, wrow * DK + ch0);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wf[e] = 1.f;
+        for (int e = 0; e < 8; ++e) ks[e] *= wf[e];
       }
-      float kb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kb[e] = ks[e] * __expf(bt[e] - gl[e]) * wf[e];
-      const bf16x8 bb = to_bf16x8(kb);
+      const bf16x8 bb = to_bf16x8(ks);
       aacc = mfma(bb, aK[b], aacc);
       m1 = mfma(bb, aQ[b], m1);
     }
-    float4 lv = make_float4(beta_r * aacc[0], beta_r * aacc[1], beta_r * aacc[2], beta_r * aacc[3]);
-    *reinterpret_cast<float4*>(&sL[r * P_LP + 16 * jb + 4 * g4]) = lv;
+    *reinterpret_cast<float4*>(&sL[r * P_LP + 16 * jb + 4 * g4]) =
+        make_float4(beta_r * aacc[0], beta_r * aacc[1], beta_r * aacc[2], beta_r * aacc[3]);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
       if (jj == jb) macc[jj] = m1;
@@ -517,15 +518,13 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     if (2 * tb > i) continue;
-    const f32x4 lo4 = macc[2 * tb];
-    const f32x4 hi4 = (2 * tb + 1 <= i) ? macc[2 * tb + 1] : (f32x4){0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<bf16x8*>(slot + SL_M + (tri_frag(i, tb) * 64 + lane) * 16) = acc_pair(lo4, hi4);
+    *reinterpret_cast<bf16x8*>(slot + SL_M + (tri_frag(i, tb) * 64 + lane) * 16) =
+        acc_pair(macc[2 * tb], macc[2 * tb + 1]);
   }
   __syncthreads();
 
-  // (4) wave 0: T_bb = (I + L_bb)^-1 by forward substitution, lane = (block, column);
-  //     waves 1-3: K^ fragments to the slot
-  float* sT = sG;
+  // (4) T_bb = (I + L_bb)^-1 by forward substitution, lane = (block, column)
+  float* sT = sE;
   if (w == 0) {
     const int bb = lane >> 4, col = lane & 15;
     float x[16];
@@ -539,10 +538,6 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sT[(16 * bb + rr) * P_LP + 16 * bb + col] = x[rr];
-  } else {
-    const uint4* src = reinterpret_cast<const uint4*>(sK);
-    uint4* dst = reinterpret_cast<uint4*>(slot + SL_KH);
-    for (int u = tid - 64; u < 1280; u += 192) dst[u] = src[u];
   }
   __syncthreads();
 
@@ -552,7 +547,7 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
   // ll = columns 0..31: wave w writes block (2 + w / 2, w % 2) as
   //   T_ij = -sum_{p=2}^{i} T_ip Z_pj,   Z_pj = sum_{m=j}^{1} L_pm T_mj.
   const int rr = lane >> 2, c4 = 4 * (lane & 3);
-  float* sZ = reinterpret_cast<float*>(sK) + 512 * w;
+  float* sZ = sE + CH * P_LP + 512 * w;
   // Z = sum_{m=m0}^{m1-1} L[pb, m] T[m, jb] for this lane's row rr and columns c4..c4+3
   auto lt_prod = [&](int pb, int m0, int m1, int jb) {
     float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
