@@ -5,6 +5,8 @@ One step is one ``kda_prefill`` call -- the whole hot path (gate cumsum,
 gated K K^T / Q K^T, triangular solve, chunk recurrence, outputs, final
 state) -- over the B8 T8192 H12 K=V=128 bf16 workload with an fp32 initial
 state, inputs resident in HBM before timing starts.  Prints one JSON line.
+With the two-launch schedule, each launch is also timed on its own (the
+library's split-stage calls) for the roofline of the dominant kernel.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -27,18 +29,28 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, vendor figure
 # The pages' number for this shape (110-SM SM120, no initial state): 0.881 ms
 PAGES_TOKENS_PER_S = 8 * 8192 / 0.881e-3
-KERNEL_SOURCE = os.path.join(ROOT, "kda_gated_delta_chunked_amd", "csrc", "kda_fused.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_b8_t8192.json")
+CSRC = os.path.join(ROOT, "kda_gated_delta_chunked_amd", "csrc")
+KERNEL_SOURCES = {"fused": os.path.join(CSRC, "kda_fused.hip"), "decomp": os.path.join(CSRC, "kda_decomp.hip")}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_b8_t8192.json")
+MFMA_FLOPS = 16 * 16 * 32 * 2    # one v_mfma_f32_16x16x32_bf16
+
+
+def stage_bytes(p):
+    """Algorithmic HBM bytes of each launch of the two-launch schedule: the
+    prepare reads q, k (bf16), g (fp32) and beta; the recurrence reads v and
+    the initial state and writes out, the final state and checkpoints."""
+    th = p.T_total * p.H
+    state = 128 * 128 * 4 * p.N * p.H
+    n_states = (1 if p.initial_state is not None else 0) + 1 + (1 if p.ckpt_offsets is not None else 0)
+    return {"prepare": th * (128 * 2 * 2 + 128 * 4 + 4),
+            "recurrence": th * (128 * 2 * 2) + state * n_states}
 
 
 def algorithmic_bytes(p) -> int:
     """HBM bytes the method must move: q, k, v (bf16), g (fp32), beta (fp32)
-    in, out (bf16) written, and the fp32 state read and written per
-    (sequence, head)."""
-    th = p.T_total * p.H
-    per_token_head = 128 * 2 * 3 + 128 * 4 + 4 + 128 * 2
-    state = 128 * 128 * 4 * p.N * p.H
-    return th * per_token_head + state * ((1 if p.initial_state is not None else 0) + 1)
+    in, out (bf16) written, the fp32 state read and written per (sequence,
+    head), and checkpoint states written."""
+    return sum(stage_bytes(p).values())
 
 
 def algorithmic_flops(p) -> float:
@@ -50,13 +62,7 @@ def algorithmic_flops(p) -> float:
     return float(per) * p.T_total * p.H
 
 
-def executed_mfma_flops(p, vsplit: int) -> float:
-    """Flops of the v_mfma_f32_16x16x32_bf16 instructions the fused kernel
-    issues (hi/lo passes included), from its schedule: per workgroup and
-    segment, 112 for the gate products and 90 per 16-column tile for the
-    recurrence."""
-    ntile = 128 // vsplit // 16
-    per_wg_seg = 112 + 90 * ntile
+def segments(p) -> int:
     segs = 0
     for n in range(p.N):
         L = int(p.cu_seqlens[n + 1] - p.cu_seqlens[n])
@@ -66,25 +72,38 @@ def executed_mfma_flops(p, vsplit: int) -> float:
             if 0 < off < L and off % 64 != 0:
                 s += 1
         segs += s
-    return float(per_wg_seg * 16 * 16 * 32 * 2) * segs * p.H * vsplit
+    return segs
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def executed_mfma_flops(p, variant: str, vsplit: int) -> float:
+    """Flops of the v_mfma_f32_16x16x32_bf16 instructions the kernels issue
+    (hi/lo passes included), from their schedules."""
+    segs = segments(p)
+    if variant == "fused":
+        # per workgroup and segment: 112 for the gate products, 90 per 16-column tile
+        return float((112 + 90 * (128 // vsplit // 16)) * MFMA_FLOPS) * segs * p.H * vsplit
+    # prepare: 4 diagonal blocks x 16, 6 off-diagonal x 8, 40 transposes of K^;
+    # recurrence: 90 per 16 columns, 8 column tiles per (sequence, head)
+    return float((152 + 8 * 90) * MFMA_FLOPS) * segs * p.H
+
+
+def kernel_sha(variant: str) -> str:
+    with open(KERNEL_SOURCES[variant], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source; else None."""
+def measured_traffic(workload: str, variant: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256") != kernel_sha() or t.get("workload") != workload:
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_sha256") != kernel_sha(variant):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return e.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(p, sample_tokens: int):
@@ -116,7 +135,7 @@ def main() -> int:
     ap.add_argument("--workload", default="b8_t8192")
     ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--variant", default="auto", choices=["auto", "decomp", "fused"])
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, --steps times "
@@ -173,33 +192,63 @@ def main() -> int:
         if st != 0:
             raise K.KDAError(st, "kda_prefill")
 
+    def timed(fn, steps):
+        """Per-launch milliseconds from events on the call's stream, and wall ms per step."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])), wall
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_launch = float(np.mean(per_launch_ms))
-    ms_step = wall * 1e3 / args.steps
+    ms_launch, ms_step = timed(step, args.steps)
     tokens = p.T_total
     value = tokens / (ms_step * 1e-3)
 
-    alg_b = algorithmic_bytes(p)
-    achieved = alg_b / (ms_launch * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    # per-kernel times: the two launches of DECOMP enqueued by separate calls
+    kernels = {}
+    if variant == "decomp":
+        for st, kname in (("prepare", "kda_prepare_kernel"), ("recurrence", "kda_recurrence_kernel")):
+            sprob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, variant="decomp",
+                                   value_split=vsplit, stages=st)
+
+            def one(sprob=sprob):
+                rc = K.prefill_raw(sprob, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), ptr(s0),
+                                   ptr(out), ptr(fin), ptr(offs), ptr(ck), ptr(ws), ws_bytes,
+                                   stream.cuda_stream)
+                if rc != 0:
+                    raise K.KDAError(rc, "kda_prefill")
+            one()
+            kernels[kname] = {"stage": st, "ms": timed(one, max(5, args.steps // 2))[0]}
+        step()  # leave a complete result behind
+        torch.cuda.synchronize()
+        sb = stage_bytes(p)
+        for kname, e in kernels.items():
+            e["algorithmic_bytes"] = sb[e["stage"]]
+    else:
+        kernels["kda_fused_kernel"] = {"stage": "both", "ms": ms_launch,
+                                       "algorithmic_bytes": algorithmic_bytes(p)}
+    dom = max(kernels, key=lambda kk: kernels[kk]["ms"])
+    dk = kernels[dom]
+    achieved = dk["algorithmic_bytes"] / (dk["ms"] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "kda_fused_kernel", "kernel_ms": round(ms_launch, 4),
-            "algorithmic_bytes": alg_b}
-    ex_fl = executed_mfma_flops(p, vsplit)
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.workload, variant, dom),
+            "kernel": dom, "kernel_ms": round(dk["ms"], 4), "algorithmic_bytes": dk["algorithmic_bytes"]}
+    alg_b = algorithmic_bytes(p)
+    path = {"ms_per_call": round(ms_launch, 4), "algorithmic_bytes": alg_b,
+            "achieved_GBps": round(alg_b / (ms_launch * 1e-3) / 1e9, 1),
+            "frac_hbm": round(alg_b / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels_ms": {kk: round(e["ms"], 4) for kk, e in kernels.items()}}
+    ex_fl = executed_mfma_flops(p, variant, vsplit)
     alg_fl = algorithmic_flops(p)
     mfma = {"executed_tflops": round(ex_fl / (ms_launch * 1e-3) / 1e12, 1),
             "executed_util": round(ex_fl / (ms_launch * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
@@ -217,7 +266,7 @@ def main() -> int:
                       "initial_state": p.initial_state is not None,
                       "checkpoints": p.ckpt_offsets is not None,
                       "variant": variant, "value_split": vsplit},
-           "roofline": roof, "mfma": mfma}
+           "roofline": roof, "path": path, "mfma": mfma}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)

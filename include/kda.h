@@ -97,7 +97,15 @@ typedef struct {
                                 owning 128/value_split columns of the state: 2 or 4 for
                                 FUSED, 2, 4 or 8 for DECOMP (FlashInfer PR #4262,
                                 Physical schedules: value rows split over CTAs) */
+  int32_t stages;            /* DECOMP only (0 otherwise): which of its two launches to
+                                enqueue.  0 = both.  KDA_STAGE_PREPARE = only the chunk-
+                                parallel prepare, which fills the workspace.
+                                KDA_STAGE_RECURRENCE = only the recurrence, which reads a
+                                workspace that an earlier PREPARE call filled from the same
+                                inputs and problem (the caller's contract, not checked) */
 } kda_problem;
+
+enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
 
 /* Bytes of caller workspace kda_prefill needs for this problem (host only, no
  * device access).  FUSED needs none (0).  DECOMP, and AUTO so that it may

@@ -51,6 +51,8 @@ kda_status check_problem(const kda_problem* p) {
   const int vs = p->value_split;
   if (vs != 0 && vs != 2 && vs != 4 && vs != 8) return KDA_ERR_UNSUPPORTED;
   if (p->variant == KDA_VARIANT_FUSED && vs == 8) return KDA_ERR_UNSUPPORTED;
+  if (p->stages < 0 || p->stages > KDA_STAGE_RECURRENCE) return KDA_ERR_INVALID_ARG;
+  if (p->stages != 0 && p->variant != KDA_VARIANT_DECOMP) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if ((int64_t)p->num_seqs * p->num_heads > kInt32Max / 8) return KDA_ERR_TOO_LARGE;
@@ -231,7 +233,8 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.slot_bound = slots;
     a.scale = p->scale;
     const int64_t prepare_slots = cu_seqlens ? slots : (int64_t)p->num_seqs * a.slots_per_seq;
-    err = kda::launch_decomp(a, vsplit, prepare_slots, st_);
+    const int stages = p->stages ? p->stages : (KDA_STAGE_PREPARE | KDA_STAGE_RECURRENCE);
+    err = kda::launch_decomp(a, vsplit, prepare_slots, stages, st_);
   } else {
     kda::FusedArgs a;
     a.q = q;

@@ -894,17 +894,21 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, hipStream_t stream) {
+hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
+                         hipStream_t stream) {
   hipError_t err;
-  if (a.cu_seqlens) {
-    hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (stages & 1) {
+    if (a.cu_seqlens) {
+      hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const int64_t blocks = prepare_slots * a.H;
+    if (blocks > 0) {
+      hipLaunchKernelGGL(kda_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
-  const int64_t blocks = prepare_slots * a.H;
-  if (blocks > 0) {
-    hipLaunchKernelGGL(kda_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+  if (!(stages & 2)) return hipSuccess;
   switch (vsplit) {
     case 2: return launch_recurrence<4>(a, stream);
     case 4: return launch_recurrence<2>(a, stream);

@@ -71,6 +71,8 @@ inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, size_
 // vsplit = workgroups per (sequence, head): 1, 2, 4 or 8.  prepare_slots =
 // slots the prepare launch covers (fixed layout: N * slots_per_seq; packed:
 // slot_bound).
-hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, hipStream_t stream);
+// stages: bit 0 = the prepare launch (and the slot plan), bit 1 = the recurrence.
+hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
+                         hipStream_t stream);
 
 }  // namespace kda

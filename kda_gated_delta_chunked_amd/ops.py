@@ -41,16 +41,20 @@ class Problem(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
                 ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("gate_lower_bound", ctypes.c_float), ("variant", ctypes.c_int32),
-                ("value_split", ctypes.c_int32)]
+                ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32)]
+
+
+STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
 
 
 def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: float,
                  gate_lower_bound: float = -5.0, variant: str | int = "auto",
                  value_split: int = 0, head_dim_k: int = HEAD_DIM,
-                 head_dim_v: int = HEAD_DIM) -> Problem:
+                 head_dim_v: int = HEAD_DIM, stages: str | int = "both") -> Problem:
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    st = STAGES[stages] if isinstance(stages, str) else int(stages)
     return Problem(int(num_seqs), int(total_tokens), int(num_heads), int(head_dim_k),
-                   int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split))
+                   int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st)
 
 
 def library_path() -> str:

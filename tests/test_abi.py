@@ -189,6 +189,23 @@ def test_workspace_rules():
     assert val(dec, b.addr["q"], need) == OVERLAP
 
 
+def test_split_stages_rules():
+    b = Bufs()
+    need = decomp_bytes(b.N, b.T, b.H)
+    ws = 1 << 44
+
+    def val(p, wsp=ws, wsb=need):
+        return K.validate_raw(p, *b.args()[:-2], wsp, wsb)
+
+    for st in ("prepare", "recurrence"):
+        assert val(prob_for(b, variant="decomp", stages=st)) == OK
+        assert val(prob_for(b, variant="decomp", stages=st), 0, 0) == WS
+        assert val(prob_for(b, variant="fused", stages=st)) == UNSUPPORTED
+        assert val(prob_for(b, stages=st)) == UNSUPPORTED       # AUTO: the stages need DECOMP
+    assert val(prob_for(b, variant="decomp", stages=3)) == INVALID
+    assert val(prob_for(b, variant="decomp", stages=-1)) == INVALID
+
+
 def test_plan_picks_a_schedule_without_a_device():
     # no GPU here: the CU count reads as 0, and the choice is still valid
     var, vs = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="fused"))

@@ -177,3 +177,32 @@ def test_decomp_matches_fused_on_packed_layout_as_separate_runs():
         assert np.array_equal(one["out"], whole["out"][sl]), n
         assert np.array_equal(one["final"][0], whole["final"][n]), n
         t0 += L
+
+
+def test_split_stages_equal_one_call():
+    # the prepare launch and the recurrence launch enqueued by two calls give
+    # the same bits as one call
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    p = synth.make_problem([300, 0, 77, 129], 3, seed=16, init_state=True, ckpt=[5, 0, 77, 64])
+    d = to_device(p)
+    whole = run_gpu(p, variant="decomp", d=d)
+    dev = d["q"].device
+    N, H, T = p.N, p.H, p.T_total
+    out = torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    fin = torch.full((N, H, 128, 128), float("nan"), device=dev)
+    ck = torch.full((N, H, 128, 128), float("nan"), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    need = K.workspace_size(K.make_problem(N, T, H, scale=p.scale, variant="decomp"))
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
+    for st in ("prepare", "recurrence"):
+        prob = K.make_problem(N, T, H, scale=p.scale, variant="decomp", stages=st)
+        rc = K.prefill_raw(prob, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                           d["g"].data_ptr(), d["beta"].data_ptr(), d["cu"].data_ptr(),
+                           d["s0"].data_ptr(), out.data_ptr(), fin.data_ptr(), d["offs"].data_ptr(),
+                           ck.data_ptr(), ws.data_ptr(), need, stream.cuda_stream)
+        assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), whole["out"])
+    assert np.array_equal(fin.cpu().numpy(), whole["final"])
+    assert np.array_equal(ck.cpu().numpy(), whole["ckpt"], equal_nan=True)
