@@ -257,7 +257,7 @@ __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
-__global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
+__global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   __shared__ __attribute__((aligned(16))) float sF[F_ROWS * DK];
   __shared__ __attribute__((aligned(16))) float sE[P_E_FLOATS];
   __shared__ __attribute__((aligned(16))) float sL[CH * P_LP];        // beta_r A[r,s]
@@ -378,7 +378,10 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     eye[hh] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
   }
   const float beta_r = sB[r];
-  bf16x8 aK[4], aQ[4], aQl[4], bD[4], bDl[4];
+  // the diagonal block's products accumulate key block by key block, so its
+  // operands (Q hi/lo, right operand hi/lo) need not stay live
+  bf16x8 aK[4], aQ[4];
+  f32x4 adiag = {0.f, 0.f, 0.f, 0.f}, mdiag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int ch0 = 32 * b + 4 * g4;
@@ -400,7 +403,8 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
       Qf[e] = qf[e] * ef;
     }
     aK[b] = to_bf16x8(Kf);
-    split8(Qf, aQ[b], aQl[b]);
+    bf16x8 aQl;
+    split8(Qf, aQ[b], aQl);
     // K~ and Q~ fragments (row tile i, key block b)
     float kt[8], qt[8];
     if (i > 0) {
@@ -426,7 +430,12 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
     float kr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) kr[e] = kb[e] * fac[e];
-    split8(kr, bD[b], bDl[b]);
+    bf16x8 bD, bDl;
+    split8(kr, bD, bDl);
+    adiag = mfma(bD, aK[b], adiag);
+    mdiag = mfma(bD, aQ[b], mdiag);
+    mdiag = mfma(bDl, aQ[b], mdiag);
+    mdiag = mfma(bD, aQl, mdiag);
     // K^ = k exp(G_end - G_r) = k exp(bt_i - Gl) R_i; transposed into K^^T
     // fragments by products with the identity slices (exact: one nonzero
     // bf16 term per output), stored as the half of each fragment that token
@@ -460,15 +469,8 @@ __global__ __launch_bounds__(256, 2) void kda_prepare_kernel(DecompArgs a) {
   // diagonal block: A_ii^T (bf16) and M_ii^T (hi + lo), lane holds row r, s = 16 i + 4 g4 + e
   f32x4 macc[4];
   {
-    f32x4 aacc = {0.f, 0.f, 0.f, 0.f};
-    f32x4 m0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      aacc = mfma(bD[b], aK[b], aacc);
-      m0 = mfma(bD[b], aQ[b], m0);
-      m0 = mfma(bDl[b], aQ[b], m0);
-      m0 = mfma(bD[b], aQl[b], m0);
-    }
+    const f32x4 aacc = adiag;
+    f32x4 m0 = mdiag;
     float4 lv;
     float* lp = &lv.x;
 #pragma unroll
