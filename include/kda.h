@@ -110,8 +110,8 @@ enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
 /* Bytes of caller workspace kda_prefill needs for this problem (host only, no
  * device access).  FUSED needs none (0).  DECOMP, and AUTO so that it may
  * pick DECOMP, need a header of (N + 1) int32 rounded up to 256 bytes plus
- * 66,560 bytes per (segment slot, head), with floor(T_total / 64) + 2 N
- * segment slots: about 1.04 KiB per token-head.  The workspace is scratch:
+ * 64,512 bytes per (segment slot, head), with floor(T_total / 64) + 2 N
+ * segment slots: about 1.01 KiB per token-head.  The workspace is scratch:
  * it carries nothing between calls, may be reused by any later call on the
  * same stream, and must not be used by two calls in flight at once. */
 kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes);

@@ -49,8 +49,8 @@ kda_status check_problem(const kda_problem* p) {
       p->variant != KDA_VARIANT_DECOMP)
     return KDA_ERR_UNSUPPORTED;
   const int vs = p->value_split;
-  if (vs != 0 && vs != 2 && vs != 4 && vs != 8) return KDA_ERR_UNSUPPORTED;
-  if (p->variant == KDA_VARIANT_FUSED && vs == 8) return KDA_ERR_UNSUPPORTED;
+  if (vs != 0 && vs != 1 && vs != 2 && vs != 4 && vs != 8) return KDA_ERR_UNSUPPORTED;
+  if (p->variant == KDA_VARIANT_FUSED && (vs == 1 || vs == 8)) return KDA_ERR_UNSUPPORTED;
   if (p->stages < 0 || p->stages > KDA_STAGE_RECURRENCE) return KDA_ERR_INVALID_ARG;
   if (p->stages != 0 && p->variant != KDA_VARIANT_DECOMP) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
@@ -85,13 +85,13 @@ size_t decomp_bytes(const kda_problem* p) {
 // workgroups per pair, four when there are too few pairs to occupy half the
 // CUs.  DECOMP: the recurrence workgroup holds two slot buffers in LDS, so one
 // runs per CU; two workgroups per pair.  AUTO takes DECOMP
-// whenever the workspace holds it (value_split 8 is DECOMP-only, 2 and 4 exist
-// in both).
+// whenever the workspace holds it (value_split 1 and 8 are DECOMP-only, 2 and 4
+// exist in both).
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
   int32_t var = p->variant;
   if (var == KDA_VARIANT_AUTO) {
     var = ws_bytes >= decomp_bytes(p) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
-    if (var == KDA_VARIANT_FUSED && p->value_split == 8)
+    if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
       var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
   }
   *variant = var;

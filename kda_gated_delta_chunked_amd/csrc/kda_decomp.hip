@@ -61,11 +61,11 @@ constexpr int SL_KT = 0;        // K~  : row tile t (4) x key block b (4), A of 
 constexpr int SL_QT = 16384;    // Q~  : token tile t (4) x key block b (4), B of S^T Q~^T
 constexpr int SL_KH = 32768;    // K^ hi: key tile m (8) x token block b (2), A of K^^T U
 constexpr int SL_KL = 49152;    // K^ lo, tokens 48..63: key tile m (8), 8 bytes per lane
-constexpr int SL_M = 53248;     // M  : token tile t x token block b <= t/2 (6 fragments)
-constexpr int SL_N = 59392;     // N  : same tiling as M
-constexpr int SL_GAM = 65536;   // exp(G_end), 128 fp32
-constexpr int SL_BETA = 66048;  // beta per tile row, 64 fp32 (0 on empty rows)
-constexpr int SLOT_UNITS = 65;  // 1 KiB copy units per slot
+constexpr int SL_M = 53248;     // M  : token tile t x token block b <= t/2 (6 fragments, 5 KiB)
+constexpr int SL_N = 58368;     // N  : same tiling as M
+constexpr int SL_GAM = 63488;   // exp(G_end), 128 fp32
+constexpr int SL_BETA = 64000;  // beta per tile row, 64 fp32 (0 on empty rows)
+constexpr int SLOT_UNITS = 63;  // 1 KiB copy units per slot
 static_assert(SLOT_UNITS * 1024 == kDecompSlotBytes, "slot size");
 static_assert(SL_BETA + 256 <= kDecompSlotBytes, "slot layout");
 
@@ -120,6 +120,13 @@ __device__ __forceinline__ void acc_pair_split(const f32x4& a, const f32x4& b, b
 }
 // M / N fragment index of (token tile t, token block b <= t / 2)
 __host__ __device__ constexpr int tri_frag(int t, int b) { return t < 2 ? t : 2 * t - 2 + b; }
+// Fragments (0, 0) and (2, 1) lie on the diagonal with an all-zero upper half
+// (token block 2b + 1 > t): only their lower 8 bytes per lane are stored.
+__host__ __device__ constexpr bool tri_half(int f) { return f == 0 || f == 3; }
+// byte offset of fragment f inside the M or N region (half fragments take 512 bytes)
+__host__ __device__ constexpr int tri_off(int f) {
+  return f == 0 ? 0 : f == 1 ? 512 : f == 2 ? 1536 : f == 3 ? 2560 : f == 4 ? 3072 : 4096;
+}
 
 // ---------------------------------------------------------------------------
 // Sequence and segment geometry (shared by both launches).
@@ -520,8 +527,12 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     if (2 * tb > i) continue;
-    *reinterpret_cast<bf16x8*>(slot + SL_M + (tri_frag(i, tb) * 64 + lane) * 16) =
-        acc_pair(macc[2 * tb], macc[2 * tb + 1]);
+    const int f = tri_frag(i, tb);
+    const uint4 mv = __builtin_bit_cast(uint4, acc_pair(macc[2 * tb], macc[2 * tb + 1]));
+    if (tri_half(f))
+      *reinterpret_cast<uint2*>(slot + SL_M + tri_off(f) + lane * 8) = make_uint2(mv.x, mv.y);
+    else
+      *reinterpret_cast<uint4*>(slot + SL_M + tri_off(f) + lane * 16) = mv;
   }
   __syncthreads();
 
@@ -605,22 +616,32 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
                         s0 + 2 < r ? v0.z : 0.f, s0 + 3 < r ? v0.w : 0.f,
                         s0 + 16 < r ? v1.x : 0.f, s0 + 17 < r ? v1.y : 0.f,
                         s0 + 18 < r ? v1.z : 0.f, s0 + 19 < r ? v1.w : 0.f};
-    *reinterpret_cast<bf16x8*>(slot + SL_N + (tri_frag(w, tb) * 64 + lane) * 16) = to_bf16x8(x);
+    const int f = tri_frag(w, tb);
+    const uint4 nv = __builtin_bit_cast(uint4, to_bf16x8(x));
+    if (tri_half(f))
+      *reinterpret_cast<uint2*>(slot + SL_N + tri_off(f) + lane * 8) = make_uint2(nv.x, nv.y);
+    else
+      *reinterpret_cast<uint4*>(slot + SL_N + tri_off(f) + lane * 16) = nv;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Launch 2: recurrence.  One workgroup per (sequence, head, column group) with
-// WAVES compute waves and WAVES copy waves.  Compute wave w owns 16 columns
+// CW compute waves and KW copy waves.  Compute wave w owns 16 columns
 // of the state (all 128 rows: 8 accumulator tiles in registers).  The copy
 // waves bring the next segment's slot and V block into the idle one of two
 // LDS buffers with global_load_lds while the compute waves consume the other;
 // a copy wave may stall on a full memory queue, a compute wave never issues a
 // load.  One barrier per segment hands the buffers over.
 
-template <int WAVES>
-__global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompArgs a) {
-  constexpr int VW = 16 * WAVES;                  // columns per workgroup
+template <int CW, int KW>
+__global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(DecompArgs a) {
+  constexpr int WAVES = CW;
+  // with at most one wave per SIMD a compute wave has 512 registers and reads
+  // its fragments in large batches; with more waves it reads them as it goes
+  // and the other compute wave on the SIMD covers the latency
+  constexpr bool BATCHED = CW + KW <= 8;
+  constexpr int VW = 16 * CW;                     // columns per workgroup
   constexpr int VUNITS = CH * VW * 2 / 1024;      // 1 KiB units of the V block
   constexpr int UNITS = SLOT_UNITS + VUNITS;
   // two buffers as separate arrays, so the compiler sees that reads of one do
@@ -648,19 +669,19 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
     tok0 = si.bos + lo - off;
   };
 
-  if (w >= WAVES) {
-    // ---- copy waves: unit u of the slot (or of the V block) goes to copy wave u % WAVES
-    const int cw = w - WAVES;
+  if (w >= CW) {
+    // ---- copy waves: unit u of the slot (or of the V block) goes to copy wave u % KW
+    const int cw = w - CW;
     auto copy = [&](int jseg, uint4* dst) {
       const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
-      for (int u = cw; u < SLOT_UNITS; u += WAVES)
+      for (int u = cw; u < SLOT_UNITS; u += KW)
         __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
       // V rows 0..63 (rows before the segment read row `off`, zeroed on use)
       int off;
       int64_t tok0;
       geometry(jseg, off, tok0);
       constexpr int LPR = VW / 8, RPI = 64 / LPR;  // lanes per row, rows per unit
-      for (int k = cw; k < VUNITS; k += WAVES) {
+      for (int k = cw; k < VUNITS; k += KW) {
         const int row = max(k * RPI + lane / LPR, off);
         const uint16_t* vsrc = a.v + ((size_t)(tok0 + row) * H + h) * DK + VW * part + 8 * (lane % LPR);
         __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS + k) * 64, 16, 0, 0);
@@ -735,13 +756,25 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
     auto f4 = [&](int byte_off) {
       return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off);
     };
+    // M or N fragment f (half fragments: upper 8 bytes are zero)
+    auto trifrag = [&](int region, int f) {
+      const char* base = reinterpret_cast<const char*>(cur) + region + tri_off(f);
+      if (tri_half(f)) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(base + lq * 8);
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, 0u, 0u));
+      }
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(base + lq * 16));
+    };
     const uint16_t* vblk = reinterpret_cast<const uint16_t*>(cur + SLOT_UNITS * 64);
 
     // The segment runs as load batches and matrix batches separated by
     // scheduling fences: fragment reads go out together and are consumed while
     // the next batch is in flight (without the fences the reads are issued one
     // at a time, each waited for before its product).
-#define KDA_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define KDA_FENCE()                                 \
+  do {                                              \
+    if (BATCHED) __builtin_amdgcn_sched_barrier(0); \
+  } while (0)
     bf16x8 fk[16], fq[16];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -788,7 +821,7 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
       for (int e = 0; e < 4; ++e) vv[4 * t + e] = vblk[(16 * t + 4 * gg + e) * VW + 16 * w + qq];
     bf16x8 fn[6];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) fn[i] = frag(SL_N + i * 1024);
+    for (int i = 0; i < 6; ++i) fn[i] = trifrag(SL_N, i);
     KDA_FENCE();
 #pragma unroll
     for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[0], fq[t * 4], (f32x4){0.f, 0.f, 0.f, 0.f});
@@ -820,7 +853,7 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
     // M and the first half of K^, read while N Y runs
     bf16x8 fm[6], fh[16];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) fm[i] = frag(SL_M + i * 1024);
+    for (int i = 0; i < 6; ++i) fm[i] = trifrag(SL_M, i);
 #pragma unroll
     for (int i = 0; i < 8; ++i) fh[i] = frag(SL_KH + i * 1024);
     KDA_FENCE();
@@ -885,12 +918,12 @@ __global__ __launch_bounds__(128 * WAVES, 1) void kda_recurrence_kernel(DecompAr
   if (a.final_state) store_state(a.final_state);
 }
 
-template <int WAVES>
+template <int CW, int KW>
 hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
-  constexpr int PARTS = 8 / WAVES;
+  constexpr int PARTS = 8 / CW;
   const int64_t pairs = (int64_t)a.N * a.H;
   const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * PARTS));
-  hipLaunchKernelGGL(kda_recurrence_kernel<WAVES>, grid, dim3(128 * WAVES), 0, stream, a);
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), grid, dim3(64 * (CW + KW)), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -912,9 +945,10 @@ hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots,
   }
   if (!(stages & 2)) return hipSuccess;
   switch (vsplit) {
-    case 2: return launch_recurrence<4>(a, stream);
-    case 4: return launch_recurrence<2>(a, stream);
-    case 8: return launch_recurrence<1>(a, stream);
+    case 1: return launch_recurrence<8, 4>(a, stream);
+    case 2: return launch_recurrence<4, 4>(a, stream);
+    case 4: return launch_recurrence<2, 2>(a, stream);
+    case 8: return launch_recurrence<1, 1>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

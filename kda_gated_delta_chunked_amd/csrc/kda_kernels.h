@@ -33,7 +33,7 @@ hipError_t launch_fused(const FusedArgs& a, int vsplit, hipStream_t stream);
 // Two-launch schedule.  The workspace holds a header of (N + 1) int32 slot
 // offsets (packed layout) followed by one slot of kDecompSlotBytes per
 // (segment, head).
-constexpr int kDecompSlotBytes = 66560;
+constexpr int kDecompSlotBytes = 64512;
 
 struct DecompArgs {
   const uint16_t* q;

@@ -147,8 +147,8 @@ def test_prefill_rejects_on_the_host_without_a_device():
 
 def decomp_bytes(N, T, H):
     """The documented workspace formula: (N + 1) int32 rounded up to 256 bytes,
-    then 66,560 bytes per (segment slot, head) for floor(T / 64) + 2 N slots."""
-    return ((N + 1) * 4 + 255) // 256 * 256 + (T // 64 + 2 * N) * H * 66560
+    then 64,512 bytes per (segment slot, head) for floor(T / 64) + 2 N slots."""
+    return ((N + 1) * 4 + 255) // 256 * 256 + (T // 64 + 2 * N) * H * 64512
 
 
 def test_workspace_size_and_plan_arguments():
@@ -178,8 +178,8 @@ def test_workspace_rules():
     assert val(prob_for(b), ws, need) == OK
     assert val(prob_for(b, value_split=8), 0, 0) == WS  # split 8 exists only in DECOMP
     assert val(prob_for(b, variant="fused", value_split=8), 0, 0) == UNSUPPORTED
-    assert val(prob_for(b, variant="decomp", value_split=1), ws, need) == UNSUPPORTED
-    for vs in (2, 4, 8):
+    assert val(prob_for(b, variant="fused", value_split=1), ws, need) == UNSUPPORTED
+    for vs in (1, 2, 4, 8):
         assert val(prob_for(b, variant="decomp", value_split=vs), ws, need) == OK
     assert val(dec, ws + 8, need) == ALIGN
     # the workspace overlaps nothing the call reads or writes

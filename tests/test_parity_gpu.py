@@ -35,7 +35,7 @@ def _gpu():
     K.load_library()
 
 
-SPLITS = [("fused", 2), ("fused", 4), ("decomp", 2), ("decomp", 4), ("decomp", 8)]
+SPLITS = [("fused", 2), ("fused", 4), ("decomp", 1), ("decomp", 2), ("decomp", 4), ("decomp", 8)]
 VARIANTS = ["fused", "decomp"]
 
 
