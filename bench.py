@@ -121,10 +121,21 @@ def cpu_baseline(p, sample_tokens: int):
     oracle.prefill(p.q[idx], p.k[idx], p.v[idx], p.g[idx], p.beta[idx], scale=p.scale,
                    num_seqs=p.N, cu_seqlens=cu, initial_state=p.initial_state, threads=threads)
     dt = time.perf_counter() - t0
+    # one core: the first sequence of the sample, one head
+    L0 = lens[0]
+    sl = slice(0, L0)
+    t1 = time.perf_counter()
+    oracle.prefill(p.q[idx][sl, :1], p.k[idx][sl, :1], p.v[idx][sl, :1], p.g[idx][sl, :1],
+                   p.beta[idx][sl, :1], scale=p.scale, num_seqs=1,
+                   cu_seqlens=np.array([0, L0], np.int32),
+                   initial_state=None if p.initial_state is None else p.initial_state[:1, :1],
+                   threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": float(cu[-1]) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of each of the {p.N} sequences, all {p.H} "
                       f"heads ({int(cu[-1]) * p.H} token-heads), fp64 token recurrence, "
-                      f"{dt:.2f} s wall"}
+                      f"{dt:.2f} s wall",
+            "one_core_token_heads_per_s": round(L0 / dt1, 1)}
 
 
 def main() -> int:
@@ -136,6 +147,8 @@ def main() -> int:
     ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--variant", default="auto", choices=["auto", "decomp", "fused"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--timing-calls", type=int, default=50,
+                    help="calls per block for the median, cold-cache and graph-replay timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, --steps times "
@@ -206,12 +219,50 @@ def main() -> int:
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])), wall
 
+    def per_call(fn, calls, before=None):
+        """Event-timed milliseconds of each of `calls` calls of fn (optionally
+        preceded, outside the events, by `before`)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        for a, b in ev:
+            if before is not None:
+                before()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ms_launch, ms_step = timed(step, args.steps)
     tokens = p.T_total
     value = tokens / (ms_step * 1e-3)
+
+    # medians of two independent blocks of calls (warm), the same with 1 GiB
+    # written between calls (the 256 MiB Infinity Cache then holds none of the
+    # inputs), and a captured HIP graph of one call replayed
+    timing = {"warm_median_ms": [round(float(np.median(per_call(step, args.timing_calls))), 4)
+                                 for _ in range(2)]}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    timing["cold_median_ms"] = round(float(np.median(
+        per_call(step, max(10, args.timing_calls // 5), before=lambda: flush.fill_(1.0)))), 4)
+    del flush
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            rc = K.prefill_raw(prob, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), ptr(s0),
+                               ptr(out), ptr(fin), ptr(offs), ptr(ck), ptr(ws), ws_bytes,
+                               torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    if rc != 0:
+        raise K.KDAError(rc, "kda_prefill (capture)")
+    graph.replay()
+    torch.cuda.synchronize()
+    timing["graph_replay_median_ms"] = round(float(np.median(per_call(graph.replay, args.timing_calls))), 4)
+    del graph
 
     # per-kernel times: the two launches of DECOMP enqueued by separate calls
     kernels = {}
@@ -266,7 +317,7 @@ def main() -> int:
                       "initial_state": p.initial_state is not None,
                       "checkpoints": p.ckpt_offsets is not None,
                       "variant": variant, "value_split": vsplit},
-           "roofline": roof, "path": path, "mfma": mfma}
+           "roofline": roof, "path": path, "mfma": mfma, "timing": timing}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)
