@@ -95,7 +95,7 @@ typedef struct {
   int32_t variant;           /* kda_variant */
   int32_t value_split;       /* 0 = automatic, else workgroups per (sequence, head), each
                                 owning 128/value_split columns of the state: 2 or 4 for
-                                FUSED, 2, 4 or 8 for DECOMP (FlashInfer PR #4262,
+                                FUSED, 1, 2, 4 or 8 for DECOMP (FlashInfer PR #4262,
                                 Physical schedules: value rows split over CTAs) */
   int32_t stages;            /* DECOMP only (0 otherwise): which of its two launches to
                                 enqueue.  0 = both.  KDA_STAGE_PREPARE = only the chunk-
@@ -109,7 +109,7 @@ enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
 
 /* Bytes of caller workspace kda_prefill needs for this problem (host only, no
  * device access).  FUSED needs none (0).  DECOMP, and AUTO so that it may
- * pick DECOMP, need a header of (N + 1) int32 rounded up to 256 bytes plus
+ * pick DECOMP, need a header of 2 N + 1 int32 rounded up to 256 bytes plus
  * 64,512 bytes per (segment slot, head), with floor(T_total / 64) + 2 N
  * segment slots: about 1.01 KiB per token-head.  The workspace is scratch:
  * it carries nothing between calls, may be reused by any later call on the

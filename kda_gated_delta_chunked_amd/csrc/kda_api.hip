@@ -224,6 +224,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.ckpt_off = ckpt_offsets;
     a.ckpt = ckpt_state;
     a.seg_base = static_cast<int32_t*>(workspace);
+    a.order = cu_seqlens ? a.seg_base + p->num_seqs + 1 : nullptr;
     a.slots = static_cast<unsigned char*>(workspace) + header;
     a.N = p->num_seqs;
     a.H = p->num_heads;

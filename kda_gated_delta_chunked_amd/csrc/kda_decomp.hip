@@ -180,9 +180,18 @@ __device__ __forceinline__ void seg_range(const SeqInfo& s, int j, int& lo, int&
 // Launch 0 (packed layout only): first slot of every sequence.  Sequence n
 // owns ceil(L_n / 64) slots, plus one when checkpoints are requested (the
 // chunk cut at the offset).  base[N] is the total.
+//
+// It also writes the order in which the recurrence takes the sequences:
+// longest first (ties by index), so that when there are more workgroups than
+// the device holds at once, the long chains start first and short ones fill
+// the tail.  Up to kOrderMax sequences are ranked; beyond that the order is
+// the identity.
+
+constexpr int kOrderMax = 1024;
 
 __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
   __shared__ int32_t wsum[16];
+  __shared__ int32_t nslots[kOrderMax];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int extra = a.ckpt_off ? 1 : 0;
   int64_t carry = 0;
@@ -210,10 +219,22 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
       tot += wsum[i];
     }
     if (n < a.N) a.seg_base[n] = (int32_t)(carry + woff + x - cnt);
+    if (a.N <= kOrderMax) nslots[t] = cnt;
+    else if (a.order && n < a.N) a.order[n] = n;
     __syncthreads();
     carry += tot;
   }
   if (t == 0) a.seg_base[a.N] = (int32_t)carry;
+  if (a.order && a.N <= kOrderMax && t < a.N) {
+    // rank = sequences that come before this one
+    const int mine = nslots[t];
+    int rank = 0;
+    for (int m = 0; m < a.N; ++m) {
+      const int o = nslots[m];
+      rank += (o > mine || (o == mine && m < t)) ? 1 : 0;
+    }
+    a.order[rank] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -655,7 +676,8 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   const int bx = blockIdx.x, xcd = bx & 7, rest = bx >> 3;
   const int pair = (rest / PARTS) * 8 + xcd, part = rest % PARTS;
   if (pair >= a.N * H) return;
-  const int n = pair / H, h = pair - n * H;
+  const int rank = pair / H, h = pair - rank * H;
+  const int n = a.order ? a.order[rank] : rank;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
 
   const SeqInfo si = seq_info(a, n);

@@ -31,8 +31,8 @@ struct FusedArgs {
 hipError_t launch_fused(const FusedArgs& a, int vsplit, hipStream_t stream);
 
 // Two-launch schedule.  The workspace holds a header of (N + 1) int32 slot
-// offsets (packed layout) followed by one slot of kDecompSlotBytes per
-// (segment, head).
+// offsets and N int32 sequence indices in recurrence order (packed layout),
+// followed by one slot of kDecompSlotBytes per (segment, head).
 constexpr int kDecompSlotBytes = 64512;
 
 struct DecompArgs {
@@ -49,6 +49,7 @@ struct DecompArgs {
   float* ckpt;
   unsigned char* slots;       // workspace slot area
   int32_t* seg_base;          // workspace header: first slot of each sequence (packed layout)
+  int32_t* order;             // workspace header: sequences by decreasing length (packed layout), or NULL
   int N;
   int H;
   int64_t T_total;
@@ -61,7 +62,7 @@ struct DecompArgs {
 // Workspace layout for (N, T_total, H): header bytes and slot capacity.
 inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, size_t* header,
                                     int64_t* slots, size_t* bytes) {
-  *header = (size_t)(((N + 1) * 4 + 255) / 256 * 256);
+  *header = (size_t)(((2 * N + 1) * 4 + 255) / 256 * 256);
   // ceil(L/64) summed over sequences is at most floor(T/64) + N; one more per
   // sequence for the chunk cut at a checkpoint offset
   *slots = T_total / 64 + 2 * N;

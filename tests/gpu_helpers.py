@@ -30,13 +30,15 @@ def to_device(p: synth.Problem):
 
 
 def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=None,
-            sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False):
+            sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False,
+            keep_workspace: bool = False):
     """Run kda_prefill through the C ABI on a fresh set of device buffers.
 
     Outputs are pre-filled with NaN so that any element the kernel fails to
     write shows up; the workspace (sized by kda_prefill_workspace_size) is
     filled with 0xFF bytes (NaN as fp32) so nothing depends on its contents.
-    Returns numpy dict(out fp32, final, ckpt)."""
+    Returns numpy dict(out fp32, final, ckpt), and the workspace bytes under
+    "workspace" when keep_workspace is set."""
     import torch
     import kda_gated_delta_chunked_amd as K
     d = d or to_device(p)
@@ -69,6 +71,8 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
     torch.cuda.synchronize()
     res = {"out": out.float().cpu().numpy(), "final": fin.cpu().numpy(),
            "ckpt": None if ck is None else ck.cpu().numpy()}
+    if keep_workspace:
+        res["workspace"] = None if ws is None else ws.cpu().numpy()
     return res
 
 

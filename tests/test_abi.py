@@ -148,7 +148,7 @@ def test_prefill_rejects_on_the_host_without_a_device():
 def decomp_bytes(N, T, H):
     """The documented workspace formula: (N + 1) int32 rounded up to 256 bytes,
     then 64,512 bytes per (segment slot, head) for floor(T / 64) + 2 N slots."""
-    return ((N + 1) * 4 + 255) // 256 * 256 + (T // 64 + 2 * N) * H * 64512
+    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + 2 * N) * H * 64512
 
 
 def test_workspace_size_and_plan_arguments():

@@ -179,6 +179,31 @@ def test_decomp_matches_fused_on_packed_layout_as_separate_runs():
         t0 += L
 
 
+def test_packed_recurrence_order_longest_first():
+    # the plan launch ranks the packed sequences by slot count, longest first
+    # and ties by index; the header holds N + 1 slot offsets, then that order
+    lens = [100, 3000, 64, 3000, 1, 0, 700, 129]
+    p = synth.make_problem(lens, 2, seed=17, init_state=True)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant="decomp", keep_workspace=True)
+    assert_parity(gpu, ref, "ordered")
+    hdr = gpu["workspace"][: 4 * (2 * p.N + 1)].view(np.int32)
+    slots = [(L + 63) // 64 for L in lens]
+    assert list(hdr[: p.N + 1]) == [0] + list(np.cumsum(slots))
+    assert list(hdr[p.N + 1:]) == sorted(range(p.N), key=lambda n: (-slots[n], n))
+
+
+def test_packed_many_sequences_identity_order():
+    # past 1024 sequences the plan keeps the identity order
+    lens = list(np.random.default_rng(18).integers(0, 41, size=1100))
+    p = synth.make_problem(lens, 1, seed=18, init_state=True)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant="decomp", keep_workspace=True)
+    _report("packed 1100 short", assert_parity(gpu, ref, "1100 sequences"))
+    hdr = gpu["workspace"][: 4 * (2 * p.N + 1)].view(np.int32)
+    assert list(hdr[p.N + 1:]) == list(range(p.N))
+
+
 def test_split_stages_equal_one_call():
     # the prepare launch and the recurrence launch enqueued by two calls give
     # the same bits as one call
