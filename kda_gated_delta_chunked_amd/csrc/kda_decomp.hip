@@ -17,6 +17,7 @@
 // are state independent (prepare).  The recurrence then does, per segment,
 //   X = V - K~ S,  Y = diag(beta) X,  U = Y + N Y
 //   O = scale (Q~ S + M U),   S <- diag(Gam) S + K^^T U
+// (the prepare folds the scale into Q~ and M)
 // which regroups the token recurrence (decay, delta-rule correction, read-out
 // of the updated state) by segments.
 //
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kf[e] = rv ? kf[e] : 0.f;
-      qf[e] = rv ? qf[e] : 0.f;
+      qf[e] = rv ? qf[e] * a.scale : 0.f;  // Q~ and M carry the read-out scale
     }
     load8_f32(sF, bt, (F_BT + i) * DK + ch0);
     float Kf[8], Qf[8], kb[8];
@@ -737,10 +738,11 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   auto store_state = [&](float* dst) {
-    // the row pointer is made opaque so the 32 store addresses are formed
-    // here, not kept live in registers across the segment loop
-    float* rowp = dst + sbase + (size_t)(4 * g4) * DK;
-    asm volatile("" : "+v"(rowp));
+    // the lane's offsets are formed here from an opaque lane index, so the 32
+    // store addresses are not kept live in registers across the segment loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    float* rowp = dst + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 4 * DK;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -748,7 +750,6 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   };
   if (a.ckpt_off && si.p == 0) store_state(a.ckpt);
 
-  const float scale = a.scale;
   uint32_t opk[8];
   int poff = CH;
   int64_t ptok = 0;
@@ -756,13 +757,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   // O^T tile t of the previous segment: lane holds token 16 t + q, columns
   // col0 + 4 g4 .. + 3 (one 8-byte store per tile)
   auto store_out = [&]() {
+    uint16_t* ob = a.out + ((size_t)ptok * H + h) * DK + col0;
+    // lane offset formed here (opaque), not kept live across the segment loop
+    int ro = q * H * DK + 4 * g4;
+    asm volatile("" : "+v"(ro));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = 16 * t + q;
-      if (row >= poff)
-        *reinterpret_cast<uint2*>(a.out + ((size_t)(ptok + row) * H + h) * DK + col0 + 4 * g4) =
-            make_uint2(opk[2 * t], opk[2 * t + 1]);
-    }
+    for (int t = 0; t < 4; ++t)
+      if (16 * t + q >= poff)
+        *reinterpret_cast<uint2*>(ob + ro + t * 16 * H * DK) = make_uint2(opk[2 * t], opk[2 * t + 1]);
   };
 
   auto step = [&](int jseg, const uint4* cur) {
@@ -828,7 +830,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
       for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4 + b], Sb[b], X[t]);
     KDA_FENCE();
-    // the rest of Q~, the V block and N, read while O^T = S^T Q~^T starts
+    // the rest of Q~, the V block and N, read while O^T = S^T Q~^T runs
     int off;
     int64_t tok0;
     geometry(jseg, off, tok0);
@@ -844,7 +846,6 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     bf16x8 fn[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) fn[i] = trifrag(SL_N, i);
-    KDA_FENCE();
 #pragma unroll
     for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[0], fq[t * 4], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -852,18 +853,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
       for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[b], fq[t * 4 + b], O[t]);
     KDA_FENCE();
-    // Y = beta (V - X), kept in U; U = Y + N Y.  Rows before the segment are
-    // masked to zero (the read above is unconditional).
+    // Y = beta (V - X), kept in U; U = Y + N Y.  Rows before the segment have
+    // beta = 0 (their V read is a copy of row `off`), so they give U = 0.
     f32x4 U[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float bv[4] = {bt4[t].x, bt4[t].y, bt4[t].z, bt4[t].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t keep = 16 * t + 4 * g4 + e >= off ? 0xffffffffu : 0u;
-        const float vx = __uint_as_float(((uint32_t)vv[4 * t + e] << 16) & keep);
-        U[t][e] = bv[e] * (vx - X[t][e]);
-      }
+      for (int e = 0; e < 4; ++e) U[t][e] = bv[e] * (__uint_as_float((uint32_t)vv[4 * t + e] << 16) - X[t][e]);
     }
     const bf16x8 Y0 = acc_pair(U[0], U[1]), Y1 = acc_pair(U[2], U[3]);
     U[0] = mfma(fn[tri_frag(0, 0)], Y0, U[0]);
@@ -902,6 +899,12 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
     for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
     KDA_FENCE();
+    // Q~ and M carry the read-out scale
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      opk[2 * t] = pack2(O[t][0], O[t][1]);
+      opk[2 * t + 1] = pack2(O[t][2], O[t][3]);
+    }
     // S <- diag(Gam) S + K^^T U
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -917,11 +920,6 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       S[m] = mfma(klf, Uh[1], S[m]);
     }
 #undef KDA_FENCE
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      opk[2 * t] = pack2(scale * O[t][0], scale * O[t][1]);
-      opk[2 * t + 1] = pack2(scale * O[t][2], scale * O[t][3]);
-    }
     poff = off;
     ptok = tok0;
     pend = true;
