@@ -138,6 +138,68 @@ def cpu_baseline(p, sample_tokens: int):
             "one_core_token_heads_per_s": round(L0 / dt1, 1)}
 
 
+def bench_decode(args, torch, K, synth) -> int:
+    """State-pool decode: N requests x T tokens, H = 12, one pool entry per
+    request (a permutation), inputs resident.  HBM-bound: each (request, head)
+    reads and writes its 64 KiB fp32 state once per call, plus 1,540 B per
+    token-head of q, k, v, g, beta and out."""
+    N, T = (int(x) for x in args.decode.split(","))
+    H = 12
+    dev = torch.device("cuda", 0)
+    p = synth.make_problem([T] * N, H, seed=2000 + N + T, fixed=True)
+    shp = (N, T, H, 128)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16).view(shp)
+
+    q, k, v = bf16(p.q), bf16(p.k), bf16(p.v)
+    g = torch.from_numpy(p.g).to(dev).view(shp)
+    beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
+    rng = np.random.default_rng(2001)
+    pool = torch.from_numpy(rng.normal(0, 0.02, (N, H, 128, 128)).astype(np.float32)).to(dev)
+    idx = torch.from_numpy(rng.permutation(N).astype(np.int32)).to(dev)
+    out = torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+    prob = K.make_decode_problem(N, T, H, N, scale=p.scale)
+
+    def step():
+        st = K.decode_raw(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                          beta.data_ptr(), pool.data_ptr(), idx.data_ptr(), out.data_ptr(),
+                          stream.cuda_stream)
+        if st != 0:
+            raise K.KDAError(st, "kda_decode")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_kernel = float(np.median(ms))
+    alg = N * H * (2 * 128 * 128 * 4) + N * T * H * (128 * 2 * 4 + 128 * 4 + 4)
+    achieved = alg / (ms_kernel * 1e-3) / 1e9
+    res = {"metric": "state-pool decode tokens/s (H=12, K=V=128, fp32 state)",
+           "value": round(N * T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+           "data": "synthetic",
+           "config": {"workload": f"decode_n{N}_t{T}", "requests": N, "tokens_per_request": T,
+                      "H": H, "pool_size": N},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "kda_decode_kernel", "kernel_ms": round(ms_kernel, 4),
+                        "algorithmic_bytes": alg}}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +212,9 @@ def main() -> int:
     ap.add_argument("--timing-calls", type=int, default=50,
                     help="calls per block for the median, cold-cache and graph-replay timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", default="", metavar="N,T",
+                    help="instead of the prefill, time the state-pool decode of N requests "
+                         "advancing T tokens each (H = 12, pool of N states)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, --steps times "
                          "(reference for the HBM byte counters)")
@@ -172,6 +237,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "steps": args.steps}), flush=True)
         return 0
+
+    if args.decode:
+        return bench_decode(args, torch, K, synth)
 
     p = synth.workload(args.workload)
     dev = torch.device("cuda", 0)

@@ -138,6 +138,55 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
                        float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * State-pool decode.  A serving step advances each of N requests by T tokens
+ * (T = 1: decode; T > 1: e.g. verifying T draft tokens) from the fp32 state
+ * its index names in a pool, and writes the state back in place.  The
+ * per-request pool index follows the state pool / ssm_state_indices of the
+ * sglang KDA decode backend (FlashInferKDAKernel page); FlashInfer PR #4262
+ * (Description) names decode (T = 1) and state-pool features as the
+ * counterpart of the prefill.  For request n with i = state_indices[n] in
+ * [0, pool_size) and every head h, starting from S = pool[i, h], each token t
+ * of the request applies the recurrence stated at the top of this file and
+ * the final S is stored to pool[i, h].  An index outside [0, pool_size)
+ * (such as -1 for an empty batch slot) leaves the pool untouched and gives
+ * zero outputs.
+ *
+ * Layouts (device memory):
+ *   q, k, v     bf16 [N * T, H, 128]   (request-major: token t of request n is row n * T + t)
+ *   g           fp32 [N * T, H, 128],  lower_bound <= g <= 0
+ *   beta        fp32 [N * T, H]
+ *   state_pool  fp32 [pool_size, H, 128, 128] (K x V), read and written in place
+ *   state_indices int32 [N]; non-negative entries must be distinct (two
+ *               requests on one state race; not checked on the device)
+ *   out         bf16 [N * T, H, 128]; may be exactly v
+ * The update runs token by token in fp32 (no chunking).  Errors are detected
+ * on the host before anything is enqueued; nothing is allocated. */
+typedef struct {
+  int32_t num_seqs;          /* N >= 0 requests */
+  int32_t tokens_per_seq;    /* T >= 1 tokens per request */
+  int32_t num_heads;         /* H >= 1 */
+  int32_t head_dim_k;        /* must be 128 */
+  int32_t head_dim_v;        /* must be 128 */
+  float scale;               /* read-out scale, finite */
+  float gate_lower_bound;    /* caller's promise g >= bound; must lie in [-5, 0] */
+  int64_t pool_size;         /* states in the pool, >= 1 */
+} kda_decode_problem;
+
+/* Host-side checks of kda_decode without launching: sizes, NULL rules,
+ * 16-byte alignment, overlap (only out == v may alias, exactly), and the
+ * INT32 bound on N * T * H * 128.  Pointers are never dereferenced. */
+kda_status kda_decode_validate(const kda_decode_problem* p, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta,
+                               const float* state_pool, const int32_t* state_indices,
+                               const void* out);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = the null
+ * stream).  Same status convention as kda_prefill. */
+kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const float* g, const float* beta, float* state_pool,
+                      const int32_t* state_indices, uint16_t* out, void* stream);
+
 /* Static string for a status code. */
 const char* kda_status_string(kda_status s);
 

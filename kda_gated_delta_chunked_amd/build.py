@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_fused.hip", "kda_decomp.hip"]
+SOURCES = ["kda_api.hip", "kda_fused.hip", "kda_decomp.hip", "kda_decode.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

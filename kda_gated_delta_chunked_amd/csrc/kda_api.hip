@@ -259,4 +259,60 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_decode_validate(const kda_decode_problem* p, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta,
+                               const float* state_pool, const int32_t* state_indices,
+                               const void* out) {
+  if (!p) return KDA_ERR_INVALID_ARG;
+  if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
+  if (p->num_seqs < 0 || p->tokens_per_seq < 1 || p->num_heads < 1 || p->pool_size < 1)
+    return KDA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale)) return KDA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->gate_lower_bound) || p->gate_lower_bound < -5.0f ||
+      p->gate_lower_bound > 0.0f)
+    return KDA_ERR_INVALID_ARG;
+  const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
+  if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
+  if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out))
+    return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, state_pool, state_indices, out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
+  const uint64_t tok_bf16 = (uint64_t)N * T * H * kHeadDim * 2;
+  const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
+  const Range rg = range_of(g, tok_bf16 * 2), rb = range_of(beta, (uint64_t)N * T * H * 4);
+  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
+  const Range ridx = range_of(state_indices, (uint64_t)N * 4);
+  const Range rout = range_of(out, tok_bf16);
+  for (const Range& r : {rq, rk, rg, rb, rpool, ridx})
+    if (overlaps(rout, r)) return KDA_ERR_OVERLAP;
+  if (overlaps(rout, rv) && !exact(rout, rv)) return KDA_ERR_OVERLAP;
+  for (const Range& r : {rq, rk, rv, rg, rb, ridx})
+    if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
+  return KDA_OK;
+}
+
+kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const float* g, const float* beta, float* state_pool,
+                      const int32_t* state_indices, uint16_t* out, void* stream) {
+  const kda_status st = kda_decode_validate(p, q, k, v, g, beta, state_pool, state_indices, out);
+  if (st != KDA_OK) return st;
+  if (p->num_seqs == 0) return KDA_OK;
+  kda::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.pool = state_pool;
+  a.state_indices = state_indices;
+  a.out = out;
+  a.N = p->num_seqs;
+  a.T = p->tokens_per_seq;
+  a.H = p->num_heads;
+  a.pool_size = p->pool_size;
+  a.scale = p->scale;
+  return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

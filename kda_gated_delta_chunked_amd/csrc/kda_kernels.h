@@ -76,4 +76,24 @@ inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, size_
 hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
                          hipStream_t stream);
 
+// State-pool decode: N requests advance by T tokens each from the pool
+// states their indices name (kda_decode.hip).
+struct DecodeArgs {
+  const uint16_t* q;          // [N * T, H, 128] bf16
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;             // [N * T, H, 128]
+  const float* beta;          // [N * T, H]
+  float* pool;                // [pool_size, H, 128, 128], updated in place
+  const int32_t* state_indices;  // [N]; outside [0, pool_size): no state
+  uint16_t* out;              // [N * T, H, 128] bf16
+  int N;
+  int T;
+  int H;
+  int64_t pool_size;
+  float scale;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace kda

@@ -47,6 +47,22 @@ class Problem(ctypes.Structure):
 STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
 
 
+class DecodeProblem(ctypes.Structure):
+    """Mirror of ``kda_decode_problem``."""
+
+    _fields_ = [("num_seqs", ctypes.c_int32), ("tokens_per_seq", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("gate_lower_bound", ctypes.c_float), ("pool_size", ctypes.c_int64)]
+
+
+def make_decode_problem(num_seqs: int, tokens_per_seq: int, num_heads: int, pool_size: int, *,
+                        scale: float, gate_lower_bound: float = -5.0,
+                        head_dim_k: int = HEAD_DIM, head_dim_v: int = HEAD_DIM) -> DecodeProblem:
+    return DecodeProblem(int(num_seqs), int(tokens_per_seq), int(num_heads), int(head_dim_k),
+                         int(head_dim_v), float(scale), float(gate_lower_bound), int(pool_size))
+
+
 def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: float,
                  gate_lower_bound: float = -5.0, variant: str | int = "auto",
                  value_split: int = 0, head_dim_k: int = HEAD_DIM,
@@ -82,6 +98,11 @@ def load_library(path: Optional[str] = None):
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_plan.argtypes = [PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.kda_plan.restype = ctypes.c_int
+    DP = ctypes.POINTER(DecodeProblem)
+    lib.kda_decode_validate.argtypes = [DP, P, P, P, P, P, P, P, P]
+    lib.kda_decode_validate.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P]
+    lib.kda_decode.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -218,3 +239,71 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
                          _ptr(ckpt_state), _ptr(workspace), ws_bytes, int(stream.cuda_stream))
     _check(st, "kda_prefill")
     return out, final_state
+
+
+def decode_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indices, out,
+               stream) -> int:
+    """Call ``kda_decode`` with raw integer pointers (0 for NULL); returns the status."""
+    lib = load_library()
+    return lib.kda_decode(ctypes.byref(problem), q or None, k or None, v or None, g or None,
+                          beta or None, state_pool or None, state_indices or None, out or None,
+                          stream or None)
+
+
+def decode_validate_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indices,
+                        out) -> int:
+    """Call ``kda_decode_validate`` with raw integer pointers; returns the status (host only)."""
+    lib = load_library()
+    return lib.kda_decode_validate(ctypes.byref(problem), q or None, k or None, v or None,
+                                   g or None, beta or None, state_pool or None,
+                                   state_indices or None, out or None)
+
+
+def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float] = None,
+           out=None, gate_lower_bound: float = -5.0, stream=None):
+    """One state-pool decode step on the GPU.
+
+    q, k, v: bf16 [N, T, H, 128] (T tokens per request; T = 1 for decode).
+    g: fp32 like q; beta: fp32 [N, T, H].  state_pool: fp32 [P, H, 128, 128],
+    updated in place.  state_indices: int32 [N]; entries outside [0, P) mark
+    empty request slots (zero outputs, no state touched).  Returns out, with
+    q's shape (``out=v`` overwrites v)."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [N, T, H, 128]")
+    N, T, H, D = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("libkda runs on the GPU: tensors must be on a cuda (HIP) device")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
+                        ("g", g, torch.float32), ("beta", beta, torch.float32),
+                        ("state_pool", state_pool, torch.float32),
+                        ("state_indices", state_indices, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, v and g must have the same shape")
+    if beta.shape != q.shape[:-1]:
+        raise ValueError("beta must be q.shape[:-1]")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError(f"state_pool must be [P, {H}, {D}, {D}]")
+    if tuple(state_indices.shape) != (N,):
+        raise ValueError(f"state_indices must be [{N}]")
+    if scale is None:
+        scale = D ** -0.5
+    prob = make_decode_problem(N, T, H, state_pool.shape[0], scale=scale,
+                               gate_lower_bound=gate_lower_bound, head_dim_k=D, head_dim_v=D)
+    if out is None:
+        out = torch.empty_like(v)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 with q's shape")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = decode_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                        _ptr(state_indices), _ptr(out), int(stream.cuda_stream))
+    _check(st, "kda_decode")
+    return out

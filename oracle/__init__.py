@@ -113,6 +113,39 @@ def prefill_problem(p, *, threads: Optional[int] = None) -> dict:
                    initial_state=p.initial_state, ckpt_offsets=p.ckpt_offsets, threads=threads)
 
 
+def decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, g: np.ndarray,
+           beta: np.ndarray, *, scale: float, num_seqs: int, tokens_per_seq: int,
+           state_pool: np.ndarray, state_indices: np.ndarray,
+           threads: Optional[int] = None) -> dict:
+    """State-pool decode: request n advances by tokens_per_seq tokens from
+    state_pool[state_indices[n]] and the result replaces that pool entry.
+
+    This is the serving step of the sglang KDA decode backend (the state pool
+    and its ssm_state_indices, FlashInferKDAKernel page; FlashInfer PR #4262,
+    Description, names decode and state-pool features).  The pages give no
+    formula for it beyond the recurrence itself, so the reading is: the same
+    token recurrence as ``prefill`` (decay, delta-rule correction, read-out),
+    run from the pool entry; an index outside [0, pool_size) means an empty
+    request slot: zero outputs, pool untouched.
+
+    Inputs are request-major [N * T, H, ...] arrays as in ``prefill``'s fixed
+    layout; state_pool [P, H, K, V] fp32; state_indices [N] int.  Returns
+    dict(out [N*T, H, V] fp64, pool [P, H, K, V] fp64 after the step)."""
+    N, T = int(num_seqs), int(tokens_per_seq)
+    idx = np.asarray(state_indices, np.int64)
+    P, H = state_pool.shape[0], state_pool.shape[1]
+    pool = state_pool.astype(np.float64)
+    out = np.zeros((N * T, H, v_bits.shape[2]), np.float64)
+    live = [n for n in range(N) if 0 <= idx[n] < P]
+    if live:
+        rows = np.concatenate([np.arange(n * T, (n + 1) * T) for n in live])
+        res = prefill(q_bits[rows], k_bits[rows], v_bits[rows], g[rows], beta[rows], scale=scale,
+                      num_seqs=len(live), initial_state=state_pool[idx[live]], threads=threads)
+        out[rows] = res["out"]
+        pool[idx[live]] = res["final"]
+    return {"out": out, "pool": pool}
+
+
 def prefill_with_library(path: str):
     """Return a ``prefill`` bound to another build of kda_oracle.c (used by the
     tests that plant mistakes in a copy of the oracle and check that the pins

@@ -219,3 +219,67 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         K.prefill(q, q, q, torch.zeros(4, 2, 128), torch.zeros(4, 2))
+
+
+class DecodeBufs:
+    """Fake, 16-byte aligned, non-overlapping host addresses for kda_decode."""
+
+    def __init__(self, N=4, T=2, H=3, P=6):
+        self.N, self.T, self.H, self.P = N, T, H, P
+        rows = N * T * H
+        base = 1 << 41
+        sizes = {"q": rows * 256, "k": rows * 256, "v": rows * 256, "g": rows * 512,
+                 "beta": rows * 4, "pool": P * H * 65536, "idx": N * 4, "out": rows * 256}
+        self.addr = {}
+        for k_, sz in sizes.items():
+            self.addr[k_] = base
+            base += (sz + 4095) // 4096 * 4096 + 4096
+
+    def args(self, **over):
+        a = dict(self.addr)
+        a.update(over)
+        return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["idx"], a["out"]]
+
+
+def _dprob(b, **kw):
+    d = dict(scale=0.0884)
+    d.update({k_: v_ for k_, v_ in kw.items() if k_ in ("scale", "gate_lower_bound", "head_dim_k",
+                                                        "head_dim_v")})
+    return ops.make_decode_problem(kw.get("N", b.N), kw.get("T", b.T), kw.get("H", b.H),
+                                   kw.get("P", b.P), **d)
+
+
+def test_decode_validation_rules():
+    b = DecodeBufs()
+    dv = ops.decode_validate_raw
+    assert dv(_dprob(b), *b.args()) == OK
+    # empty batch: nothing to check but the scalars
+    assert dv(_dprob(b, N=0), *[0] * 8) == OK
+    assert dv(_dprob(b, T=0), *b.args()) == INVALID
+    assert dv(_dprob(b, P=0), *b.args()) == INVALID
+    assert dv(_dprob(b, H=0), *b.args()) == INVALID
+    assert dv(_dprob(b, head_dim_k=64), *b.args()) == UNSUPPORTED
+    assert dv(_dprob(b, gate_lower_bound=-6.0), *b.args()) == INVALID
+    assert dv(_dprob(b, gate_lower_bound=0.5), *b.args()) == INVALID
+    assert dv(_dprob(b, scale=float("nan")), *b.args()) == INVALID
+    assert dv(_dprob(b), *b.args(idx=0)) == INVALID
+    assert dv(_dprob(b), *b.args(pool=b.addr["pool"] + 4)) == ALIGN
+    # out may be exactly v, nothing else
+    assert dv(_dprob(b), *b.args(out=b.addr["v"])) == OK
+    assert dv(_dprob(b), *b.args(out=b.addr["v"] + 256)) == OVERLAP
+    assert dv(_dprob(b), *b.args(out=b.addr["pool"])) == OVERLAP
+    assert dv(_dprob(b), *b.args(pool=b.addr["idx"])) == OVERLAP
+    assert dv(_dprob(b), *b.args(pool=b.addr["q"])) == OVERLAP
+    # flat output index bound
+    assert dv(_dprob(b, N=1 << 20, T=16, H=2), *b.args()) == TOO_LARGE
+
+
+def test_decode_rejects_on_the_host():
+    # argument errors come back before anything touches a device
+    b = DecodeBufs()
+    lib = K.load_library()
+    prob = _dprob(b, T=0)
+    P = b.args()
+    assert lib.kda_decode(ctypes.byref(prob), *P, None) == INVALID
+    prob = _dprob(b)
+    assert lib.kda_decode(ctypes.byref(prob), *b.args(out=b.addr["pool"]), None) == OVERLAP
