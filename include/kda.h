@@ -38,11 +38,16 @@
  *   final_state    fp32  [N, H, 128, 128], or NULL; may be exactly
  *                  initial_state (in-place update, FlashInfer PR #4262,
  *                  Physical schedules and true in-place state update)
- *   ckpt_offsets   int32 [N], or NULL: ckpt_offsets[n] = number of tokens of
- *                  sequence n consumed when its state is exported (0 exports
- *                  the initial state, L_n the final state).  Offsets outside
- *                  [0, L_n] export nothing and leave that slot untouched.
- *   ckpt_state     fp32  [N, H, 128, 128] caller-owned, contiguous; NULL iff
+ *   ckpt_offsets   int32 [N, C] (C = kda_problem.ckpt_per_seq, 1 by default),
+ *                  or NULL: ckpt_offsets[n, c] = number of tokens of sequence
+ *                  n consumed when its state is exported into slot c (0
+ *                  exports the initial state, L_n the final state).  A
+ *                  sequence's offsets are taken in order; one is honoured when
+ *                  it lies in [0, L_n] and is not below the previous honoured
+ *                  one.  The others export nothing and leave their slot
+ *                  untouched, so -1 pads a shorter list (e.g. periodic
+ *                  checkpoints every n tokens of sequences of unequal length).
+ *   ckpt_state     fp32  [N, C, H, 128, 128] caller-owned, contiguous; NULL iff
  *                  ckpt_offsets is NULL; must not overlap either state buffer.
  *
  * Ownership and streams: every buffer belongs to the caller; the library
@@ -103,6 +108,9 @@ typedef struct {
                                 KDA_STAGE_RECURRENCE = only the recurrence, which reads a
                                 workspace that an earlier PREPARE call filled from the same
                                 inputs and problem (the caller's contract, not checked) */
+  int32_t ckpt_per_seq;      /* C, checkpoint offsets per sequence, 0..64 (0 means 1).
+                                ckpt_offsets is then int32 [N, C] and ckpt_state fp32
+                                [N, C, H, 128, 128]; see kda_prefill */
 } kda_problem;
 
 enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
@@ -110,8 +118,9 @@ enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
 /* Bytes of caller workspace kda_prefill needs for this problem (host only, no
  * device access).  FUSED needs none (0).  DECOMP, and AUTO so that it may
  * pick DECOMP, need a header of 2 N + 1 int32 rounded up to 256 bytes plus
- * 64,512 bytes per (segment slot, head), with floor(T_total / 64) + 2 N
- * segment slots: about 1.01 KiB per token-head.  The workspace is scratch:
+ * 64,512 bytes per (segment slot, head), with floor(T_total / 64) + N + N C
+ * segment slots (C = ckpt_per_seq, at least 1): about 1.01 KiB per
+ * token-head.  The workspace is scratch:
  * it carries nothing between calls, may be reused by any later call on the
  * same stream, and must not be used by two calls in flight at once. */
 kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes);

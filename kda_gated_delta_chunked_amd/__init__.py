@@ -6,9 +6,9 @@ requests held in a state pool by a few tokens.  ``synth`` draws the
 seeded synthetic workloads used by the tests and the benchmark.
 """
 from .ops import (DecodeProblem, KDAError, Problem, decode, decode_raw, decode_validate_raw,
-                  load_library, library_path, make_decode_problem, make_problem, plan, prefill,
-                  prefill_raw, validate_raw, workspace_size)
+                  load_library, library_path, make_decode_problem, make_problem, periodic_offsets,
+                  plan, prefill, prefill_raw, validate_raw, workspace_size)
 
 __all__ = ["DecodeProblem", "KDAError", "Problem", "decode", "decode_raw", "decode_validate_raw",
-           "load_library", "library_path", "make_decode_problem", "make_problem", "plan",
-           "prefill", "prefill_raw", "validate_raw", "workspace_size"]
+           "load_library", "library_path", "make_decode_problem", "make_problem",
+           "periodic_offsets", "plan", "prefill", "prefill_raw", "validate_raw", "workspace_size"]

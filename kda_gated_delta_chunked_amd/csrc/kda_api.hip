@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int kHeadDim = 128;
+constexpr int kMaxCkptPerSeq = 64;
 constexpr int64_t kInt32Max = 2147483647LL;
 
 struct Range {
@@ -36,6 +37,9 @@ bool exact(const Range& a, const Range& b) { return !a.empty() && a.lo == b.lo &
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// checkpoint offsets per sequence (0 in the problem means 1)
+int ckpt_count(const kda_problem* p) { return p->ckpt_per_seq > 1 ? p->ckpt_per_seq : 1; }
+
 kda_status check_problem(const kda_problem* p) {
   if (!p) return KDA_ERR_INVALID_ARG;
   if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
@@ -53,6 +57,8 @@ kda_status check_problem(const kda_problem* p) {
   if (p->variant == KDA_VARIANT_FUSED && (vs == 1 || vs == 8)) return KDA_ERR_UNSUPPORTED;
   if (p->stages < 0 || p->stages > KDA_STAGE_RECURRENCE) return KDA_ERR_INVALID_ARG;
   if (p->stages != 0 && p->variant != KDA_VARIANT_DECOMP) return KDA_ERR_UNSUPPORTED;
+  if (p->ckpt_per_seq < 0) return KDA_ERR_INVALID_ARG;
+  if (p->ckpt_per_seq > kMaxCkptPerSeq) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if ((int64_t)p->num_seqs * p->num_heads > kInt32Max / 8) return KDA_ERR_TOO_LARGE;
@@ -76,7 +82,8 @@ int device_cu_count() {
 size_t decomp_bytes(const kda_problem* p) {
   size_t header = 0, bytes = 0;
   int64_t slots = 0;
-  kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, &header, &slots, &bytes);
+  kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, ckpt_count(p), &header,
+                              &slots, &bytes);
   return bytes;
 }
 
@@ -165,8 +172,8 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
   const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4);
   const Range rs0 = range_of(initial_state, state);
   const Range rout = range_of(out, tok_bf16), rfin = range_of(final_state, state);
-  const Range roff = range_of(ckpt_offsets, (uint64_t)N * 4);
-  const Range rck = range_of(ckpt_state, state);
+  const Range roff = range_of(ckpt_offsets, (uint64_t)N * ckpt_count(p) * 4);
+  const Range rck = range_of(ckpt_state, state * ckpt_count(p));
   const Range rws = range_of(workspace, workspace_bytes);
 
   // out: may be exactly v; must not touch any other buffer
@@ -210,7 +217,8 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
   if (variant == KDA_VARIANT_DECOMP) {
     size_t header = 0, bytes = 0;
     int64_t slots = 0;
-    kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, &header, &slots, &bytes);
+    kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, ckpt_count(p), &header,
+                              &slots, &bytes);
     kda::DecompArgs a;
     a.q = q;
     a.k = k;
@@ -223,6 +231,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.final_state = final_state;
     a.ckpt_off = ckpt_offsets;
     a.ckpt = ckpt_state;
+    a.ckpt_per_seq = ckpt_count(p);
     a.seg_base = static_cast<int32_t*>(workspace);
     a.order = cu_seqlens ? a.seg_base + p->num_seqs + 1 : nullptr;
     a.slots = static_cast<unsigned char*>(workspace) + header;
@@ -230,7 +239,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.H = p->num_heads;
     a.T_total = p->total_tokens;
     a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
-    a.slots_per_seq = cu_seqlens ? 0 : (a.T_fixed + 63) / 64 + (ckpt_offsets ? 1 : 0);
+    a.slots_per_seq = cu_seqlens ? 0 : (a.T_fixed + 63) / 64 + (ckpt_offsets ? a.ckpt_per_seq : 0);
     a.slot_bound = slots;
     a.scale = p->scale;
     const int64_t prepare_slots = cu_seqlens ? slots : (int64_t)p->num_seqs * a.slots_per_seq;
@@ -249,6 +258,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.final_state = final_state;
     a.ckpt_off = ckpt_offsets;
     a.ckpt = ckpt_state;
+    a.ckpt_per_seq = ckpt_count(p);
     a.N = p->num_seqs;
     a.H = p->num_heads;
     a.num_pairs = p->num_seqs * p->num_heads;

@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_ckpt.h"
 #include "kda_kernels.h"
 
 namespace kda {
@@ -66,9 +67,13 @@ constexpr int SL_M = 53248;     // M  : token tile t x token block b <= t/2 (6 f
 constexpr int SL_N = 58368;     // N  : same tiling as M
 constexpr int SL_GAM = 63488;   // exp(G_end), 128 fp32
 constexpr int SL_BETA = 64000;  // beta per tile row, 64 fp32 (0 on empty rows)
+// segment header: int32 off (first tile row of the segment), int32 spare,
+// int64 tok0 (token of tile row 0), uint64 export mask (bit c: checkpoint c
+// of the sequence is the state after this segment)
+constexpr int SL_HDR = 64256;
 constexpr int SLOT_UNITS = 63;  // 1 KiB copy units per slot
 static_assert(SLOT_UNITS * 1024 == kDecompSlotBytes, "slot size");
-static_assert(SL_BETA + 256 <= kDecompSlotBytes, "slot layout");
+static_assert(SL_BETA + 256 <= SL_HDR && SL_HDR + 24 <= kDecompSlotBytes, "slot layout");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -135,9 +140,8 @@ __host__ __device__ constexpr int tri_off(int f) {
 struct SeqInfo {
   int64_t bos;   // first token of the sequence
   int len;       // tokens
-  int p;         // checkpoint offset (-1 when none)
-  int nseg;      // segments
-  bool split;    // the chunk holding p is cut at p
+  int nseg;      // segments: the 64-token chunks, those holding a cut point cut in two
+  CkptList ck;   // checkpoint offsets (C = 0 when none)
 };
 
 __device__ __forceinline__ SeqInfo seq_info(const DecompArgs& a, int n) {
@@ -155,32 +159,21 @@ __device__ __forceinline__ SeqInfo seq_info(const DecompArgs& a, int n) {
   e = e < b ? b : (e > a.T_total ? a.T_total : e);
   s.bos = b;
   s.len = (int)(e - b);
-  s.p = a.ckpt_off ? a.ckpt_off[n] : -1;
-  s.split = s.p > 0 && s.p < s.len && (s.p & (CH - 1)) != 0;
-  s.nseg = (s.len + CH - 1) / CH + (s.split ? 1 : 0);
+  s.ck = load_ckpt_list(a.ckpt_off, a.ckpt_per_seq, n, s.len);
+  s.nseg = (s.len + CH - 1) / CH + count_cuts(s.ck);
   return s;
 }
 
 // token range [lo, hi) of segment j, relative to the sequence start
 __device__ __forceinline__ void seg_range(const SeqInfo& s, int j, int& lo, int& hi) {
-  const int pc = s.split ? (s.p >> 6) : 0x7fffffff;
-  if (j < pc) {
-    lo = CH * j;
-    hi = min(lo + CH, s.len);
-  } else if (j == pc) {
-    lo = CH * j;
-    hi = s.p;
-  } else {
-    const int jj = j - 1;
-    lo = (j == pc + 1) ? s.p : CH * jj;
-    hi = min(CH * jj + CH, s.len);
-  }
+  lo = j == 0 ? 0 : interior_boundary(s.ck, j - 1);
+  hi = j >= s.nseg - 1 ? s.len : interior_boundary(s.ck, j);
 }
 
 // ---------------------------------------------------------------------------
 // Launch 0 (packed layout only): first slot of every sequence.  Sequence n
-// owns ceil(L_n / 64) slots, plus one when checkpoints are requested (the
-// chunk cut at the offset).  base[N] is the total.
+// owns ceil(L_n / 64) slots, plus C when C checkpoint offsets per sequence are
+// requested (each may cut a chunk in two).  base[N] is the total.
 //
 // It also writes the order in which the recurrence takes the sequences:
 // longest first (ties by index), so that when there are more workgroups than
@@ -194,7 +187,7 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t nslots[kOrderMax];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int extra = a.ckpt_off ? 1 : 0;
+  const int extra = a.ckpt_off ? a.ckpt_per_seq : 0;
   int64_t carry = 0;
   for (int n0 = 0; n0 < a.N; n0 += 1024) {
     const int n = n0 + t;
@@ -389,6 +382,16 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     reinterpret_cast<float*>(slot + SL_GAM)[d] = __expf(b0 + b1 + b2 + b3);
   } else if (tid < DK + CH) {
     reinterpret_cast<float*>(slot + SL_BETA)[tid - DK] = sB[tid - DK];
+  } else if (tid == DK + CH) {
+    // the recurrence's compute waves take the segment geometry and the
+    // checkpoints it completes from here, with no scalar memory access
+    unsigned long long mask = 0;
+    for_each_honoured(si.ck, [&](int c, int p) {
+      if (p > 0 && p == hi_t) mask |= 1ull << c;
+    });
+    *reinterpret_cast<int4*>(slot + SL_HDR) =
+        make_int4(off, 0, (int)(uint32_t)(uint64_t)tok0, (int)(uint32_t)((uint64_t)tok0 >> 32));
+    *reinterpret_cast<unsigned long long*>(slot + SL_HDR + 16) = mask;
   }
   __syncthreads();
 
@@ -695,14 +698,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   if (w >= CW) {
     // ---- copy waves: unit u of the slot (or of the V block) goes to copy wave u % KW
     const int cw = w - CW;
-    auto copy = [&](int jseg, uint4* dst) {
+    // geometry (off, tok0) of the segment copied next, worked out one copy
+    // ahead: its scalar reads of the checkpoint offsets then wait while the
+    // previous copy is in flight, not before the V rows are requested
+    auto copy = [&](int jseg, uint4* dst, int off, int64_t tok0) {
       const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
       for (int u = cw; u < SLOT_UNITS; u += KW)
         __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
-      // V rows 0..63 (rows before the segment read row `off`, zeroed on use)
-      int off;
-      int64_t tok0;
-      geometry(jseg, off, tok0);
+      // V rows 0..63 (rows before the segment read row `off`; their beta is 0)
       constexpr int LPR = VW / 8, RPI = 64 / LPR;  // lanes per row, rows per unit
       for (int k = cw; k < VUNITS; k += KW) {
         const int row = max(k * RPI + lane / LPR, off);
@@ -710,15 +713,25 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
         __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS + k) * 64, 16, 0, 0);
       }
     };
-    if (nseg > 0) copy(0, opsA);
+    int goff = 0;
+    int64_t gtok = 0;
+    if (nseg > 0) {
+      geometry(0, goff, gtok);
+      copy(0, opsA, goff, gtok);
+    }
+    if (nseg > 1) geometry(1, goff, gtok);
     for (int jseg = 0; jseg < nseg; jseg += 2) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
       __syncthreads();
-      if (jseg + 1 < nseg) copy(jseg + 1, opsB);
       if (jseg + 1 < nseg) {
+        copy(jseg + 1, opsB, goff, gtok);
+        if (jseg + 2 < nseg) geometry(jseg + 2, goff, gtok);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (jseg + 2 < nseg) copy(jseg + 2, opsA);
+        if (jseg + 2 < nseg) {
+          copy(jseg + 2, opsA, goff, gtok);
+          if (jseg + 3 < nseg) geometry(jseg + 3, goff, gtok);
+        }
       }
     }
     return;
@@ -748,7 +761,13 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
       for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = S[m][e];
   };
-  if (a.ckpt_off && si.p == 0) store_state(a.ckpt);
+  // checkpoint c of this sequence (layout [N, C, H, K, V])
+  auto ckpt_slot = [&](int c) {
+    return a.ckpt + ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DK;
+  };
+  for_each_honoured(si.ck, [&](int c, int p) {
+    if (p == 0) store_state(ckpt_slot(c));
+  });
 
   uint32_t opk[8];
   int poff = CH;
@@ -831,9 +850,11 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4 + b], Sb[b], X[t]);
     KDA_FENCE();
     // the rest of Q~, the V block and N, read while O^T = S^T Q~^T runs
-    int off;
-    int64_t tok0;
-    geometry(jseg, off, tok0);
+    const int4 hd = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(cur) + SL_HDR);
+    const uint2 hmask = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_HDR + 16);
+    const int off = __builtin_amdgcn_readfirstlane(hd.x);
+    const int64_t tok0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(hd.w) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane(hd.z));
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -923,10 +944,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     poff = off;
     ptok = tok0;
     pend = true;
-    if (a.ckpt_off && si.p > 0) {
-      int lo, hi;
-      seg_range(si, jseg, lo, hi);
-      if (hi == si.p) store_state(a.ckpt);
+    if (si.ck.C > 0) {
+      unsigned long long mask = ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane(hmask.y) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane(hmask.x);
+      while (mask) {
+        const int c = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        store_state(ckpt_slot(c));
+      }
     }
   };
 

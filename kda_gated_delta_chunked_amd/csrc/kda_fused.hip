@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_ckpt.h"
 #include "kda_kernels.h"
 
 namespace kda {
@@ -178,7 +179,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     len = a.T_fixed;
     bos = (int64_t)n * len;
   }
-  const int64_t ckpt_at = a.ckpt_off ? (int64_t)a.ckpt_off[n] : -1;
+  // checkpoint offsets of the sequence (C = 0 when none)
+  const CkptList ck = load_ckpt_list(a.ckpt_off, a.ckpt_per_seq, n, (int)len);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // w is wave-uniform
@@ -247,7 +249,13 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       }
   };
 
-  if (ckpt_at == 0) export_state(a.ckpt);
+  // checkpoint c of this sequence (layout [N, C, H, K, V])
+  auto ckpt_slot = [&](int c) {
+    return a.ckpt + ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DVT;
+  };
+  for_each_honoured(ck, [&](int c, int p) {
+    if (p == 0) export_state(ckpt_slot(c));
+  });
 
   // elementwise role: block ib, rows 16ib + 8hb .. +7, channels d0, d0+1
   const int ib = w >> 1;
@@ -264,10 +272,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
   // zero and contribute nothing), so its final 16 tokens are always tile rows
   // 48..63, the rows whose K exp(G_end - G) carries a lo part.  Tile row r
   // holds token tok0 + r.
-  auto seg_end_of = [&](int64_t p0) {
-    const int64_t ce = (p0 / CH + 1) * CH < len ? (p0 / CH + 1) * CH : len;
-    return (ckpt_at > p0 && ckpt_at < ce) ? ckpt_at : ce;
-  };
+  auto seg_end_of = [&](int64_t p0) { return (int64_t)next_boundary(ck, (int)p0); };
   const size_t row_stride = (size_t)H * DK;   // elements between consecutive tokens
   auto load_segment = [&](int64_t p0, SegmentLoads& L) {
     const int d0 = 2 * l;
@@ -775,7 +780,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
 
     pending_off = off;
     pending_tok0 = tok0;
-    if (seg_end == ckpt_at) export_state(a.ckpt);
+    for_each_honoured(ck, [&](int c, int p) {
+      if (p > 0 && p == seg_end) export_state(ckpt_slot(c));
+    });
     pos = seg_end;
   }
 

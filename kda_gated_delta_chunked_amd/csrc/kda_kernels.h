@@ -18,8 +18,9 @@ struct FusedArgs {
   const float* s0;            // NULL: zero initial state
   uint16_t* out;
   float* final_state;         // may be NULL
-  const int32_t* ckpt_off;    // NULL: no export
-  float* ckpt;
+  const int32_t* ckpt_off;    // [N, ckpt_per_seq]; NULL: no export
+  float* ckpt;                // [N, ckpt_per_seq, H, 128, 128]
+  int ckpt_per_seq;           // C >= 1
   int N;
   int H;
   int num_pairs;              // N * H
@@ -45,8 +46,9 @@ struct DecompArgs {
   const float* s0;            // NULL: zero initial state
   uint16_t* out;
   float* final_state;         // may be NULL
-  const int32_t* ckpt_off;    // NULL: no export
-  float* ckpt;
+  const int32_t* ckpt_off;    // [N, ckpt_per_seq]; NULL: no export
+  float* ckpt;                // [N, ckpt_per_seq, H, 128, 128]
+  int ckpt_per_seq;           // C >= 1
   unsigned char* slots;       // workspace slot area
   int32_t* seg_base;          // workspace header: first slot of each sequence (packed layout)
   int32_t* order;             // workspace header: sequences by decreasing length (packed layout), or NULL
@@ -60,12 +62,12 @@ struct DecompArgs {
 };
 
 // Workspace layout for (N, T_total, H): header bytes and slot capacity.
-inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, size_t* header,
-                                    int64_t* slots, size_t* bytes) {
+inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64_t C,
+                                    size_t* header, int64_t* slots, size_t* bytes) {
   *header = (size_t)(((2 * N + 1) * 4 + 255) / 256 * 256);
-  // ceil(L/64) summed over sequences is at most floor(T/64) + N; one more per
-  // sequence for the chunk cut at a checkpoint offset
-  *slots = T_total / 64 + 2 * N;
+  // ceil(L/64) summed over sequences is at most floor(T/64) + N; C more per
+  // sequence for the chunks cut at its C checkpoint offsets
+  *slots = T_total / 64 + N + N * (C < 1 ? 1 : C);
   *bytes = *header + (size_t)(*slots) * (size_t)H * kDecompSlotBytes;
 }
 

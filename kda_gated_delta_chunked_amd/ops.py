@@ -41,7 +41,8 @@ class Problem(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
                 ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("gate_lower_bound", ctypes.c_float), ("variant", ctypes.c_int32),
-                ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32)]
+                ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("ckpt_per_seq", ctypes.c_int32)]
 
 
 STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
@@ -66,11 +67,29 @@ def make_decode_problem(num_seqs: int, tokens_per_seq: int, num_heads: int, pool
 def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: float,
                  gate_lower_bound: float = -5.0, variant: str | int = "auto",
                  value_split: int = 0, head_dim_k: int = HEAD_DIM,
-                 head_dim_v: int = HEAD_DIM, stages: str | int = "both") -> Problem:
+                 head_dim_v: int = HEAD_DIM, stages: str | int = "both",
+                 ckpt_per_seq: int = 0) -> Problem:
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     st = STAGES[stages] if isinstance(stages, str) else int(stages)
     return Problem(int(num_seqs), int(total_tokens), int(num_heads), int(head_dim_k),
-                   int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st)
+                   int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st,
+                   int(ckpt_per_seq))
+
+
+def periodic_offsets(seq_lens, every: int):
+    """Checkpoint offsets [N, C] (int32 numpy) for a checkpoint every `every`
+    tokens of each sequence (every, 2 every, ... <= L_n), padded with -1 (an
+    offset that exports nothing) up to the longest list; C >= 1."""
+    import numpy as np
+    if every < 1:
+        raise ValueError("every must be >= 1")
+    lens = [int(x) for x in seq_lens]
+    C = max([1] + [L // every for L in lens])
+    offs = np.full((len(lens), C), -1, np.int32)
+    for n, L in enumerate(lens):
+        m = L // every
+        offs[n, :m] = np.arange(1, m + 1, dtype=np.int64) * every
+    return offs
 
 
 def library_path() -> str:
@@ -166,7 +185,9 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
     shape, final_state is None when output_final_state is False.  Pass
     ``final_state=initial_state`` for an in-place update and ``out=v`` to
     overwrite v.  ckpt_offsets int32 [N] / ckpt_state fp32 [N, H, 128, 128]
-    export the state after ckpt_offsets[n] tokens of sequence n.
+    export the state after ckpt_offsets[n] tokens of sequence n; with
+    ckpt_offsets [N, C] and ckpt_state [N, C, H, 128, 128], C states per
+    sequence (``periodic_offsets`` builds a checkpoint every n tokens).
     workspace: a device buffer of at least ``workspace_size`` bytes; when None
     and the schedule may use one, a buffer is taken from torch's allocator.
     """
@@ -212,14 +233,23 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         if t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on {dev}")
     state_shape = (N, H, D, D)
-    for name, t in (("initial_state", initial_state), ("final_state", final_state),
-                    ("ckpt_state", ckpt_state)):
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
         if t is not None and tuple(t.shape) != state_shape:
             raise ValueError(f"{name} must have shape {state_shape}")
+    C = 1
+    if ckpt_offsets is not None:
+        if ckpt_offsets.dim() == 2:
+            C = int(ckpt_offsets.shape[1])
+        if tuple(ckpt_offsets.shape) not in ((N,), (N, C)) or ckpt_state is None:
+            raise ValueError("ckpt_offsets must be [N] or [N, C], with ckpt_state")
+        want = (N, H, D, D) if ckpt_offsets.dim() == 1 else (N, C, H, D, D)
+        if tuple(ckpt_state.shape) != want:
+            raise ValueError(f"ckpt_state must have shape {want}")
     if scale is None:
         scale = D ** -0.5
     prob = make_problem(N, T_total, H, scale=scale, gate_lower_bound=gate_lower_bound,
-                        variant=variant, value_split=value_split, head_dim_k=D, head_dim_v=D)
+                        variant=variant, value_split=value_split, head_dim_k=D, head_dim_v=D,
+                        ckpt_per_seq=C)
     if out is None:
         out = torch.empty_like(v)
     elif out.shape != q.shape:

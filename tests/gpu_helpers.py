@@ -54,9 +54,13 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
         fin = torch.full((N, H, 128, 128), float("nan") if sentinel else 0.0, dtype=torch.float32,
                          device=dev)
     ck = None
+    C = 0
     if d["offs"] is not None:
-        ck = torch.full((N, H, 128, 128), float("nan"), dtype=torch.float32, device=dev)
-    prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split)
+        C = 1 if d["offs"].dim() == 1 else int(d["offs"].shape[1])
+        shape = (N, H, 128, 128) if d["offs"].dim() == 1 else (N, C, H, 128, 128)
+        ck = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+    prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split,
+                          ckpt_per_seq=C)
     need = K.workspace_size(prob)
     ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev) if need else None
     stream = torch.cuda.current_stream(dev)

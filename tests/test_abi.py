@@ -145,10 +145,41 @@ def test_prefill_rejects_on_the_host_without_a_device():
     assert st == OVERLAP
 
 
-def decomp_bytes(N, T, H):
-    """The documented workspace formula: (N + 1) int32 rounded up to 256 bytes,
-    then 64,512 bytes per (segment slot, head) for floor(T / 64) + 2 N slots."""
-    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + 2 * N) * H * 64512
+def decomp_bytes(N, T, H, C=1):
+    """The documented workspace formula: 2 N + 1 int32 rounded up to 256
+    bytes, then 64,512 bytes per (segment slot, head) for floor(T / 64) + N +
+    N C slots (C checkpoint offsets per sequence, at least 1)."""
+    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + N + N * max(C, 1)) * H * 64512
+
+
+def test_workspace_grows_with_checkpoints_per_sequence():
+    for C in (0, 1, 2, 7, 64):
+        p = K.make_problem(3, 1000, 2, scale=0.088, variant="decomp", ckpt_per_seq=C)
+        assert K.workspace_size(p) == decomp_bytes(3, 1000, 2, C)
+    with pytest.raises(K.KDAError):
+        K.workspace_size(K.make_problem(3, 1000, 2, scale=0.088, ckpt_per_seq=65))
+    with pytest.raises(K.KDAError):
+        K.workspace_size(K.make_problem(3, 1000, 2, scale=0.088, ckpt_per_seq=-1))
+
+
+def test_checkpoint_buffers_scale_with_offsets_per_sequence():
+    # with C offsets per sequence the checkpoint buffer spans N C states: a
+    # final state placed right after a one-state-per-sequence buffer overlaps it
+    b = Bufs()
+    C = 3
+    prob = K.make_problem(b.N, b.T, b.H, scale=0.088, variant="fused", ckpt_per_seq=C)
+    ck = b.addr["ck"]
+    state = b.N * b.H * 65536
+    assert ops.validate_raw(prob, *b.args(fin=0)[:-2], 0, 0) == OK
+    assert ops.validate_raw(prob, *b.args(fin=ck + state)[:-2], 0, 0) == OVERLAP
+    assert ops.validate_raw(prob, *b.args(fin=ck + C * state)[:-2], 0, 0) == OK
+
+
+def test_periodic_offsets():
+    offs = K.periodic_offsets([0, 5, 64, 200], 64)
+    assert offs.dtype.name == "int32" and offs.shape == (4, 3)
+    assert offs.tolist() == [[-1, -1, -1], [-1, -1, -1], [64, -1, -1], [64, 128, 192]]
+    assert K.periodic_offsets([10], 64).tolist() == [[-1]]
 
 
 def test_workspace_size_and_plan_arguments():

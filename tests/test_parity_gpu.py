@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import assert_parity, metrics, run_gpu, to_device
+from gpu_helpers import assert_parity, metrics, rel_l2, run_gpu, to_device
 from kda_gated_delta_chunked_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -177,6 +177,68 @@ def test_decomp_matches_fused_on_packed_layout_as_separate_runs():
         assert np.array_equal(one["out"], whole["out"][sl]), n
         assert np.array_equal(one["final"][0], whole["final"][n]), n
         t0 += L
+
+
+def _honoured(offs, L):
+    """Offsets taken in order, honoured when inside [0, L] and not below the
+    previous honoured one."""
+    out, last = [], 0
+    for c, x in enumerate(offs):
+        if 0 <= x <= L and x >= last:
+            out.append(c)
+            last = x
+    return out
+
+
+def _check_multi_ckpt(p, offs, gpu):
+    # each honoured slot holds the state after that many tokens (the oracle
+    # run with that one offset); the others keep their NaN sentinel
+    for c in range(offs.shape[1]):
+        col = offs[:, c].copy()
+        ref = oracle.prefill(p.q, p.k, p.v, p.g, p.beta, scale=p.scale, num_seqs=p.N,
+                             cu_seqlens=None if p.fixed else p.cu_seqlens,
+                             initial_state=p.initial_state, ckpt_offsets=col)
+        for n, L in enumerate(p.seq_lens):
+            if c in _honoured(list(offs[n]), L):
+                err = rel_l2(gpu["ckpt"][n, c], ref["ckpt"][n])
+                assert err <= 1e-3, (n, c, offs[n, c], err)
+            else:
+                assert np.all(np.isnan(gpu["ckpt"][n, c])), (n, c, offs[n, c])
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_several_checkpoints_per_sequence(variant):
+    lens = [300, 0, 129, 64, 700]
+    offs = np.array([[5, 77, 77, 128, 300, -1],       # duplicate, grid point, the end
+                     [0, 0, 1, -1, -1, -1],            # empty sequence: offset 0 only
+                     [64, 20, 65, 129, 130, 0],        # 20 and 0 come after 64: skipped
+                     [-1, 63, 64, 1, 64, 64],          # 1 after 63: skipped
+                     [1, 2, 3, 4, 699, 700]], np.int32)
+    p = synth.make_problem(lens, 2, seed=19, init_state=True)
+    p.ckpt_offsets = offs
+    p0 = synth.make_problem(lens, 2, seed=19, init_state=True)
+    ref = oracle.prefill_problem(p0)
+    gpu = run_gpu(p, variant=variant)
+    _report(f"6 checkpoints per sequence {variant}", assert_parity(
+        {"out": gpu["out"], "final": gpu["final"]}, ref, "multi-ckpt"))
+    _check_multi_ckpt(p, offs, gpu)
+    # an offset of L exports the final state bit for bit, 0 the initial state
+    assert np.array_equal(gpu["ckpt"][0, 4], gpu["final"][0])
+    assert np.array_equal(gpu["ckpt"][1, 0], p.initial_state[1])
+    assert np.array_equal(gpu["ckpt"][4, 5], gpu["final"][4])
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_periodic_checkpoints(variant):
+    import kda_gated_delta_chunked_amd as K
+    lens = [1000, 37, 512, 333]
+    p = synth.make_problem(lens, 2, seed=20, init_state=True)
+    offs = K.periodic_offsets(lens, 100)
+    p.ckpt_offsets = offs
+    gpu = run_gpu(p, variant=variant)
+    p0 = synth.make_problem(lens, 2, seed=20, init_state=True)
+    assert_parity({"out": gpu["out"], "final": gpu["final"]}, oracle.prefill_problem(p0), "periodic")
+    _check_multi_ckpt(p, offs, gpu)
 
 
 def test_packed_recurrence_order_longest_first():
