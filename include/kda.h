@@ -111,7 +111,17 @@ typedef struct {
   int32_t ckpt_per_seq;      /* C, checkpoint offsets per sequence, 0..64 (0 means 1).
                                 ckpt_offsets is then int32 [N, C] and ckpt_state fp32
                                 [N, C, H, 128, 128]; see kda_prefill */
+  int32_t state_dtype;       /* kda_state_dtype of initial_state, final_state and
+                                ckpt_state (same layouts, 2-byte elements for BF16).
+                                The recurrence itself always carries fp32; a BF16 state
+                                is widened on load and rounded to nearest even on store
+                                (the BF16 state of FlashInfer PR #4262's benchmark) */
 } kda_problem;
+
+typedef enum {
+  KDA_STATE_F32 = 0,         /* fp32 states (the contract the pages fix) */
+  KDA_STATE_BF16 = 1         /* bf16 states */
+} kda_state_dtype;
 
 enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
 

@@ -58,6 +58,7 @@ kda_status check_problem(const kda_problem* p) {
   if (p->stages < 0 || p->stages > KDA_STAGE_RECURRENCE) return KDA_ERR_INVALID_ARG;
   if (p->stages != 0 && p->variant != KDA_VARIANT_DECOMP) return KDA_ERR_UNSUPPORTED;
   if (p->ckpt_per_seq < 0) return KDA_ERR_INVALID_ARG;
+  if (p->state_dtype != KDA_STATE_F32 && p->state_dtype != KDA_STATE_BF16) return KDA_ERR_UNSUPPORTED;
   if (p->ckpt_per_seq > kMaxCkptPerSeq) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
@@ -166,7 +167,8 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
 
   const uint64_t tok_bf16 = (uint64_t)T * H * kHeadDim * 2;
   const uint64_t tok_f32 = (uint64_t)T * H * kHeadDim * 4;
-  const uint64_t state = (uint64_t)N * H * kHeadDim * kHeadDim * 4;
+  const uint64_t state =
+      (uint64_t)N * H * kHeadDim * kHeadDim * (p->state_dtype == KDA_STATE_BF16 ? 2 : 4);
   const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
   const Range rg = range_of(g, tok_f32), rb = range_of(beta, (uint64_t)T * H * 4);
   const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4);
@@ -232,6 +234,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.ckpt_off = ckpt_offsets;
     a.ckpt = ckpt_state;
     a.ckpt_per_seq = ckpt_count(p);
+    a.state_bf16 = p->state_dtype == KDA_STATE_BF16;
     a.seg_base = static_cast<int32_t*>(workspace);
     a.order = cu_seqlens ? a.seg_base + p->num_seqs + 1 : nullptr;
     a.slots = static_cast<unsigned char*>(workspace) + header;
@@ -259,6 +262,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.ckpt_off = ckpt_offsets;
     a.ckpt = ckpt_state;
     a.ckpt_per_seq = ckpt_count(p);
+    a.state_bf16 = p->state_dtype == KDA_STATE_BF16;
     a.N = p->num_seqs;
     a.H = p->num_heads;
     a.num_pairs = p->num_seqs * p->num_heads;

@@ -741,7 +741,13 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   const int col0 = 16 * (part * WAVES + w);
   const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q;
   f32x4 S[8];
-  if (a.s0) {
+  if (a.s0 && a.state_bf16) {
+    const uint16_t* s0 = reinterpret_cast<const uint16_t*>(a.s0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[m][e] = bf2f(s0[sbase + (size_t)(16 * m + 4 * g4 + e) * DK]);
+  } else if (a.s0) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -750,23 +756,32 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
     for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  auto store_state = [&](float* dst) {
+  // state store into dst at element offset e0 (fp32, or bf16 rounded to
+  // nearest even when the states are bf16)
+  auto store_state = [&](float* dst, size_t e0) {
     // the lane's offsets are formed here from an opaque lane index, so the 32
     // store addresses are not kept live in registers across the segment loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    float* rowp = dst + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 4 * DK;
+    const size_t o = e0 + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 4 * DK;
+    if (a.state_bf16) {
+      uint16_t* rowp = reinterpret_cast<uint16_t*>(dst) + o;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = S[m][e];
+        for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = (uint16_t)pack2(S[m][e], 0.f);
+    } else {
+      float* rowp = dst + o;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = S[m][e];
+    }
   };
-  // checkpoint c of this sequence (layout [N, C, H, K, V])
-  auto ckpt_slot = [&](int c) {
-    return a.ckpt + ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DK;
-  };
+  // checkpoint c of this sequence (layout [N, C, H, K, V]): element offset
+  auto ckpt_slot = [&](int c) { return ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DK; };
   for_each_honoured(si.ck, [&](int c, int p) {
-    if (p == 0) store_state(ckpt_slot(c));
+    if (p == 0) store_state(a.ckpt, ckpt_slot(c));
   });
 
   uint32_t opk[8];
@@ -950,7 +965,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       while (mask) {
         const int c = __builtin_ctzll(mask);
         mask &= mask - 1;
-        store_state(ckpt_slot(c));
+        store_state(a.ckpt, ckpt_slot(c));
       }
     }
   };
@@ -960,7 +975,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     if (jseg + 1 < nseg) step(jseg + 1, opsB);
   }
   if (pend) store_out();
-  if (a.final_state) store_state(a.final_state);
+  if (a.final_state) store_state(a.final_state, 0);
 }
 
 template <int CW, int KW>

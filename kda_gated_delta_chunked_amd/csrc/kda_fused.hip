@@ -228,7 +228,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int d = 16 * w + 4 * lg + e;
         const int j = col0 + 16 * nt + lr;
-        S[nt][e] = a.s0 ? a.s0[state_base + (size_t)d * DVT + j] : 0.f;
+        const size_t i = state_base + (size_t)d * DVT + j;
+        S[nt][e] = !a.s0 ? 0.f
+                         : a.state_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.s0)[i]) : a.s0[i];
       }
     // bf16 copy of the state, transposed, as the B operand of the next segment
 #pragma unroll
@@ -237,7 +239,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
           make_uint2(pack2(S[nt][0], S[nt][1]), pack2(S[nt][2], S[nt][3]));
   }
 
-  auto export_state = [&](float* dst) {
+  // state store into dst at element offset e0 (fp32, or bf16 rounded to
+  // nearest even when the states are bf16)
+  auto export_state = [&](float* dst, size_t e0) {
     const int lr = l & 15, lg = l >> 4;
 #pragma unroll
     for (int nt = 0; nt < NTILE; ++nt)
@@ -245,16 +249,18 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int d = 16 * w + 4 * lg + e;
         const int j = col0 + 16 * nt + lr;
-        dst[state_base + (size_t)d * DVT + j] = S[nt][e];
+        const size_t i = e0 + state_base + (size_t)d * DVT + j;
+        if (a.state_bf16)
+          reinterpret_cast<uint16_t*>(dst)[i] = (uint16_t)pack2(S[nt][e], 0.f);
+        else
+          dst[i] = S[nt][e];
       }
   };
 
-  // checkpoint c of this sequence (layout [N, C, H, K, V])
-  auto ckpt_slot = [&](int c) {
-    return a.ckpt + ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DVT;
-  };
+  // checkpoint c of this sequence (layout [N, C, H, K, V]): element offset
+  auto ckpt_slot = [&](int c) { return ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DVT; };
   for_each_honoured(ck, [&](int c, int p) {
-    if (p == 0) export_state(ckpt_slot(c));
+    if (p == 0) export_state(a.ckpt, ckpt_slot(c));
   });
 
   // elementwise role: block ib, rows 16ib + 8hb .. +7, channels d0, d0+1
@@ -781,13 +787,13 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     pending_off = off;
     pending_tok0 = tok0;
     for_each_honoured(ck, [&](int c, int p) {
-      if (p > 0 && p == seg_end) export_state(ckpt_slot(c));
+      if (p > 0 && p == seg_end) export_state(a.ckpt, ckpt_slot(c));
     });
     pos = seg_end;
   }
 
   if (pending_off >= 0) flush_out(pending_off, pending_tok0);
-  if (a.final_state) export_state(a.final_state);
+  if (a.final_state) export_state(a.final_state, 0);
 }
 
 }  // namespace

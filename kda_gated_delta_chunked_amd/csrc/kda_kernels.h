@@ -21,6 +21,7 @@ struct FusedArgs {
   const int32_t* ckpt_off;    // [N, ckpt_per_seq]; NULL: no export
   float* ckpt;                // [N, ckpt_per_seq, H, 128, 128]
   int ckpt_per_seq;           // C >= 1
+  int state_bf16;             // states (s0, final_state, ckpt) are bf16, not fp32
   int N;
   int H;
   int num_pairs;              // N * H
@@ -49,6 +50,7 @@ struct DecompArgs {
   const int32_t* ckpt_off;    // [N, ckpt_per_seq]; NULL: no export
   float* ckpt;                // [N, ckpt_per_seq, H, 128, 128]
   int ckpt_per_seq;           // C >= 1
+  int state_bf16;             // states (s0, final_state, ckpt) are bf16, not fp32
   unsigned char* slots;       // workspace slot area
   int32_t* seg_base;          // workspace header: first slot of each sequence (packed layout)
   int32_t* order;             // workspace header: sequences by decreasing length (packed layout), or NULL

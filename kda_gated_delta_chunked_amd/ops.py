@@ -42,10 +42,11 @@ class Problem(ctypes.Structure):
                 ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("gate_lower_bound", ctypes.c_float), ("variant", ctypes.c_int32),
                 ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32),
-                ("ckpt_per_seq", ctypes.c_int32)]
+                ("ckpt_per_seq", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
+STATE_DTYPES = {"fp32": 0, "bf16": 1}
 
 
 class DecodeProblem(ctypes.Structure):
@@ -68,12 +69,12 @@ def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: flo
                  gate_lower_bound: float = -5.0, variant: str | int = "auto",
                  value_split: int = 0, head_dim_k: int = HEAD_DIM,
                  head_dim_v: int = HEAD_DIM, stages: str | int = "both",
-                 ckpt_per_seq: int = 0) -> Problem:
+                 ckpt_per_seq: int = 0, state_dtype: str = "fp32") -> Problem:
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     st = STAGES[stages] if isinstance(stages, str) else int(stages)
     return Problem(int(num_seqs), int(total_tokens), int(num_heads), int(head_dim_k),
                    int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st,
-                   int(ckpt_per_seq))
+                   int(ckpt_per_seq), STATE_DTYPES[state_dtype])
 
 
 def periodic_offsets(seq_lens, every: int):
@@ -175,13 +176,15 @@ def _ptr(t) -> int:
 def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Optional[float] = None,
             out=None, final_state=None, output_final_state: bool = True, ckpt_offsets=None,
             ckpt_state=None, gate_lower_bound: float = -5.0, variant: str = "auto",
-            value_split: int = 0, workspace=None, stream=None):
+            value_split: int = 0, workspace=None, stream=None, state_dtype=None):
     """KDA multi-token recurrent prefill on the GPU.
 
     q, k, v: bf16 [T, H, 128] (packed, with cu_seqlens int32 [N+1]) or
     [B, T, H, 128] (fixed layout).  g: fp32 like q (log-decay, >= the gate
     lower bound, <= 0).  beta: fp32 [T, H] or [B, T, H].  initial_state:
-    fp32 [N, H, 128, 128] or None.  Returns (out, final_state); out has q's
+    fp32 [N, H, 128, 128] or None; bf16 states (initial, final and
+    checkpoint alike, or state_dtype=torch.bfloat16) are widened on load and
+    rounded on store.  Returns (out, final_state); out has q's
     shape, final_state is None when output_final_state is False.  Pass
     ``final_state=initial_state`` for an in-place update and ``out=v`` to
     overwrite v.  ckpt_offsets int32 [N] / ckpt_state fp32 [N, H, 128, 128]
@@ -222,10 +225,17 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         raise ValueError("q, k, v and g must have the same shape")
     if beta.shape != q.shape[:-1]:
         raise ValueError("beta must be q.shape[:-1]")
+    # states: fp32, or bf16 (all of them alike); taken from the given state
+    # tensors unless state_dtype names it
+    if state_dtype is None:
+        given = [t for t in (initial_state, final_state, ckpt_state) if t is not None]
+        state_dtype = torch.bfloat16 if given and given[0].dtype == torch.bfloat16 else torch.float32
+    if state_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("states must be float32 or bfloat16")
     for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int32), ("initial_state", initial_state,
-                        torch.float32), ("ckpt_offsets", ckpt_offsets, torch.int32),
-                        ("ckpt_state", ckpt_state, torch.float32), ("out", out, torch.bfloat16),
-                        ("final_state", final_state, torch.float32)):
+                        state_dtype), ("ckpt_offsets", ckpt_offsets, torch.int32),
+                        ("ckpt_state", ckpt_state, state_dtype), ("out", out, torch.bfloat16),
+                        ("final_state", final_state, state_dtype)):
         if t is None:
             continue
         if t.dtype != dt:
@@ -249,13 +259,14 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         scale = D ** -0.5
     prob = make_problem(N, T_total, H, scale=scale, gate_lower_bound=gate_lower_bound,
                         variant=variant, value_split=value_split, head_dim_k=D, head_dim_v=D,
-                        ckpt_per_seq=C)
+                        ckpt_per_seq=C,
+                        state_dtype="bf16" if state_dtype == torch.bfloat16 else "fp32")
     if out is None:
         out = torch.empty_like(v)
     elif out.shape != q.shape:
         raise ValueError("out must have q's shape")
     if final_state is None and output_final_state:
-        final_state = torch.empty(state_shape, dtype=torch.float32, device=dev)
+        final_state = torch.empty(state_shape, dtype=state_dtype, device=dev)
     if workspace is None:
         need = workspace_size(prob)
         if need and variant != "fused":

@@ -31,14 +31,16 @@ def to_device(p: synth.Problem):
 
 def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=None,
             sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False,
-            keep_workspace: bool = False):
+            keep_workspace: bool = False, state_bf16: bool = False):
     """Run kda_prefill through the C ABI on a fresh set of device buffers.
 
     Outputs are pre-filled with NaN so that any element the kernel fails to
     write shows up; the workspace (sized by kda_prefill_workspace_size) is
     filled with 0xFF bytes (NaN as fp32) so nothing depends on its contents.
     Returns numpy dict(out fp32, final, ckpt), and the workspace bytes under
-    "workspace" when keep_workspace is set."""
+    "workspace" when keep_workspace is set.  With state_bf16 the states are
+    bf16 tensors (the initial state must hold bf16 values) and come back as
+    fp32 arrays of their bf16 values."""
     import torch
     import kda_gated_delta_chunked_amd as K
     d = d or to_device(p)
@@ -46,21 +48,23 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
     N, H, T = p.N, p.H, p.T_total
     out = d["v"].clone() if out_alias_v else torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16,
                                                         device=dev)
+    sdt = torch.bfloat16 if state_bf16 else torch.float32
     if state_in_place:
         s0 = d["s0"].clone() if d["s0"] is not None else torch.zeros((N, H, 128, 128), device=dev)
+        s0 = s0.to(sdt)
         fin = s0
     else:
-        s0 = d["s0"]
-        fin = torch.full((N, H, 128, 128), float("nan") if sentinel else 0.0, dtype=torch.float32,
+        s0 = None if d["s0"] is None else d["s0"].to(sdt)
+        fin = torch.full((N, H, 128, 128), float("nan") if sentinel else 0.0, dtype=sdt,
                          device=dev)
     ck = None
     C = 0
     if d["offs"] is not None:
         C = 1 if d["offs"].dim() == 1 else int(d["offs"].shape[1])
         shape = (N, H, 128, 128) if d["offs"].dim() == 1 else (N, C, H, 128, 128)
-        ck = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+        ck = torch.full(shape, float("nan"), dtype=sdt, device=dev)
     prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split,
-                          ckpt_per_seq=C)
+                          ckpt_per_seq=C, state_dtype="bf16" if state_bf16 else "fp32")
     need = K.workspace_size(prob)
     ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev) if need else None
     stream = torch.cuda.current_stream(dev)
@@ -73,8 +77,8 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
                        stream.cuda_stream)
     assert st == 0, f"kda_prefill returned {st}"
     torch.cuda.synchronize()
-    res = {"out": out.float().cpu().numpy(), "final": fin.cpu().numpy(),
-           "ckpt": None if ck is None else ck.cpu().numpy()}
+    res = {"out": out.float().cpu().numpy(), "final": fin.float().cpu().numpy(),
+           "ckpt": None if ck is None else ck.float().cpu().numpy()}
     if keep_workspace:
         res["workspace"] = None if ws is None else ws.cpu().numpy()
     return res

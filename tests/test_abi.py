@@ -314,3 +314,17 @@ def test_decode_rejects_on_the_host():
     assert lib.kda_decode(ctypes.byref(prob), *P, None) == INVALID
     prob = _dprob(b)
     assert lib.kda_decode(ctypes.byref(prob), *b.args(out=b.addr["pool"]), None) == OVERLAP
+
+
+def test_state_dtype_rules():
+    b = Bufs()
+    bad = K.make_problem(2, 256, 4, scale=0.088, variant="fused")
+    bad.state_dtype = 2
+    with pytest.raises(K.KDAError):
+        K.workspace_size(bad)
+    # bf16 states take half the bytes: a final state right after a bf16
+    # initial state does not overlap it, while with fp32 states it would
+    half = b.N * b.H * 128 * 128 * 2
+    for dt, want in (("bf16", OK), ("fp32", OVERLAP)):
+        prob = K.make_problem(b.N, b.T, b.H, scale=0.088, variant="fused", state_dtype=dt)
+        assert ops.validate_raw(prob, *b.args(fin=b.addr["s0"] + half)[:-2], 0, 0) == want
