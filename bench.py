@@ -30,8 +30,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, vendor figure
 # The pages' number for this shape (110-SM SM120, no initial state): 0.881 ms
 PAGES_TOKENS_PER_S = 8 * 8192 / 0.881e-3
 CSRC = os.path.join(ROOT, "kda_gated_delta_chunked_amd", "csrc")
-KERNEL_SOURCES = {"fused": os.path.join(CSRC, "kda_fused.hip"), "decomp": os.path.join(CSRC, "kda_decomp.hip")}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_b8_t8192.json")
+KERNEL_SOURCES = {"fused": os.path.join(CSRC, "kda_fused.hip"), "decomp": os.path.join(CSRC, "kda_decomp.hip"),
+                  "decode": os.path.join(CSRC, "kda_decode.hip")}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 MFMA_FLOPS = 16 * 16 * 32 * 2    # one v_mfma_f32_16x16x32_bf16
 
 
@@ -193,7 +194,8 @@ def bench_decode(args, torch, K, synth) -> int:
            "config": {"workload": f"decode_n{N}_t{T}", "requests": N, "tokens_per_request": T,
                       "H": H, "pool_size": N},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(f"decode_n{N}_t{T}", "decode", "kda_decode_kernel"),
                         "kernel": "kda_decode_kernel", "kernel_ms": round(ms_kernel, 4),
                         "algorithmic_bytes": alg}}
     print(json.dumps(res), flush=True)
