@@ -37,7 +37,7 @@ def _open(path: str):
     f = lib.kda_oracle_prefill_f64
     P = ctypes.c_void_p
     f.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_double, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+                  ctypes.c_double, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
     f.restype = ctypes.c_int
     return lib
 
@@ -66,7 +66,8 @@ def prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, g: np.nd
             cu_seqlens: Optional[np.ndarray] = None,
             initial_state: Optional[np.ndarray] = None,
             ckpt_offsets: Optional[np.ndarray] = None,
-            threads: Optional[int] = None, _library=None) -> dict:
+            threads: Optional[int] = None, qk_l2norm: bool = False, beta_logit: bool = False,
+            _library=None) -> dict:
     """Run the token-by-token fp64 recurrence.
 
     q_bits, k_bits: [T, H, K] uint16 bf16 patterns; v_bits [T, H, V]; g [T, H, K]
@@ -74,6 +75,8 @@ def prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, g: np.nd
     sequences); initial_state [N, H, K, V] fp32 or None; ckpt_offsets [N] int32
     or None.  Returns dict(out [T,H,V], final [N,H,K,V], ckpt [N,H,K,V] or
     None), all fp64.  Checkpoint slots whose offset is outside [0, L] stay NaN.
+    qk_l2norm / beta_logit: the input prologue of kda_oracle.c (q and k divided
+    by their L2 norms per token and head; beta given as a logit).
     """
     lib = _library if _library is not None else _load()
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
@@ -100,23 +103,27 @@ def prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, g: np.nd
     rc = lib.kda_oracle_prefill_f64(N, T, H, K, V, float(scale), _ptr(q_bits), _ptr(k_bits),
                                     _ptr(v_bits), _ptr(g), _ptr(beta), _ptr(cu), _ptr(s0),
                                     _ptr(offs), _ptr(out), _ptr(final), _ptr(ck),
+                                    (1 if qk_l2norm else 0) | (2 if beta_logit else 0),
                                     int(threads if threads is not None else default_threads()))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return {"out": out, "final": final, "ckpt": ck}
 
 
-def prefill_problem(p, *, threads: Optional[int] = None) -> dict:
+def prefill_problem(p, *, threads: Optional[int] = None, qk_l2norm: bool = False,
+                    beta_logit: bool = False) -> dict:
     """Run the oracle on a ``synth.Problem``."""
     return prefill(p.q, p.k, p.v, p.g, p.beta, scale=p.scale, num_seqs=p.N,
                    cu_seqlens=None if p.fixed else p.cu_seqlens,
-                   initial_state=p.initial_state, ckpt_offsets=p.ckpt_offsets, threads=threads)
+                   initial_state=p.initial_state, ckpt_offsets=p.ckpt_offsets, threads=threads,
+                   qk_l2norm=qk_l2norm, beta_logit=beta_logit)
 
 
 def decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, g: np.ndarray,
            beta: np.ndarray, *, scale: float, num_seqs: int, tokens_per_seq: int,
            state_pool: np.ndarray, state_indices: np.ndarray,
-           threads: Optional[int] = None) -> dict:
+           threads: Optional[int] = None, qk_l2norm: bool = False,
+           beta_logit: bool = False) -> dict:
     """State-pool decode: request n advances by tokens_per_seq tokens from
     state_pool[state_indices[n]] and the result replaces that pool entry.
 
@@ -140,7 +147,8 @@ def decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, g: np.nda
     if live:
         rows = np.concatenate([np.arange(n * T, (n + 1) * T) for n in live])
         res = prefill(q_bits[rows], k_bits[rows], v_bits[rows], g[rows], beta[rows], scale=scale,
-                      num_seqs=len(live), initial_state=state_pool[idx[live]], threads=threads)
+                      num_seqs=len(live), initial_state=state_pool[idx[live]], threads=threads,
+                      qk_l2norm=qk_l2norm, beta_logit=beta_logit)
         out[rows] = res["out"]
         pool[idx[live]] = res["final"]
     return {"out": out, "pool": pool}

@@ -53,9 +53,17 @@
  *   final_state   [N, H, K, V]     fp64
  *   ckpt_state    [N, H, K, V]     fp64 (may be NULL iff ckpt_offsets is NULL)
  *
+ * Input prologue (flags).  FlashInfer PR #4262 (Dispatch contract) lists
+ * kernels that L2-normalise q and k per token and head inside the kernel and
+ * take beta as a logit.  With flag 1 each q_t and k_t is divided by its
+ * Euclidean norm over the K channels (a zero vector stays zero); with flag 2
+ * beta_t is replaced by 1 / (1 + exp(-beta_t)).  Both in fp64, before the
+ * step above.
+ *
  * Parity status: pinned by tests against a dense per-step matrix form, the
  * closed-form product expansion, and invariants (no-decay/no-write identity,
- * pure decay, orthonormal overwrite, repeated-key EMA, scalar K = V = 1).
+ * pure decay, orthonormal overwrite, repeated-key EMA, scalar K = V = 1); the
+ * prologue by a hand-worked two-token case and scale invariance.
  */
 #include <math.h>
 #include <pthread.h>
@@ -80,6 +88,7 @@ typedef struct {
   const float *initial_state;
   const int32_t *ckpt_offsets;
   double *out, *final_state, *ckpt_state;
+  int flags;                    /* 1: L2-normalise q and k; 2: beta is a logit */
   long next_pair;               /* work counter, guarded by lock */
   pthread_mutex_t lock;
 } oracle_job;
@@ -114,11 +123,25 @@ static void run_pair(const oracle_job *J, int n, int h, double *S, double *p,
   for (long t = 0; t < len; ++t) {
     const size_t row = (size_t)(bos + t) * H + h;
     const float *gt = J->g + row * K;
-    const double bt = (double)J->beta[row];
+    double bt = (double)J->beta[row];
     for (int d = 0; d < K; ++d) {
       kt[d] = bf16_bits_to_double(J->k[row * K + d]);
       qt[d] = bf16_bits_to_double(J->q[row * K + d]);
     }
+    if (J->flags & 1) {
+      double nk = 0.0, nq = 0.0;
+      for (int d = 0; d < K; ++d) {
+        nk += kt[d] * kt[d];
+        nq += qt[d] * qt[d];
+      }
+      nk = sqrt(nk);
+      nq = sqrt(nq);
+      for (int d = 0; d < K; ++d) {
+        if (nk > 0.0) kt[d] /= nk;
+        if (nq > 0.0) qt[d] /= nq;
+      }
+    }
+    if (J->flags & 2) bt = 1.0 / (1.0 + exp(-bt));
     for (int j = 0; j < V; ++j) vt[j] = bf16_bits_to_double(J->v[row * V + j]);
 
     /* decay: S <- Diag(exp(g_t)) S */
@@ -178,7 +201,7 @@ int kda_oracle_prefill_f64(int N, long T_total, int H, int K, int V, double scal
                            const int32_t *cu_seqlens, const float *initial_state,
                            const int32_t *ckpt_offsets,
                            double *out, double *final_state, double *ckpt_state,
-                           int num_threads) {
+                           int flags, int num_threads) {
   if (N <= 0 || H <= 0 || K <= 0 || V <= 0 || T_total < 0) return -1;
   if (!q || !k || !v || !g || !beta || !out || !final_state) return -1;
   if ((ckpt_offsets == NULL) != (ckpt_state == NULL)) return -1;
@@ -194,6 +217,7 @@ int kda_oracle_prefill_f64(int N, long T_total, int H, int K, int V, double scal
   J.cu_seqlens = cu_seqlens; J.initial_state = initial_state;
   J.ckpt_offsets = ckpt_offsets;
   J.out = out; J.final_state = final_state; J.ckpt_state = ckpt_state;
+  J.flags = flags;
   J.next_pair = 0;
   pthread_mutex_init(&J.lock, NULL);
   if (num_threads <= 1) {
