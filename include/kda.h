@@ -116,7 +116,19 @@ typedef struct {
                                 The recurrence itself always carries fp32; a BF16 state
                                 is widened on load and rounded to nearest even on store
                                 (the BF16 state of FlashInfer PR #4262's benchmark) */
+  int32_t prologue;          /* kda_prologue flags, 0 = none: inputs as given.  Only the
+                                DECOMP schedule has the prologue; FUSED with flags is
+                                KDA_ERR_UNSUPPORTED and AUTO then needs the workspace */
 } kda_problem;
+
+/* Input prologue, done in the kernels before anything else reads q, k or
+ * beta (FlashInfer PR #4262, Dispatch contract, lists kernels with q/k
+ * L2-normalisation inside and beta as a logit). */
+typedef enum {
+  KDA_PROLOGUE_QK_L2NORM = 1,  /* q_t, k_t divided by their Euclidean norms over the 128
+                                  channels, per token and head (a zero vector stays zero) */
+  KDA_PROLOGUE_BETA_LOGIT = 2  /* beta holds logits: beta_t = 1 / (1 + exp(-beta_t)) */
+} kda_prologue;
 
 typedef enum {
   KDA_STATE_F32 = 0,         /* fp32 states (the contract the pages fix) */
@@ -190,6 +202,7 @@ typedef struct {
   float scale;               /* read-out scale, finite */
   float gate_lower_bound;    /* caller's promise g >= bound; must lie in [-5, 0] */
   int64_t pool_size;         /* states in the pool, >= 1 */
+  int32_t prologue;          /* kda_prologue flags, as for kda_prefill */
 } kda_decode_problem;
 
 /* Host-side checks of kda_decode without launching: sizes, NULL rules,

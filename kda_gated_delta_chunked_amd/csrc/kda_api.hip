@@ -59,6 +59,9 @@ kda_status check_problem(const kda_problem* p) {
   if (p->stages != 0 && p->variant != KDA_VARIANT_DECOMP) return KDA_ERR_UNSUPPORTED;
   if (p->ckpt_per_seq < 0) return KDA_ERR_INVALID_ARG;
   if (p->state_dtype != KDA_STATE_F32 && p->state_dtype != KDA_STATE_BF16) return KDA_ERR_UNSUPPORTED;
+  if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
+  // the input prologue is built into the two-launch schedule only
+  if (p->prologue && p->variant == KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;
   if (p->ckpt_per_seq > kMaxCkptPerSeq) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
@@ -98,7 +101,7 @@ size_t decomp_bytes(const kda_problem* p) {
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
   int32_t var = p->variant;
   if (var == KDA_VARIANT_AUTO) {
-    var = ws_bytes >= decomp_bytes(p) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
+    var = ws_bytes >= decomp_bytes(p) || p->prologue ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
     if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
       var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
   }
@@ -241,6 +244,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.N = p->num_seqs;
     a.H = p->num_heads;
     a.T_total = p->total_tokens;
+    a.prologue = p->prologue;
     a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
     a.slots_per_seq = cu_seqlens ? 0 : (a.T_fixed + 63) / 64 + (ckpt_offsets ? a.ckpt_per_seq : 0);
     a.slot_bound = slots;
@@ -285,6 +289,7 @@ kda_status kda_decode_validate(const kda_decode_problem* p, const void* q, const
   if (!std::isfinite(p->gate_lower_bound) || p->gate_lower_bound < -5.0f ||
       p->gate_lower_bound > 0.0f)
     return KDA_ERR_INVALID_ARG;
+  if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
   const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
   if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out))
@@ -326,6 +331,7 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
   a.H = p->num_heads;
   a.pool_size = p->pool_size;
   a.scale = p->scale;
+  a.prologue = p->prologue;
   return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
   __shared__ float sk[DK], sq[DK], sd[DK];  // k, q and exp(g) of the token
   __shared__ float sv[QCOLS];               // v of the token, this workgroup's columns
   __shared__ float red[2][4][QCOLS];        // per-wave partial S^T k and S^T q
-  __shared__ float skq, sbeta;
+  __shared__ float sbeta;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cg = tid & 7, rr = tid >> 3;
@@ -101,22 +101,37 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     } else if (tid < DK + QCOLS) {
       sv[tid - DK] = bf16_to_f32(nk);
     } else if (tid == DK + QCOLS) {
-      sbeta = nx;
+      sbeta = (a.prologue & 2) ? 1.f / (1.f + __expf(-nx)) : nx;  // beta given as a logit
     }
     __syncthreads();
     if (t + 1 < T) fetch(t + 1);
-    if (w == 0) {
-      float x = sk[lane] * sq[lane] + sk[lane + 64] * sq[lane + 64];
+    // k . q, and with the prologue the norms of k and q: every wave sums the
+    // 128 staged values itself (no further barrier)
+    float kq = sk[lane] * sq[lane] + sk[lane + 64] * sq[lane + 64];
+    float kk = 0.f, qq = 0.f;
+    if (a.prologue & 1) {
+      kk = sk[lane] * sk[lane] + sk[lane + 64] * sk[lane + 64];
+      qq = sq[lane] * sq[lane] + sq[lane + 64] * sq[lane + 64];
+    }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-      if (lane == 0) skq = x;
+    for (int o = 32; o >= 1; o >>= 1) {
+      kq += __shfl_xor(kq, o, 64);
+      if (a.prologue & 1) {
+        kk += __shfl_xor(kk, o, 64);
+        qq += __shfl_xor(qq, o, 64);
+      }
+    }
+    float inv_k = 1.f, inv_q = 1.f;
+    if (a.prologue & 1) {
+      inv_k = kk > 0.f ? 1.f / __builtin_sqrtf(kk) : 0.f;
+      inv_q = qq > 0.f ? 1.f / __builtin_sqrtf(qq) : 0.f;
     }
     // decay the rows, then partial S^T k and S^T q over this thread's rows
     float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rr + 32 * i;
-      const float d = sd[r], kr = sk[r], qr = sq[r];
+      const float d = sd[r], kr = sk[r] * inv_k, qr = sq[r] * inv_q;
       S[i].x *= d;
       S[i].y *= d;
       S[i].z *= d;
@@ -147,7 +162,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
     float u[4], o[4];
-    const float beta = sbeta, kq = skq;
+    const float beta = sbeta;
+    kq *= inv_k * inv_q;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 4 * cg + j;
@@ -158,7 +174,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float kr = sk[rr + 32 * i];
+      const float kr = sk[rr + 32 * i] * inv_k;
       S[i].x += kr * u[0];
       S[i].y += kr * u[1];
       S[i].z += kr * u[2];

@@ -358,7 +358,31 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) store8_f32(sF, gl[b], (F_BT + i) * DK + 32 * b + 4 * g4);
   }
-  if (tid < CH) sB[tid] = tid >= off ? beta_ld : 0.f;
+  // input prologue: beta given as a logit; q and k divided by their L2 norms
+  // (the row's 128 channels sit in lanes q, q + 16, q + 32, q + 48)
+  if (tid < CH) sB[tid] = tid >= off ? ((a.prologue & 2) ? 1.f / (1.f + __expf(-beta_ld)) : beta_ld) : 0.f;
+  float inv_k = 1.f, inv_q = 1.f;
+  if (a.prologue & 1) {
+    float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float kf[8], qf[8];
+      unpack8(kA[b], kf);
+      unpack8(qA[b], qf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ssk += kf[e] * kf[e];
+        ssq += qf[e] * qf[e];
+      }
+    }
+    ssk += __shfl_xor(ssk, 16, 64);
+    ssk += __shfl_xor(ssk, 32, 64);
+    ssq += __shfl_xor(ssq, 16, 64);
+    ssq += __shfl_xor(ssq, 32, 64);
+    inv_k = ssk > 0.f ? 1.f / __builtin_sqrtf(ssk) : 0.f;
+    inv_q = ssq > 0.f ? 1.f / __builtin_sqrtf(ssq) : 0.f;
+  }
+  const float qmul = a.scale * inv_q;
   __syncthreads();
 
   // (1) per-channel block factors; Gam and beta go straight to the slot
@@ -422,8 +446,8 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     unpack8(qA[b], qf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kf[e] = rv ? kf[e] : 0.f;
-      qf[e] = rv ? qf[e] * a.scale : 0.f;  // Q~ and M carry the read-out scale
+      kf[e] = rv ? kf[e] * inv_k : 0.f;
+      qf[e] = rv ? qf[e] * qmul : 0.f;  // Q~ and M carry the read-out scale
     }
     load8_f32(sF, bt, (F_BT + i) * DK + ch0);
     float Kf[8], Qf[8], kb[8];

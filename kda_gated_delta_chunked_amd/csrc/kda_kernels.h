@@ -51,6 +51,7 @@ struct DecompArgs {
   float* ckpt;                // [N, ckpt_per_seq, H, 128, 128]
   int ckpt_per_seq;           // C >= 1
   int state_bf16;             // states (s0, final_state, ckpt) are bf16, not fp32
+  int prologue;               // bit 0: L2-normalise q and k; bit 1: beta is a logit
   unsigned char* slots;       // workspace slot area
   int32_t* seg_base;          // workspace header: first slot of each sequence (packed layout)
   int32_t* order;             // workspace header: sequences by decreasing length (packed layout), or NULL
@@ -96,6 +97,7 @@ struct DecodeArgs {
   int H;
   int64_t pool_size;
   float scale;
+  int prologue;               // bit 0: L2-normalise q and k; bit 1: beta is a logit
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

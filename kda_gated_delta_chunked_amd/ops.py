@@ -42,7 +42,8 @@ class Problem(ctypes.Structure):
                 ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("gate_lower_bound", ctypes.c_float), ("variant", ctypes.c_int32),
                 ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32),
-                ("ckpt_per_seq", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
+                ("ckpt_per_seq", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("prologue", ctypes.c_int32)]
 
 
 STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
@@ -55,26 +56,31 @@ class DecodeProblem(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("tokens_per_seq", ctypes.c_int32),
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
                 ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("gate_lower_bound", ctypes.c_float), ("pool_size", ctypes.c_int64)]
+                ("gate_lower_bound", ctypes.c_float), ("pool_size", ctypes.c_int64),
+                ("prologue", ctypes.c_int32)]
 
 
 def make_decode_problem(num_seqs: int, tokens_per_seq: int, num_heads: int, pool_size: int, *,
                         scale: float, gate_lower_bound: float = -5.0,
-                        head_dim_k: int = HEAD_DIM, head_dim_v: int = HEAD_DIM) -> DecodeProblem:
+                        head_dim_k: int = HEAD_DIM, head_dim_v: int = HEAD_DIM,
+                        qk_l2norm: bool = False, beta_logit: bool = False) -> DecodeProblem:
     return DecodeProblem(int(num_seqs), int(tokens_per_seq), int(num_heads), int(head_dim_k),
-                         int(head_dim_v), float(scale), float(gate_lower_bound), int(pool_size))
+                         int(head_dim_v), float(scale), float(gate_lower_bound), int(pool_size),
+                         (1 if qk_l2norm else 0) | (2 if beta_logit else 0))
 
 
 def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: float,
                  gate_lower_bound: float = -5.0, variant: str | int = "auto",
                  value_split: int = 0, head_dim_k: int = HEAD_DIM,
                  head_dim_v: int = HEAD_DIM, stages: str | int = "both",
-                 ckpt_per_seq: int = 0, state_dtype: str = "fp32") -> Problem:
+                 ckpt_per_seq: int = 0, state_dtype: str = "fp32", qk_l2norm: bool = False,
+                 beta_logit: bool = False) -> Problem:
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     st = STAGES[stages] if isinstance(stages, str) else int(stages)
     return Problem(int(num_seqs), int(total_tokens), int(num_heads), int(head_dim_k),
                    int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st,
-                   int(ckpt_per_seq), STATE_DTYPES[state_dtype])
+                   int(ckpt_per_seq), STATE_DTYPES[state_dtype],
+                   (1 if qk_l2norm else 0) | (2 if beta_logit else 0))
 
 
 def periodic_offsets(seq_lens, every: int):
@@ -176,7 +182,8 @@ def _ptr(t) -> int:
 def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Optional[float] = None,
             out=None, final_state=None, output_final_state: bool = True, ckpt_offsets=None,
             ckpt_state=None, gate_lower_bound: float = -5.0, variant: str = "auto",
-            value_split: int = 0, workspace=None, stream=None, state_dtype=None):
+            value_split: int = 0, workspace=None, stream=None, state_dtype=None,
+            qk_l2norm: bool = False, beta_logit: bool = False):
     """KDA multi-token recurrent prefill on the GPU.
 
     q, k, v: bf16 [T, H, 128] (packed, with cu_seqlens int32 [N+1]) or
@@ -260,7 +267,8 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
     prob = make_problem(N, T_total, H, scale=scale, gate_lower_bound=gate_lower_bound,
                         variant=variant, value_split=value_split, head_dim_k=D, head_dim_v=D,
                         ckpt_per_seq=C,
-                        state_dtype="bf16" if state_dtype == torch.bfloat16 else "fp32")
+                        state_dtype="bf16" if state_dtype == torch.bfloat16 else "fp32",
+                        qk_l2norm=qk_l2norm, beta_logit=beta_logit)
     if out is None:
         out = torch.empty_like(v)
     elif out.shape != q.shape:
@@ -301,7 +309,8 @@ def decode_validate_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, st
 
 
 def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float] = None,
-           out=None, gate_lower_bound: float = -5.0, stream=None):
+           out=None, gate_lower_bound: float = -5.0, stream=None, qk_l2norm: bool = False,
+           beta_logit: bool = False):
     """One state-pool decode step on the GPU.
 
     q, k, v: bf16 [N, T, H, 128] (T tokens per request; T = 1 for decode).
@@ -336,7 +345,8 @@ def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float
     if scale is None:
         scale = D ** -0.5
     prob = make_decode_problem(N, T, H, state_pool.shape[0], scale=scale,
-                               gate_lower_bound=gate_lower_bound, head_dim_k=D, head_dim_v=D)
+                               gate_lower_bound=gate_lower_bound, head_dim_k=D, head_dim_v=D,
+                               qk_l2norm=qk_l2norm, beta_logit=beta_logit)
     if out is None:
         out = torch.empty_like(v)
     elif out.shape != q.shape or out.dtype != torch.bfloat16:

@@ -31,7 +31,8 @@ def to_device(p: synth.Problem):
 
 def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=None,
             sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False,
-            keep_workspace: bool = False, state_bf16: bool = False):
+            keep_workspace: bool = False, state_bf16: bool = False, qk_l2norm: bool = False,
+            beta_logit: bool = False):
     """Run kda_prefill through the C ABI on a fresh set of device buffers.
 
     Outputs are pre-filled with NaN so that any element the kernel fails to
@@ -64,7 +65,8 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
         shape = (N, H, 128, 128) if d["offs"].dim() == 1 else (N, C, H, 128, 128)
         ck = torch.full(shape, float("nan"), dtype=sdt, device=dev)
     prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split,
-                          ckpt_per_seq=C, state_dtype="bf16" if state_bf16 else "fp32")
+                          ckpt_per_seq=C, state_dtype="bf16" if state_bf16 else "fp32",
+                          qk_l2norm=qk_l2norm, beta_logit=beta_logit)
     need = K.workspace_size(prob)
     ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev) if need else None
     stream = torch.cuda.current_stream(dev)

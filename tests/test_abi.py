@@ -328,3 +328,25 @@ def test_state_dtype_rules():
     for dt, want in (("bf16", OK), ("fp32", OVERLAP)):
         prob = K.make_problem(b.N, b.T, b.H, scale=0.088, variant="fused", state_dtype=dt)
         assert ops.validate_raw(prob, *b.args(fin=b.addr["s0"] + half)[:-2], 0, 0) == want
+
+
+def test_prologue_rules():
+    b = Bufs()
+    lib = K.load_library()
+    # unknown flag bits
+    bad = K.make_problem(b.N, b.T, b.H, scale=0.088)
+    bad.prologue = 4
+    with pytest.raises(K.KDAError):
+        K.workspace_size(bad)
+    # the one-launch schedule has no prologue; AUTO then takes the two-launch one
+    p = K.make_problem(b.N, b.T, b.H, scale=0.088, variant="fused", qk_l2norm=True)
+    assert ops.validate_raw(p, *b.args()[:-2], 0, 0) == UNSUPPORTED
+    p = K.make_problem(b.N, b.T, b.H, scale=0.088, beta_logit=True)
+    var, _ = K.plan(p)
+    assert var == "decomp"
+    assert ops.validate_raw(p, *b.args()[:-2], 0, 0) == WS
+    d = DecodeBufs()
+    dp = ops.make_decode_problem(d.N, d.T, d.H, d.P, scale=0.088, qk_l2norm=True, beta_logit=True)
+    assert ops.decode_validate_raw(dp, *d.args()) == OK
+    dp.prologue = 8
+    assert ops.decode_validate_raw(dp, *d.args()) == INVALID

@@ -34,7 +34,7 @@ def _case(N, T, H, P, seed, empty=0, g_fill=None, beta_fill=None):
     return p, pool, idx
 
 
-def _run(p, pool, idx, T, out_alias_v=False):
+def _run(p, pool, idx, T, out_alias_v=False, qk_l2norm=False, beta_logit=False):
     import torch
     import kda_gated_delta_chunked_amd as K
     dev = torch.device("cuda", 0)
@@ -50,14 +50,15 @@ def _run(p, pool, idx, T, out_alias_v=False):
     dpool = torch.from_numpy(pool).to(dev)
     didx = torch.from_numpy(idx).to(dev)
     out = v if out_alias_v else torch.full(shp, float("nan"), dtype=torch.bfloat16, device=dev)
-    K.decode(q, k, v, g, beta, dpool, didx, scale=p.scale, out=out)
+    K.decode(q, k, v, g, beta, dpool, didx, scale=p.scale, out=out, qk_l2norm=qk_l2norm,
+             beta_logit=beta_logit)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().reshape(N * T, H, 128), dpool.cpu().numpy()
 
 
-def _check(p, pool, idx, T, gout, gpool, what):
+def _check(p, pool, idx, T, gout, gpool, what, **prologue):
     ref = oracle.decode(p.q, p.k, p.v, p.g, p.beta, scale=p.scale, num_seqs=len(idx),
-                        tokens_per_seq=T, state_pool=pool, state_indices=idx)
+                        tokens_per_seq=T, state_pool=pool, state_indices=idx, **prologue)
     assert np.all(np.isfinite(gout)), what
     err = float(np.max(np.abs(gout - ref["out"]))) if gout.size else 0.0
     assert err <= OUT_MAX_ABS, (what, err)
@@ -115,3 +116,14 @@ def test_decode_equals_prefill_of_the_same_tokens():
     pre = run_gpu(p, variant="decomp")
     assert rel_l2(gout, pre["out"]) <= 2 * OUT_REL_L2
     assert rel_l2(gpool[idx], pre["final"]) <= 1e-3
+
+
+def test_decode_input_prologue():
+    from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32
+    p, pool, idx = _case(9, 3, 4, 12, seed=160, empty=2)
+    rng = np.random.default_rng(161)
+    p.q = bf16_bits_from_f32(rng.normal(0, 2.0, p.q.shape).astype(np.float32))
+    p.k = bf16_bits_from_f32(rng.normal(0, 2.0, p.k.shape).astype(np.float32))
+    p.beta = rng.normal(0, 1.5, p.beta.shape).astype(np.float32)
+    gout, gpool = _run(p, pool, idx, 3, qk_l2norm=True, beta_logit=True)
+    _check(p, pool, idx, 3, gout, gpool, "decode prologue", qk_l2norm=True, beta_logit=True)

@@ -280,6 +280,32 @@ def test_bf16_states(variant):
                 assert np.all(np.isnan(gpu["ckpt"][n, c])), (n, c)
 
 
+def _raw_inputs(p, seed):
+    """q and k as raw (not normalised) N(0, 2^2) vectors, beta as N(0, 1.5^2) logits."""
+    from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32
+    rng = np.random.default_rng(seed)
+    p.q = bf16_bits_from_f32(rng.normal(0, 2.0, p.q.shape).astype(np.float32))
+    p.k = bf16_bits_from_f32(rng.normal(0, 2.0, p.k.shape).astype(np.float32))
+    p.beta = rng.normal(0, 1.5, p.beta.shape).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("flags", [(True, True), (True, False), (False, True)])
+def test_input_prologue(flags):
+    # q and k normalised and beta taken through a sigmoid inside the prepare
+    # launch, against the oracle doing the same in fp64
+    qk, bl = flags
+    lens = [300, 0, 129, 64, 77]
+    p = synth.make_problem(lens, 3, seed=23, init_state=True, ckpt=[5, 0, 129, 64, 70])
+    if qk:
+        p = _raw_inputs(p, 24)
+    else:
+        p.beta = np.random.default_rng(25).normal(0, 1.5, p.beta.shape).astype(np.float32)
+    ref = oracle.prefill_problem(p, qk_l2norm=qk, beta_logit=bl)
+    gpu = run_gpu(p, variant="decomp", qk_l2norm=qk, beta_logit=bl)
+    _report(f"prologue qk={qk} logit={bl}", assert_parity(gpu, ref, "prologue"))
+
+
 def test_packed_recurrence_order_longest_first():
     # the plan launch ranks the packed sequences by slot count, longest first
     # and ties by index; the header holds N + 1 slot offsets, then that order
