@@ -680,15 +680,17 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 // of the state (all 128 rows: 8 accumulator tiles in registers).  The copy
 // waves bring the next segment's slot and V block into the idle one of two
 // LDS buffers with global_load_lds while the compute waves consume the other;
-// a copy wave may stall on a full memory queue, a compute wave never issues a
-// load.  One barrier per segment hands the buffers over.
+// a copy wave may stall on a full memory queue, while inside the segment loop
+// a compute wave reads only LDS.  One barrier per segment hands the buffers
+// over.
 
 template <int CW, int KW>
 __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(DecompArgs a) {
   constexpr int WAVES = CW;
-  // with at most one wave per SIMD a compute wave has 512 registers and reads
-  // its fragments in large batches; with more waves it reads them as it goes
-  // and the other compute wave on the SIMD covers the latency
+  // with at most two waves per SIMD (one compute, one copy) a compute wave has
+  // up to 256 registers and reads its fragments in large batches; with more
+  // waves it reads them as it goes and the other compute wave on the SIMD
+  // covers the latency
   constexpr bool BATCHED = CW + KW <= 8;
   constexpr int VW = 16 * CW;                     // columns per workgroup
   constexpr int VUNITS = CH * VW * 2 / 1024;      // 1 KiB units of the V block
