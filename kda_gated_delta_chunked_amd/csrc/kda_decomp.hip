@@ -695,10 +695,20 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   constexpr int VW = 16 * CW;                     // columns per workgroup
   constexpr int VUNITS = CH * VW * 2 / 1024;      // 1 KiB units of the V block
   constexpr int UNITS = SLOT_UNITS + VUNITS;
-  // two buffers as separate arrays, so the compiler sees that reads of one do
-  // not wait for copies into the other
-  __shared__ __attribute__((aligned(16))) uint4 opsA[UNITS * 64];
-  __shared__ __attribute__((aligned(16))) uint4 opsB[UNITS * 64];
+  // K~ (the first KTU units of a slot, read first in a segment) has three
+  // buffers when LDS holds them, so its copy can run two segments ahead; the
+  // rest of the slot and the V block have two
+  constexpr int KTU = 16;
+  constexpr bool KT3 = 2 * (UNITS - KTU) + 3 * KTU <= 158;
+  constexpr int KB = KT3 ? KTU * 1024 : 0;        // bytes of the slot not in the `ops` buffers
+  constexpr int OPS_UNITS = UNITS - KB / 1024;
+  // buffers as separate arrays, so the compiler sees that reads of one do not
+  // wait for copies into another
+  __shared__ __attribute__((aligned(16))) uint4 opsA[OPS_UNITS * 64];
+  __shared__ __attribute__((aligned(16))) uint4 opsB[OPS_UNITS * 64];
+  __shared__ __attribute__((aligned(16))) uint4 ktA[KT3 ? KTU * 64 : 1];
+  __shared__ __attribute__((aligned(16))) uint4 ktB[KT3 ? KTU * 64 : 1];
+  __shared__ __attribute__((aligned(16))) uint4 ktC[KT3 ? KTU * 64 : 1];
   constexpr int PARTS = 8 / WAVES;
   const int H = a.H;
   // workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8): keep
@@ -727,20 +737,66 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     // geometry (off, tok0) of the segment copied next, worked out one copy
     // ahead: its scalar reads of the checkpoint offsets then wait while the
     // previous copy is in flight, not before the V rows are requested
+    // the slot from unit KB / 1024 on, and the V block, into an `ops` buffer
     auto copy = [&](int jseg, uint4* dst, int off, int64_t tok0) {
       const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
-      for (int u = cw; u < SLOT_UNITS; u += KW)
-        __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
+      for (int u = KB / 1024 + cw; u < SLOT_UNITS; u += KW)
+        __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + (u - KB / 1024) * 64, 16, 0, 0);
       // V rows 0..63 (rows before the segment read row `off`; their beta is 0)
       constexpr int LPR = VW / 8, RPI = 64 / LPR;  // lanes per row, rows per unit
       for (int k = cw; k < VUNITS; k += KW) {
         const int row = max(k * RPI + lane / LPR, off);
         const uint16_t* vsrc = a.v + ((size_t)(tok0 + row) * H + h) * DK + VW * part + 8 * (lane % LPR);
-        __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS + k) * 64, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS - KB / 1024 + k) * 64, 16, 0, 0);
       }
     };
     int goff = 0;
     int64_t gtok = 0;
+    if (KT3) {
+      // K~ of segment j + 2 is requested after the rest of segment j + 1, and
+      // the wait before each barrier leaves only those newest KT_PER copies in
+      // flight (loads of one kind complete in order)
+      constexpr int KT_PER = KTU / KW;
+      auto copy_kt = [&](int jseg) {
+        uint4* dst = jseg % 3 == 0 ? ktA : (jseg % 3 == 1 ? ktB : ktC);
+        const unsigned char* src = a.slots + ((size_t)(base + jseg) * H + h) * kDecompSlotBytes;
+        for (int u = cw; u < KTU; u += KW)
+          __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
+      };
+      bool kt_last = false;
+      if (nseg > 0) {
+        geometry(0, goff, gtok);
+        copy_kt(0);
+        copy(0, opsA, goff, gtok);
+      }
+      if (nseg > 1) {
+        copy_kt(1);
+        kt_last = true;
+        geometry(1, goff, gtok);
+      }
+      for (int jseg = 0; jseg < nseg; ++jseg) {
+        if (kt_last)
+          __builtin_amdgcn_s_waitcnt((KT_PER & 15) | ((KT_PER >> 4) << 14) | 0x0F70);
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        // a workgroup barrier without the workgroup-scope fence (whose wait
+        // for all memory operations would also take in the K~ copies kept in
+        // flight); the wavefront-scope fences keep the copies on their side
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        kt_last = false;
+        if (jseg + 1 < nseg) {
+          copy(jseg + 1, (jseg & 1) ? opsA : opsB, goff, gtok);
+          if (jseg + 2 < nseg) geometry(jseg + 2, goff, gtok);
+        }
+        if (jseg + 2 < nseg) {
+          copy_kt(jseg + 2);
+          kt_last = true;
+        }
+      }
+      return;
+    }
     if (nseg > 0) {
       geometry(0, goff, gtok);
       copy(0, opsA, goff, gtok);
@@ -828,6 +884,8 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   };
 
   auto step = [&](int jseg, const uint4* cur) {
+    // K~ of this segment: its own buffer, or the start of `cur`
+    const uint4* kcur = !KT3 ? cur : (jseg % 3 == 0 ? ktA : (jseg % 3 == 1 ? ktB : ktC));
     __syncthreads();  // the copy waves have filled `cur`
     if (pend) store_out();
     // An opaque copy of the lane index, renewed every segment: LDS addresses
@@ -836,20 +894,24 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     int lq = lane;
     asm volatile("" : "+v"(lq));
     const int qq = lq & 15, gg = lq >> 4;
-    auto frag = [&](int byte_off) { return __builtin_bit_cast(bf16x8, cur[(byte_off >> 4) + lq]); };
+    // slot byte offsets: K~ from `kcur`, the rest from `cur` (shifted by KB)
+    auto frag = [&](int byte_off) {
+      return __builtin_bit_cast(bf16x8, byte_off < SL_QT ? kcur[(byte_off >> 4) + lq]
+                                                         : cur[((byte_off - KB) >> 4) + lq]);
+    };
     auto f4 = [&](int byte_off) {
-      return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off);
+      return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off - KB);
     };
     // M or N fragment f (half fragments: upper 8 bytes are zero)
     auto trifrag = [&](int region, int f) {
-      const char* base = reinterpret_cast<const char*>(cur) + region + tri_off(f);
+      const char* base = reinterpret_cast<const char*>(cur) + region - KB + tri_off(f);
       if (tri_half(f)) {
         const uint2 lo = *reinterpret_cast<const uint2*>(base + lq * 8);
         return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, 0u, 0u));
       }
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(base + lq * 16));
     };
-    const uint16_t* vblk = reinterpret_cast<const uint16_t*>(cur + SLOT_UNITS * 64);
+    const uint16_t* vblk = reinterpret_cast<const uint16_t*>(cur + (SLOT_UNITS - KB / 1024) * 64);
 
     // The segment runs as load batches and matrix batches separated by
     // scheduling fences: fragment reads go out together and are consumed while
@@ -891,8 +953,8 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4 + b], Sb[b], X[t]);
     KDA_FENCE();
     // the rest of Q~, the V block and N, read while O^T = S^T Q~^T runs
-    const int4 hd = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(cur) + SL_HDR);
-    const uint2 hmask = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_HDR + 16);
+    const int4 hd = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(cur) + SL_HDR - KB);
+    const uint2 hmask = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_HDR - KB + 16);
     const int off = __builtin_amdgcn_readfirstlane(hd.x);
     const int64_t tok0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(hd.w) << 32) |
                                    (uint32_t)__builtin_amdgcn_readfirstlane(hd.z));
@@ -956,7 +1018,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     uint2 kl[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      kl[m] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_KL + m * 512 + lq * 8);
+      kl[m] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_KL - KB + m * 512 + lq * 8);
     float4 gm[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
