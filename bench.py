@@ -306,7 +306,16 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms_launch, ms_step = timed(step, args.steps)
+    # the timed region: exactly `steps` calls, bracketed by synchronisations,
+    # with nothing else enqueued between them
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-call time from events on the call's stream, in a separate pass
+    ms_launch = timed(step, args.steps)[0]
     tokens = p.T_total
     value = tokens / (ms_step * 1e-3)
 
