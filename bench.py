@@ -107,6 +107,17 @@ def measured_traffic(workload: str, variant: str, kernel: str):
     return e.get("hbm_bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(p, sample_tokens: int):
     """Time the fp64 oracle (as it stands) on the first `sample_tokens` tokens
     of every sequence of the workload, all heads, on all host cores."""
@@ -136,7 +147,7 @@ def cpu_baseline(p, sample_tokens: int):
             "sample": f"first {sample_tokens} tokens of each of the {p.N} sequences, all {p.H} "
                       f"heads ({int(cu[-1]) * p.H} token-heads), fp64 token recurrence, "
                       f"{dt:.2f} s wall",
-            "one_core_token_heads_per_s": round(L0 / dt1, 1)}
+            "one_core_token_heads_per_s": round(L0 / dt1, 1), "cpu_model": _cpu_model()}
 
 
 def bench_decode(args, torch, K, synth) -> int:

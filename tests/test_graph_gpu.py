@@ -28,14 +28,28 @@ def _problems():
     return a, b
 
 
-@pytest.mark.parametrize("variant", ["decomp", "fused"])
-def test_graph_capture_and_replay_with_new_inputs(variant):
+def _full_size_problems():
+    # the checkpoint workload at full size (16 sequences of 512..8192 tokens,
+    # H = 12, one offset each), and a second input with the same N and T_total
+    # but moved lengths and offsets
+    a = synth.workload("ckpt_16_rand")
+    lens_b = np.array(a.seq_lens, np.int64)
+    lens_b[0] += 257
+    lens_b[1] -= 257
+    b = synth.make_problem(list(lens_b), a.H, seed=a.seed + 1, init_state=True, ckpt="inside",
+                           name="ckpt_16_moved")
+    assert a.T_total == b.T_total and a.N == b.N
+    return a, b
+
+
+@pytest.mark.parametrize("variant,size", [("decomp", "small"), ("fused", "small"), ("decomp", "full")])
+def test_graph_capture_and_replay_with_new_inputs(variant, size):
     import torch
     import kda_gated_delta_chunked_amd as K
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     dev = torch.device("cuda", 0)
-    pa, pb = _problems()
+    pa, pb = _problems() if size == "small" else _full_size_problems()
     N, H, T = pa.N, pa.H, pa.T_total
 
     def dev_bf16(bits):
