@@ -170,6 +170,10 @@ def workload(name: str, *, H: int = 12) -> Problem:
     packed_32_rand 32 sequences, lengths uniform in [1, 4096]
     ckpt_16_rand   16 sequences, lengths uniform in [512, 8192], one
                    checkpoint offset per sequence inside it
+    packed_512x32, packed_128x8, mixed_6
+                   the packed shapes of FlashInfer PR #4262's B200 table
+                   (32 x 512, 8 x 128, and six lengths 1300, 547, 2048,
+                   963, 271, 3063), per-sequence initial states
     """
     table = {
         "b1_t64_h1": dict(lens=[64], H=1, fixed=True, init=False, seed=1000),
@@ -184,6 +188,10 @@ def workload(name: str, *, H: int = 12) -> Problem:
                                init=True, seed=1003),
         "ckpt_16_rand": dict(lens=uniform_lengths(2004, 16, 512, 8192), H=H, fixed=False,
                              init=True, seed=1004, ckpt="inside"),
+        "packed_512x32": dict(lens=[512] * 32, H=H, fixed=False, init=True, seed=1005),
+        "packed_128x8": dict(lens=[128] * 8, H=H, fixed=False, init=True, seed=1005),
+        "mixed_6": dict(lens=[1300, 547, 2048, 963, 271, 3063], H=H, fixed=False, init=True,
+                        seed=1005),
     }
     if name not in table:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(table)}")

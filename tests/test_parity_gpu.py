@@ -153,7 +153,8 @@ def test_deterministic(variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("name", ["b1_t8192", "b8_t8192", "packed_32_rand", "ckpt_16_rand"])
+@pytest.mark.parametrize("name", ["b1_t8192", "b8_t8192", "packed_32_rand", "ckpt_16_rand",
+                                  "packed_512x32", "packed_128x8", "mixed_6"])
 def test_full_size_workloads(name, variant):
     p, ref = _workload_ref(name)
     gpu = run_gpu(p, variant=variant)

@@ -37,5 +37,10 @@ def test_named_workloads_shapes():
     for name, (N, T) in {"b1_t64_h1": (1, 64)}.items():
         p = synth.workload(name)
         assert p.N == N and p.T_total == T and p.H == 1
+    for name, lens in {"packed_512x32": [512] * 32, "packed_128x8": [128] * 8,
+                       "mixed_6": [1300, 547, 2048, 963, 271, 3063]}.items():
+        p = synth.workload(name)
+        assert list(p.seq_lens) == lens and not p.fixed and p.H == 12
+        assert p.initial_state is not None and p.T_total == sum(lens)
     lens = synth.uniform_lengths(2003, 32, 1, 4096)
     assert len(lens) == 32 and min(lens) >= 1 and max(lens) <= 4096
