@@ -718,7 +718,10 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   if (pair >= a.N * H) return;
   const int rank = pair / H, h = pair - rank * H;
   const int n = a.order ? a.order[rank] : rank;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
+  // the wave index as a scalar: the role branch below is then uniform, so the
+  // compiler keeps the two roles' code paths (and their memory counters) apart
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, q = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const SeqInfo si = seq_info(a, n);
   const int64_t base = a.cu_seqlens ? (int64_t)a.seg_base[n] : (int64_t)n * a.slots_per_seq;
@@ -750,6 +753,9 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
         __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS - KB / 1024 + k) * 64, 16, 0, 0);
       }
     };
+    // the checkpoint offsets (read at kernel start) have landed: the
+    // geometry walks below then add no wait to the copies in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     int goff = 0;
     int64_t gtok = 0;
     if (KT3) {
@@ -886,7 +892,11 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   auto step = [&](int jseg, const uint4* cur) {
     // K~ of this segment: its own buffer, or the start of `cur`
     const uint4* kcur = !KT3 ? cur : (jseg % 3 == 0 ? ktA : (jseg % 3 == 1 ? ktB : ktC));
-    __syncthreads();  // the copy waves have filled `cur`
+    // the copy waves have filled `cur`: a barrier on LDS only, whose release
+    // side waits for this wave's LDS reads but not for its global stores
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     if (pend) store_out();
     // An opaque copy of the lane index, renewed every segment: LDS addresses
     // become one register plus an immediate offset instead of dozens of
