@@ -80,8 +80,11 @@ typedef enum {
 } kda_status;
 
 typedef enum {
-  KDA_VARIANT_AUTO = 0,          /* pick the schedule from the problem shape and the CU count;
-                                    the two-launch schedule only when the workspace holds it */
+  KDA_VARIANT_AUTO = 0,          /* pick the schedule from a table keyed on the CU count and
+                                    the shape the host knows (N, H, T_total / N): the one-launch
+                                    schedule for short sequences (a mean of at most 128 tokens)
+                                    whose workgroups all fit on the device at once, else the
+                                    two-launch schedule when the workspace holds it */
   KDA_VARIANT_DECOMP = 1,        /* two launches through the workspace: a chunk-parallel
                                     prepare, then the recurrence (FlashInfer PR #4633,
                                     Description: the "decomp" variant) */

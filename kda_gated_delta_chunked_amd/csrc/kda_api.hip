@@ -98,19 +98,42 @@ size_t decomp_bytes(const kda_problem* p) {
 // runs per CU; two workgroups per pair.  AUTO takes DECOMP
 // whenever the workspace holds it (value_split 1 and 8 are DECOMP-only, 2 and 4
 // exist in both).
+// workgroups per pair of the one-launch schedule
+int fused_vsplit(const kda_problem* p, int cus) {
+  if (p->value_split) return p->value_split;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
+  return (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
+}
+
+// The schedule table, keyed on the CU count and on what the host knows of the
+// shape (N, H and the mean sequence length T_total / N).  The one-launch
+// schedule wins when all its workgroups run at once (pairs x workgroups per
+// pair <= CUs) and the sequences are short (a mean of at most two 64-token
+// chunks): the per-segment chain is then too short to repay the prepare
+// launch and its workspace round trip.  Measured on MI355X (256 CUs), H = 12,
+// in us per call, DECOMP / FUSED: B1 T64 26.4 / 18.9, B8 T64 28.6 / 21.7,
+// B8 T128 32.9 / 31.4, packed 8 x 128 30.8 / 25.5; past either bound DECOMP
+// wins: B8 T192 39.2 / 40.7, B16 T128 45.3 / 53.7, B32 T64 49.9 / 52.6.
+bool fused_is_faster(const kda_problem* p, int cus) {
+  if (cus <= 0 || p->prologue || p->value_split == 1 || p->value_split == 8) return false;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
+  const int64_t mean_len = p->total_tokens / p->num_seqs;
+  return mean_len <= 2 * 64 && pairs * fused_vsplit(p, cus) <= cus;
+}
+
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
   int32_t var = p->variant;
   if (var == KDA_VARIANT_AUTO) {
     var = ws_bytes >= decomp_bytes(p) || p->prologue ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
     if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
       var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
+    if (var == KDA_VARIANT_DECOMP && fused_is_faster(p, cus)) var = KDA_VARIANT_FUSED;
   }
   *variant = var;
-  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
-  if (p->value_split) {
+  if (var == KDA_VARIANT_FUSED) {
+    *vsplit = fused_vsplit(p, cus);
+  } else if (p->value_split) {
     *vsplit = p->value_split;
-  } else if (var == KDA_VARIANT_FUSED) {
-    *vsplit = (cus > 0 && pairs * 2 < cus / 2) ? 4 : 2;
   } else {
     // measured on MI355X (256 CUs): two workgroups per pair is best from 12 to
     // 384 pairs (B1 and B8 at T = 8192, B32 at T = 512); more splits add slot

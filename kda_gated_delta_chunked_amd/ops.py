@@ -275,14 +275,16 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         raise ValueError("out must have q's shape")
     if final_state is None and output_final_state:
         final_state = torch.empty(state_shape, dtype=state_dtype, device=dev)
-    if workspace is None:
-        need = workspace_size(prob)
-        if need and variant != "fused":
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
+        if workspace is None:
+            # a workspace only for the two-launch schedule (AUTO: when the
+            # library's table picks it on this device)
+            need = workspace_size(prob)
+            if need and variant != "fused" and (variant != "auto" or plan(prob)[0] == "decomp"):
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         st = prefill_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                          _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(ckpt_offsets),
                          _ptr(ckpt_state), _ptr(workspace), ws_bytes, int(stream.cuda_stream))
