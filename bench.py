@@ -88,9 +88,17 @@ def executed_mfma_flops(p, variant: str, vsplit: int) -> float:
     return float((152 + 8 * 90) * MFMA_FLOPS) * segs * p.H
 
 
+# headers every kernel source includes: a change there changes the kernel too
+KERNEL_HEADERS = [os.path.join(CSRC, "kda_kernels.h"), os.path.join(CSRC, "kda_ckpt.h")]
+
+
 def kernel_sha(variant: str) -> str:
-    with open(KERNEL_SOURCES[variant], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the kernel source followed by the shared headers."""
+    h = hashlib.sha256()
+    for path in [KERNEL_SOURCES[variant]] + KERNEL_HEADERS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str, variant: str, kernel: str):
