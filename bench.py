@@ -64,15 +64,22 @@ def algorithmic_flops(p) -> float:
 
 
 def segments(p) -> int:
+    """Segments the kernels process: the 64-token chunks of every sequence,
+    plus one for each distinct honoured checkpoint offset strictly inside a
+    chunk (offsets are taken in order; one is honoured when it lies in
+    [0, L] and is not below the previous honoured one)."""
     segs = 0
+    offs = None if p.ckpt_offsets is None else np.asarray(p.ckpt_offsets).reshape(p.N, -1)
     for n in range(p.N):
         L = int(p.cu_seqlens[n + 1] - p.cu_seqlens[n])
-        s = (L + 63) // 64
-        if p.ckpt_offsets is not None:
-            off = int(p.ckpt_offsets[n])
-            if 0 < off < L and off % 64 != 0:
-                s += 1
-        segs += s
+        cuts, last = set(), 0
+        for x in ([] if offs is None else [int(v) for v in offs[n]]):
+            if x < last or x > L:
+                continue
+            last = x
+            if 0 < x < L and x % 64 != 0:
+                cuts.add(x)
+        segs += (L + 63) // 64 + len(cuts)
     return segs
 
 
