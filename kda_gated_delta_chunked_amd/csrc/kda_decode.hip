@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     } else if (tid == DK + QCOLS) {
       sbeta = (a.prologue & 2) ? 1.f / (1.f + __expf(-nx)) : nx;  // beta given as a logit
     }
-    __syncthreads();
+    lds_barrier();
     if (t + 1 < T) fetch(t + 1);
     // k . q, and with the prologue the norms of k and q: every wave sums the
     // 128 staged values itself (no further barrier)
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
         red[1][w][4 * cg + j] = pq[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
     float u[4], o[4];
     const float beta = sbeta;
     kq *= inv_k * inv_q;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     }
     if (rr == 0)
       *reinterpret_cast<uint2*>(a.out + vbase + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    __syncthreads();  // the staged vectors and partial sums are rewritten next token
+    lds_barrier();  // the staged vectors and partial sums are rewritten next token
   }
 
 #pragma unroll

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     inv_q = ssq > 0.f ? 1.f / __builtin_sqrtf(ssq) : 0.f;
   }
   const float qmul = a.scale * inv_q;
-  __syncthreads();
+  lds_barrier();
 
   // (1) per-channel block factors; Gam and beta go straight to the slot
   if (tid < DK) {
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
         make_int4(off, 0, (int)(uint32_t)(uint64_t)tok0, (int)(uint32_t)((uint64_t)tok0 >> 32));
     *reinterpret_cast<unsigned long long*>(slot + SL_HDR + 16) = mask;
   }
-  __syncthreads();
+  lds_barrier();
 
   // (2) wave i: operands of row block i and the diagonal block (i, i).
   // Identity slices that transpose a K^ tile with one exact matrix product:
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     for (int jj = 0; jj < 4; ++jj)
       if (jj == i) macc[jj] = m0;
   }
-  __syncthreads();
+  lds_barrier();
 
   // (3) off-diagonal blocks (i, jb < i): right operand k exp(bt_jb - Gl_s) W_{i,jb}
   // from LDS, W = prod_{jb<m<i} exp(bt_m)
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     else
       *reinterpret_cast<uint4*>(slot + SL_M + tri_off(f) + lane * 16) = mv;
   }
-  __syncthreads();
+  lds_barrier();
 
   // (4) T_bb = (I + L_bb)^-1 by forward substitution, lane = (block, column)
   float* sT = sE;
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sT[(16 * bb + rr) * P_LP + 16 * bb + col] = x[rr];
   }
-  __syncthreads();
+  lds_barrier();
 
   // (5) off-diagonal blocks of T in two levels.  First the 32 x 32 halves:
   // T_10 = -T_11 L_10 T_00 and T_32 = -T_33 L_32 T_22.  Then the lower-left
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const float4 o = tz_prod(ib, ib, ib);
     *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o.x, -o.y, -o.z, -o.w);
   }
-  __syncthreads();
+  lds_barrier();
   {
     const int ib = 2 + (w >> 1), jb = w & 1;
     for (int pb = 2; pb <= ib; ++pb)
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const float4 o = tz_prod(ib, 2, ib);
     *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o.x, -o.y, -o.z, -o.w);
   }
-  __syncthreads();
+  lds_barrier();
 
   // (6) N = T - I fragments of token tile w (A operand of N Y)
 #pragma unroll
@@ -892,11 +892,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   auto step = [&](int jseg, const uint4* cur) {
     // K~ of this segment: its own buffer, or the start of `cur`
     const uint4* kcur = !KT3 ? cur : (jseg % 3 == 0 ? ktA : (jseg % 3 == 1 ? ktB : ktC));
-    // the copy waves have filled `cur`: a barrier on LDS only, whose release
-    // side waits for this wave's LDS reads but not for its global stores
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    lds_barrier();  // the copy waves have filled `cur`
     if (pend) store_out();
     // An opaque copy of the lane index, renewed every segment: LDS addresses
     // become one register plus an immediate offset instead of dozens of

@@ -364,9 +364,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     load_segment(pos, ld);
     gate_factors_1(ld);
     stage_v_beta(ld);
-    __syncthreads();
+    lds_barrier();
     gate_factors_2();
-    __syncthreads();
+    lds_barrier();
   }
   while (pos < len) {
     const int64_t seg_end = seg_end_of(pos);
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
             pack2(kb[e][0] * W1[0], kb[e][1] * W1[1]);
       }
     }
-    __syncthreads();  // (3) gate operands ready
+    lds_barrier();  // (3) gate operands ready
     if (pending_off >= 0) flush_out(pending_off, pending_tok0);
 
     // ================= phase B: gated K K^T and Q K^T blocks ==================
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         for (int r = s2 + 1; r < 16; ++r) tcol[r] = fmaf(-lcol[r], tcol[s2], tcol[r]);
       }
     }
-    __syncthreads();  // (4) gate operands consumed; region reused below
+    lds_barrier();  // (4) gate operands consumed; region reused below
 
     // L off-diagonal blocks (bf16, for the matrix-core merges) and M (bf16,
     // lower incl. diagonal)
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     }
     // prefetch the next segment's inputs; they land during phases C and D
     if (has_next) load_segment(seg_end, ld);
-    __syncthreads();  // (5) L, M, T_ii and prepared operands ready
+    lds_barrier();  // (5) L, M, T_ii and prepared operands ready
 
     // ================= phase C: merges of N = (I + L)^-1 - I ==================
     // With Ta = T[0:32,0:32], Tb = T[32:64,32:64]:
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (w < 2) {
       // column block ni = w of T[32:64, 0:32]: Q = L[32:64,0:32] Ta[:, ni] (two
       // 16-row tiles), then -Tb Q
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
         for (int e = 0; e < 4; ++e) pN[(32 + 16 * mi + 4 * lg + e) * RP + 16 * ni + lr] = f2bf(-Tn[e]);
       }
     }
-    __syncthreads();  // (C) solve done; solve scratch free
+    lds_barrier();  // (C) solve done; solve scratch free
 
     // ================= phase D: the chunk recurrence ==========================
     // dST holds the incoming state in bf16.  X = V - K exp(G) S, Y = beta X and
@@ -708,7 +708,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     }
     // next segment's gate factors, first half (its inputs were prefetched)
     if (has_next) gate_factors_1(ld);
-    __syncthreads();  // (D1) Y and the next segment's half-block products ready
+    lds_barrier();  // (D1) Y and the next segment's half-block products ready
 
     // U = Y + N Y
     const int nks = rb >= 2 ? 2 : 1;   // k-steps of 32 rows covering rows < 16(rb+1)
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
       gate_factors_2();
       stage_v_beta(ld);
     }
-    __syncthreads();  // (D2) U ready; nobody reads dST, mV, mBeta again in this segment
+    lds_barrier();  // (D2) U ready; nobody reads dST, mV, mBeta again in this segment
 
     // O = scale (P + M U)   (rows of block rb), staged for 16-byte stores
     if (rb_active) {
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
             make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
       }
     }
-    __syncthreads();  // (E) segment done: the gate-operand region is free again
+    lds_barrier();  // (E) segment done: the gate-operand region is free again
 
     pending_off = off;
     pending_tok0 = tok0;

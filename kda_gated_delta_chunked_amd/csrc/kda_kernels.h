@@ -6,6 +6,17 @@
 
 namespace kda {
 
+// A workgroup barrier that orders LDS accesses only.  Its release side waits
+// for the wave's own outstanding LDS operations, not for its global loads and
+// stores, as a barrier on all memory (__syncthreads) does: that one waits for
+// every store of the wave to be acknowledged.  For kernels whose waves share
+// data through LDS only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Arguments of the one-launch schedule.  Pointers are device memory; q/k/v/out
 // are bf16 bit patterns.  Layouts are those of include/kda.h.
 struct FusedArgs {
