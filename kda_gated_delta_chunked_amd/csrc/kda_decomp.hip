@@ -34,6 +34,13 @@
 // this order, the accumulators of row tiles 2b and 2b+1 of a matrix Z, taken
 // side by side, are exactly the B operand of Z for block b (and the A operand
 // of Z^T), so state and U feed the next product without any data movement.
+// Token contractions (U, M, N, the token axis of K^^T) use kidx as it is.  The
+// state is held with its rows permuted: row R of the accumulators holds key
+// channel state_row_channel(R), chosen so that in the key-channel operands
+// (K~, Q~) element e of lane l in block b is channel 32 b + 8 g + e -- eight
+// consecutive channels, which the prepare reads with one 16-byte load of q
+// and k per lane (8-byte pieces, two per lane, were about a fifth slower to
+// fetch).
 //
 // Exponent range (prepare): rows form 16-row blocks i with local cumulative
 // sums Gl_r = G_r - G_{16i-1} <= 0 and block sums bt_i.  With g >= -5 (the gate
@@ -123,6 +130,12 @@ __device__ __forceinline__ bf16x8 acc_pair(const f32x4& a, const f32x4& b) {
 __device__ __forceinline__ void acc_pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   split8(x, hi, lo);
+}
+// key channel of accumulator row R of the state: R = 32 b + 16 h + 4 g + e
+// holds channel 32 b + 8 g + 4 h + e, so that kidx(b, g, e) maps to channel
+// 32 b + 8 g + e
+__host__ __device__ constexpr int state_row_channel(int R) {
+  return (R & ~31) + 8 * ((R >> 2) & 3) + 4 * ((R >> 4) & 1) + (R & 3);
 }
 // M / N fragment index of (token tile t, token block b <= t / 2)
 __host__ __device__ constexpr int tri_frag(int t, int b) { return t < 2 ? t : 2 * t - 2 + b; }
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
 // Launch 1: prepare.  One workgroup of 4 waves per (slot, head).  Wave i owns
 // the 16-row block i of the tile and works in the lane order of the matrix
 // fragments throughout: lane l = 16 g + q holds row 16 i + q and, for key
-// block b, the 8 channels kidx(b, g, 0..7).
+// block b, the 8 channels 32 b + 8 g + (0..7).
 
 constexpr int P_LP = CH + 4;    // fp32 pitch of L and T
 // per-channel factor rows
@@ -258,16 +271,16 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// the 8 channels of key block b of this lane: two runs of 4 at p + off, p + off + 16
+// the 8 channels of key block b of this lane: 8 consecutive at p + off
 __device__ __forceinline__ void load8_f32(const float* p, float (&x)[8], int off) {
   const float4 a = *reinterpret_cast<const float4*>(p + off);
-  const float4 b = *reinterpret_cast<const float4*>(p + off + 16);
+  const float4 b = *reinterpret_cast<const float4*>(p + off + 4);
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 __device__ __forceinline__ void store8_f32(float* p, const float (&x)[8], int off) {
   *reinterpret_cast<float4*>(p + off) = make_float4(x[0], x[1], x[2], x[3]);
-  *reinterpret_cast<float4*>(p + off + 16) = make_float4(x[4], x[5], x[6], x[7]);
+  *reinterpret_cast<float4*>(p + off + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 __device__ __forceinline__ void unpack8(const uint2 (&u)[2], float (&x)[8]) {
   x[0] = lo_of(u[0].x); x[1] = hi_of(u[0].x); x[2] = lo_of(u[0].y); x[3] = hi_of(u[0].y);
@@ -326,14 +339,17 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   uint2 kA[4][2], qA[4][2];
   float4 gA[4][2];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int ch = 32 * b + 16 * hh + 4 * g4;
-      kA[b][hh] = *reinterpret_cast<const uint2*>(a.k + erow + ch);
-      qA[b][hh] = *reinterpret_cast<const uint2*>(a.q + erow + ch);
-      gA[b][hh] = *reinterpret_cast<const float4*>(a.g + erow + ch);
-    }
+  for (int b = 0; b < 4; ++b) {
+    const int ch = 32 * b + 8 * g4;
+    const uint4 kv = *reinterpret_cast<const uint4*>(a.k + erow + ch);
+    const uint4 qv = *reinterpret_cast<const uint4*>(a.q + erow + ch);
+    kA[b][0] = make_uint2(kv.x, kv.y);
+    kA[b][1] = make_uint2(kv.z, kv.w);
+    qA[b][0] = make_uint2(qv.x, qv.y);
+    qA[b][1] = make_uint2(qv.z, qv.w);
+    gA[b][0] = *reinterpret_cast<const float4*>(a.g + erow + ch);
+    gA[b][1] = *reinterpret_cast<const float4*>(a.g + erow + ch + 4);
+  }
   const float beta_ld = a.beta[(size_t)(tok0 + max(tid & (CH - 1), off)) * H + h];
 
   // Gl: cumulative sum of g over the rows of the block, for this lane's 32
@@ -356,7 +372,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   // block sums (row 15 of the block) and beta to LDS
   if (q == 15) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) store8_f32(sF, gl[b], (F_BT + i) * DK + 32 * b + 4 * g4);
+    for (int b = 0; b < 4; ++b) store8_f32(sF, gl[b], (F_BT + i) * DK + 32 * b + 8 * g4);
   }
   // input prologue: beta given as a logit; q and k divided by their L2 norms
   // (the row's 128 channels sit in lanes q, q + 16, q + 32, q + 48)
@@ -403,7 +419,11 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     sF[F_W20 * DK + d] = __expf(b1);
     sF[F_W31 * DK + d] = __expf(b2);
     sF[F_W30 * DK + d] = __expf(b1 + b2);
-    reinterpret_cast<float*>(slot + SL_GAM)[d] = __expf(b0 + b1 + b2 + b3);
+    // Gam in the state's row order
+    const int sd = state_row_channel(d);
+    reinterpret_cast<float*>(slot + SL_GAM)[d] =
+        __expf(sF[F_BT * DK + sd] + sF[(F_BT + 1) * DK + sd] + sF[(F_BT + 2) * DK + sd] +
+               sF[(F_BT + 3) * DK + sd]);
   } else if (tid < DK + CH) {
     reinterpret_cast<float*>(slot + SL_BETA)[tid - DK] = sB[tid - DK];
   } else if (tid == DK + CH) {
@@ -440,7 +460,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   f32x4 adiag = {0.f, 0.f, 0.f, 0.f}, mdiag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int ch0 = 32 * b + 4 * g4;
+    const int ch0 = 32 * b + 8 * g4;
     float kf[8], qf[8], bt[8], fac[8];
     unpack8(kA[b], kf);
     unpack8(qA[b], qf);
@@ -554,7 +574,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const int wrow = (jb == i - 1) ? -1 : (i == 2 ? F_W20 : (jb == 1 ? F_W31 : F_W30));
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int ch0 = 32 * b + 4 * g4;
+      const int ch0 = 32 * b + 8 * g4;
       float ks[8], wf[8];
       load8_f32(sE, ks, (jb * 16 + q) * DK + ch0);
       if (wrow >= 0) {
@@ -827,19 +847,22 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 
   // ---- compute waves
   const int col0 = 16 * (part * WAVES + w);
-  const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q;
+  // accumulator row 16 m + 4 g4 + e holds key channel state_row_channel of it,
+  // that is 8 g4 + srow(m, e)
+  const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q + (size_t)(8 * g4) * DK;
+  auto srow = [](int m, int e) { return 32 * (m >> 1) + 4 * (m & 1) + e; };
   f32x4 S[8];
   if (a.s0 && a.state_bf16) {
     const uint16_t* s0 = reinterpret_cast<const uint16_t*>(a.s0);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][e] = bf2f(s0[sbase + (size_t)(16 * m + 4 * g4 + e) * DK]);
+      for (int e = 0; e < 4; ++e) S[m][e] = bf2f(s0[sbase + (size_t)srow(m, e) * DK]);
   } else if (a.s0) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][e] = a.s0[sbase + (size_t)(16 * m + 4 * g4 + e) * DK];
+      for (int e = 0; e < 4; ++e) S[m][e] = a.s0[sbase + (size_t)srow(m, e) * DK];
   } else {
 #pragma unroll
     for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -851,19 +874,19 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     // store addresses are not kept live in registers across the segment loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const size_t o = e0 + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 4 * DK;
+    const size_t o = e0 + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 8 * DK;
     if (a.state_bf16) {
       uint16_t* rowp = reinterpret_cast<uint16_t*>(dst) + o;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = (uint16_t)pack2(S[m][e], 0.f);
+        for (int e = 0; e < 4; ++e) rowp[srow(m, e) * DK] = (uint16_t)pack2(S[m][e], 0.f);
     } else {
       float* rowp = dst + o;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rowp[(16 * m + e) * DK] = S[m][e];
+        for (int e = 0; e < 4; ++e) rowp[srow(m, e) * DK] = S[m][e];
     }
   };
   // checkpoint c of this sequence (layout [N, C, H, K, V]): element offset
