@@ -389,3 +389,41 @@ def test_auto_schedule_table():
     want = run_gpu(p, variant=K.plan(K.make_problem(p.N, p.T_total, p.H, scale=p.scale))[0])
     assert np.array_equal(auto["out"], want["out"]) and np.array_equal(auto["final"], want["final"])
     _report("packed_128x8 auto", assert_parity(auto, ref, "packed_128x8 auto"))
+
+
+def _random_case(seed):
+    """A random small problem: ragged or fixed layout, empty sequences, an
+    initial state or none, 0 to 4 checkpoint offsets per sequence (some out
+    of range or out of order), a schedule and its value split."""
+    rng = np.random.default_rng(9000 + seed)
+    N = int(rng.integers(1, 7))
+    H = int(rng.integers(1, 4))
+    fixed = bool(rng.random() < 0.3)
+    if fixed:
+        lens = [int(rng.integers(1, 300))] * N
+    else:
+        lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 400, N)]
+    p = synth.make_problem(lens, H, seed=9100 + seed, fixed=fixed, init_state=bool(rng.random() < 0.7),
+                           gate="min" if rng.random() < 0.1 else "random")
+    C = int(rng.integers(0, 5))
+    offs = None
+    if C:
+        offs = np.stack([rng.integers(-5, L + 6, C) for L in lens]).astype(np.int32)
+        sort_rows = rng.random(N) < 0.6
+        offs[sort_rows] = np.sort(offs[sort_rows], axis=1)
+    variant = "fused" if rng.random() < 0.4 else "decomp"
+    vs = int(rng.choice([2, 4] if variant == "fused" else [1, 2, 4, 8]))
+    return p, offs, variant, vs
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_problems(seed):
+    p, offs, variant, vs = _random_case(seed)
+    ref = oracle.prefill_problem(p)
+    if offs is not None:
+        p.ckpt_offsets = offs
+    gpu = run_gpu(p, variant=variant, value_split=vs)
+    what = f"seed {seed}: lens {list(p.seq_lens)} H {p.H} {variant} vs{vs} C {0 if offs is None else offs.shape[1]}"
+    assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref, what)
+    if offs is not None:
+        _check_multi_ckpt(p, offs, gpu)
