@@ -427,3 +427,27 @@ def test_random_problems(seed):
     assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref, what)
     if offs is not None:
         _check_multi_ckpt(p, offs, gpu)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_resume_from_exported_checkpoint(variant):
+    # prefix reuse: a second call on the remaining tokens, started from the
+    # state the first call exported, reproduces the full run's outputs for
+    # those tokens and its final state (chunks now align to the resume point,
+    # so the rounding differs; both are held to the gates against the oracle)
+    lens, offs = [700, 333, 130], [300, 100, 64]
+    p = synth.make_problem(lens, 2, seed=23, init_state=True, ckpt=offs)
+    ref = oracle.prefill_problem(p)
+    first = run_gpu(p, variant=variant)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    rows = np.concatenate([np.arange(cu[n] + offs[n], cu[n + 1]) for n in range(len(lens))])
+    rest = [L - o for L, o in zip(lens, offs)]
+    p2 = synth.Problem(name="resume", seq_lens=rest, H=p.H, q=p.q[rows], k=p.k[rows], v=p.v[rows],
+                       g=p.g[rows], beta=p.beta[rows],
+                       cu_seqlens=np.concatenate([[0], np.cumsum(rest)]).astype(np.int32),
+                       fixed=False, initial_state=first["ckpt"].astype(np.float32).copy(),
+                       ckpt_offsets=None, scale=p.scale, seed=p.seed)
+    second = run_gpu(p2, variant=variant)
+    m = assert_parity({"out": second["out"], "final": second["final"]},
+                      {"out": ref["out"][rows], "final": ref["final"]}, f"resume {variant}")
+    _report(f"resume from checkpoint {variant}", m)
