@@ -191,14 +191,15 @@ def _honoured(offs, L):
     return out
 
 
-def _check_multi_ckpt(p, offs, gpu):
+def _check_multi_ckpt(p, offs, gpu, qk_l2norm=False, beta_logit=False):
     # each honoured slot holds the state after that many tokens (the oracle
     # run with that one offset); the others keep their NaN sentinel
     for c in range(offs.shape[1]):
         col = offs[:, c].copy()
         ref = oracle.prefill(p.q, p.k, p.v, p.g, p.beta, scale=p.scale, num_seqs=p.N,
                              cu_seqlens=None if p.fixed else p.cu_seqlens,
-                             initial_state=p.initial_state, ckpt_offsets=col)
+                             initial_state=p.initial_state, ckpt_offsets=col,
+                             qk_l2norm=qk_l2norm, beta_logit=beta_logit)
         for n, L in enumerate(p.seq_lens):
             if c in _honoured(list(offs[n]), L):
                 err = rel_l2(gpu["ckpt"][n, c], ref["ckpt"][n])
@@ -413,20 +414,28 @@ def _random_case(seed):
         offs[sort_rows] = np.sort(offs[sort_rows], axis=1)
     variant = "fused" if rng.random() < 0.4 else "decomp"
     vs = int(rng.choice([2, 4] if variant == "fused" else [1, 2, 4, 8]))
-    return p, offs, variant, vs
+    # the input prologue (two-launch schedule only): raw q, k and beta logits
+    qk = variant == "decomp" and rng.random() < 0.3
+    bl = variant == "decomp" and rng.random() < 0.3
+    beta = p.beta
+    if qk:
+        p = _raw_inputs(p, 9200 + seed)
+    p.beta = rng.normal(0, 1.5, beta.shape).astype(np.float32) if bl else beta
+    return p, offs, variant, vs, qk, bl
 
 
 @pytest.mark.parametrize("seed", range(32))
 def test_random_problems(seed):
-    p, offs, variant, vs = _random_case(seed)
-    ref = oracle.prefill_problem(p)
+    p, offs, variant, vs, qk, bl = _random_case(seed)
+    ref = oracle.prefill_problem(p, qk_l2norm=qk, beta_logit=bl)
     if offs is not None:
         p.ckpt_offsets = offs
-    gpu = run_gpu(p, variant=variant, value_split=vs)
-    what = f"seed {seed}: lens {list(p.seq_lens)} H {p.H} {variant} vs{vs} C {0 if offs is None else offs.shape[1]}"
+    gpu = run_gpu(p, variant=variant, value_split=vs, qk_l2norm=qk, beta_logit=bl)
+    what = (f"seed {seed}: lens {list(p.seq_lens)} H {p.H} {variant} vs{vs} "
+            f"C {0 if offs is None else offs.shape[1]} prologue {int(qk)}{int(bl)}")
     assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref, what)
     if offs is not None:
-        _check_multi_ckpt(p, offs, gpu)
+        _check_multi_ckpt(p, offs, gpu, qk_l2norm=qk, beta_logit=bl)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
