@@ -263,7 +263,11 @@ constexpr int F_ROWS = 17;
 // k exp(bt_j - Gl_s) of row blocks 0..2 (fp32 [block][row][channel]); after
 // the gated products the same space holds T (pitch P_LP) and solve scratch
 constexpr int P_E_FLOATS = CH * P_LP + 4 * 512;
-static_assert(P_E_FLOATS >= 3 * 16 * DK, "prepare LDS layout");
+// during steps 2-3 the same space holds k exp(bt_j - Gl_s) as bf16 (12 KiB)
+// and, after it, the K^^T half fragments that waves hand to their partner
+// (4 waves x 4 fragments x 512 bytes)
+constexpr int P_X_BYTES = 3 * 16 * DK * 2;
+static_assert(P_E_FLOATS * 4 >= P_X_BYTES + 4 * 4 * 512, "prepare LDS layout");
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -457,6 +461,9 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   // the diagonal block's products accumulate key block by key block, so its
   // operands (Q hi/lo, right operand hi/lo) need not stay live
   bf16x8 aK[4], aQ[4];
+  uint16_t* sEb = reinterpret_cast<uint16_t*>(sE);
+  uint2* sX = reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(sE) + P_X_BYTES);
+  uint2 kh_keep[4];
   f32x4 adiag = {0.f, 0.f, 0.f, 0.f}, mdiag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -499,8 +506,9 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     }
     *reinterpret_cast<bf16x8*>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(kt);
     *reinterpret_cast<bf16x8*>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(qt);
-    // k exp(bt - Gl) of this block for the later waves' off-diagonal products
-    if (i < 3) store8_f32(sE, kb, (i * 16 + q) * DK + ch0);
+    // k exp(bt - Gl) of this block, as bf16, for the later waves' off-diagonal
+    // products (those round it again after the factor W, when W is not 1)
+    if (i < 3) *reinterpret_cast<bf16x8*>(sEb + (i * 16 + q) * DK + ch0) = to_bf16x8(kb);
     // diagonal-block right operand k exp(-Gl) = k exp(bt - Gl) exp(-bt), hi + lo
     load8_f32(sF, fac, (F_IBD + i) * DK + ch0);
     float kr[8];
@@ -532,8 +540,13 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
       const int m = 2 * b + hh;
       const f32x4 th = mfma(khi, eye[hh], z4);
-      *reinterpret_cast<uint2*>(slot + SL_KH + ((m * 2 + (i >> 1)) * 64 + lane) * 16 + 8 * (i & 1)) =
-          make_uint2(pack2(th[0], th[1]), pack2(th[2], th[3]));
+      // K^^T fragment (m, i / 2) takes 8 bytes per lane from token tile i and
+      // 8 from its partner i ^ 1.  Wave i stores the whole fragments of key
+      // tiles 4 (i & 1) .. + 3 after the next barrier: it keeps its halves of
+      // those and hands the partner its halves of the others through LDS.
+      const uint2 half = make_uint2(pack2(th[0], th[1]), pack2(th[2], th[3]));
+      if ((m >> 2) == (i & 1)) kh_keep[m & 3] = half;
+      else sX[(i * 4 + (m & 3)) * 64 + lane] = half;
       if (i == 3) {
         const f32x4 tl = mfma(klo, eye[hh], z4);
         *reinterpret_cast<uint2*>(slot + SL_KL + m * 512 + lane * 8) =
@@ -563,6 +576,16 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
       if (jj == i) macc[jj] = m0;
   }
   lds_barrier();
+  // whole K^^T fragments (m, i / 2) for m = 4 (i & 1) .. + 3: the even token
+  // tile's 8 bytes first
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const int m = 4 * (i & 1) + s4;
+    const uint2 other = sX[((i ^ 1) * 4 + s4) * 64 + lane];
+    const uint2 lo = (i & 1) ? other : kh_keep[s4], hi = (i & 1) ? kh_keep[s4] : other;
+    *reinterpret_cast<uint4*>(slot + SL_KH + ((m * 2 + (i >> 1)) * 64 + lane) * 16) =
+        make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
 
   // (3) off-diagonal blocks (i, jb < i): right operand k exp(bt_jb - Gl_s) W_{i,jb}
   // from LDS, W = prod_{jb<m<i} exp(bt_m)
@@ -576,7 +599,11 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     for (int b = 0; b < 4; ++b) {
       const int ch0 = 32 * b + 8 * g4;
       float ks[8], wf[8];
-      load8_f32(sE, ks, (jb * 16 + q) * DK + ch0);
+      {
+        const uint4 kv = *reinterpret_cast<const uint4*>(sEb + (jb * 16 + q) * DK + ch0);
+        const uint2 kv2[2] = {make_uint2(kv.x, kv.y), make_uint2(kv.z, kv.w)};
+        unpack8(kv2, ks);
+      }
       if (wrow >= 0) {
         load8_f32(sF, wf, wrow * DK + ch0);
 #pragma unroll
