@@ -266,7 +266,8 @@ constexpr int P_E_FLOATS = CH * P_LP + 4 * 512;
 // during steps 2-3 the same space holds k exp(bt_j - Gl_s) as bf16 (12 KiB)
 // and, after it, the K^^T half fragments that waves hand to their partner
 // (4 waves x 4 fragments x 512 bytes)
-constexpr int P_X_BYTES = 3 * 16 * DK * 2;
+constexpr int P_EP = DK + 8;    // bf16 pitch of those rows (16-byte shift per row: fewer bank conflicts)
+constexpr int P_X_BYTES = 3 * 16 * P_EP * 2;
 static_assert(P_E_FLOATS * 4 >= P_X_BYTES + 4 * 4 * 512, "prepare LDS layout");
 
 __device__ __forceinline__ void wave_sync() {
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     *reinterpret_cast<bf16x8*>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(qt);
     // k exp(bt - Gl) of this block, as bf16, for the later waves' off-diagonal
     // products (those round it again after the factor W, when W is not 1)
-    if (i < 3) *reinterpret_cast<bf16x8*>(sEb + (i * 16 + q) * DK + ch0) = to_bf16x8(kb);
+    if (i < 3) *reinterpret_cast<bf16x8*>(sEb + (i * 16 + q) * P_EP + ch0) = to_bf16x8(kb);
     // diagonal-block right operand k exp(-Gl) = k exp(bt - Gl) exp(-bt), hi + lo
     load8_f32(sF, fac, (F_IBD + i) * DK + ch0);
     float kr[8];
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
       const int ch0 = 32 * b + 8 * g4;
       float ks[8], wf[8];
       {
-        const uint4 kv = *reinterpret_cast<const uint4*>(sEb + (jb * 16 + q) * DK + ch0);
+        const uint4 kv = *reinterpret_cast<const uint4*>(sEb + (jb * 16 + q) * P_EP + ch0);
         const uint2 kv2[2] = {make_uint2(kv.x, kv.y), make_uint2(kv.z, kv.w)};
         unpack8(kv2, ks);
       }
