@@ -52,7 +52,6 @@ constexpr int NT = 512;       // threads per workgroup (8 wave64s)
 constexpr int KP = DK + 8;    // bf16 pitch of [row][d] operand tiles
 constexpr int RP = CH + 8;    // bf16 pitch of [*][r] tiles (64 wide)
 constexpr int LP = 16 + 8;    // bf16 pitch of the 16-wide lo tile
-constexpr int FP = CH + 4;    // fp32 pitch of 64 x 64 matrices
 constexpr int LDP = 16 + 4;   // fp32 pitch of the 16 x 16 diagonal L blocks
 constexpr int TP = 32 + 8;    // bf16 pitch of 32 x 32 solve tiles
 constexpr int SP = 16 + 8;    // bf16 pitch of 16 x 16 solve tiles
