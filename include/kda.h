@@ -119,9 +119,8 @@ typedef struct {
                                 The recurrence itself always carries fp32; a BF16 state
                                 is widened on load and rounded to nearest even on store
                                 (the BF16 state of FlashInfer PR #4262's benchmark) */
-  int32_t prologue;          /* kda_prologue flags, 0 = none: inputs as given.  Only the
-                                DECOMP schedule has the prologue; FUSED with flags is
-                                KDA_ERR_UNSUPPORTED and AUTO then needs the workspace */
+  int32_t prologue;          /* kda_prologue flags, 0 = none: inputs as given.  Both
+                                schedules apply them */
 } kda_problem;
 
 /* Input prologue, done in the kernels before anything else reads q, k or

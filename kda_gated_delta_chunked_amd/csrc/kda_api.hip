@@ -60,8 +60,6 @@ kda_status check_problem(const kda_problem* p) {
   if (p->ckpt_per_seq < 0) return KDA_ERR_INVALID_ARG;
   if (p->state_dtype != KDA_STATE_F32 && p->state_dtype != KDA_STATE_BF16) return KDA_ERR_UNSUPPORTED;
   if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
-  // the input prologue is built into the two-launch schedule only
-  if (p->prologue && p->variant == KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;
   if (p->ckpt_per_seq > kMaxCkptPerSeq) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
@@ -115,7 +113,7 @@ int fused_vsplit(const kda_problem* p, int cus) {
 // B8 T128 32.9 / 31.4, packed 8 x 128 30.8 / 25.5; past either bound DECOMP
 // wins: B8 T192 39.2 / 40.7, B16 T128 45.3 / 53.7, B32 T64 49.9 / 52.6.
 bool fused_is_faster(const kda_problem* p, int cus) {
-  if (cus <= 0 || p->prologue || p->value_split == 1 || p->value_split == 8) return false;
+  if (cus <= 0 || p->value_split == 1 || p->value_split == 8) return false;
   const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
   const int64_t mean_len = p->total_tokens / p->num_seqs;
   return mean_len <= 2 * 64 && pairs * fused_vsplit(p, cus) <= cus;
@@ -124,7 +122,7 @@ bool fused_is_faster(const kda_problem* p, int cus) {
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
   int32_t var = p->variant;
   if (var == KDA_VARIANT_AUTO) {
-    var = ws_bytes >= decomp_bytes(p) || p->prologue ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
+    var = ws_bytes >= decomp_bytes(p) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
     if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
       var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
     if (var == KDA_VARIANT_DECOMP && fused_is_faster(p, cus)) var = KDA_VARIANT_FUSED;
@@ -295,6 +293,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.num_pairs = p->num_seqs * p->num_heads;
     a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
     a.scale = p->scale;
+    a.prologue = p->prologue;
     err = kda::launch_fused(a, vsplit, st_);
   }
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -148,6 +148,7 @@ struct SegmentLoads {
   uint32_t k[8], q[8];
   uint4 v;
   float beta;
+  bool bvalid;  // this thread's beta row lies in the segment
 };
 
 template <int VW>
@@ -303,7 +304,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     L.v = make_uint4(0, 0, 0, 0);
     if (v_thread && vr >= off)
       L.v = *reinterpret_cast<const uint4*>(a.v + ((size_t)(t0 + vr) * H + h) * DVT + col0 + 8 * vc8);
-    L.beta = (tid < 64 && tid >= off) ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    L.bvalid = tid < 64 && tid >= off;
+    L.beta = L.bvalid ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
   };
   // Gate factors of a segment, first half: exp(g), prefix (Ef) and suffix (Eb)
   // products inside this thread's half block, the half-block product to LDS,
@@ -331,7 +333,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
   auto stage_v_beta = [&](const SegmentLoads& L) {
     const int vr = tid / PER_ROW, vc8 = tid % PER_ROW;
     if (v_thread) *reinterpret_cast<uint4*>(mV + vr * Lay::VP + 8 * vc8) = L.v;
-    if (tid < 64) mBeta[tid] = L.beta;
+    // input prologue: beta given as a logit (rows outside the segment stay 0)
+    if (tid < 64) mBeta[tid] = ((a.prologue & 2) && L.bvalid) ? 1.f / (1.f + __expf(-L.beta)) : L.beta;
   };
   auto gate_factors_2 = [&]() {
     const int d0 = 2 * l;
@@ -407,14 +410,45 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
     // carry a lo part)
     uint32_t kfp[8], qfp[8];
     float kb[8][2];
+    // input prologue: q and k of each row divided by their L2 norms over the
+    // 128 channels (the row's channels sit two per lane across this wave; a
+    // zero row stays zero)
+    float ink[8], inq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ink[e] = 1.f;
+      inq[e] = 1.f;
+    }
+    if (a.prologue & 1) {
+      float sk[8], sq[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float k0 = lo_of(ld.k[e]), k1 = hi_of(ld.k[e]);
+        const float q0 = lo_of(ld.q[e]), q1 = hi_of(ld.q[e]);
+        sk[e] = k0 * k0 + k1 * k1;
+        sq[e] = q0 * q0 + q1 * q1;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sk[e] += __shfl_xor(sk[e], o, 64);
+          sq[e] += __shfl_xor(sq[e], o, 64);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ink[e] = sk[e] > 0.f ? 1.f / __builtin_sqrtf(sk[e]) : 0.f;
+        inq[e] = sq[e] > 0.f ? 1.f / __builtin_sqrtf(sq[e]) : 0.f;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int rl = 8 * hb + e;        // row within the block
       const int r = 16 * ib + rl;
       // k, q of this segment are still in the prefetch registers (the next
       // prefetch is issued only after this phase)
-      const float kk[2] = {lo_of(ld.k[e]), hi_of(ld.k[e])};
-      const float qq[2] = {lo_of(ld.q[e]), hi_of(ld.q[e])};
+      const float kk[2] = {lo_of(ld.k[e]) * ink[e], hi_of(ld.k[e]) * ink[e]};
+      const float qq[2] = {lo_of(ld.q[e]) * inq[e], hi_of(ld.q[e]) * inq[e]};
       float kf[2], qf[2];
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {

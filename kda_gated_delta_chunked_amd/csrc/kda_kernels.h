@@ -38,6 +38,7 @@ struct FusedArgs {
   int num_pairs;              // N * H
   int64_t T_fixed;
   float scale;
+  int prologue;               // bit 0: L2-normalise q and k; bit 1: beta is a logit
 };
 
 // vsplit = workgroups per (sequence, head): 2 or 4.

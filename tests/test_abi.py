@@ -338,12 +338,13 @@ def test_prologue_rules():
     bad.prologue = 4
     with pytest.raises(K.KDAError):
         K.workspace_size(bad)
-    # the one-launch schedule has no prologue; AUTO then takes the two-launch one
+    # both schedules take the prologue; AUTO with no workspace takes the
+    # one-launch schedule as without it
     p = K.make_problem(b.N, b.T, b.H, scale=0.088, variant="fused", qk_l2norm=True)
-    assert ops.validate_raw(p, *b.args()[:-2], 0, 0) == UNSUPPORTED
+    assert ops.validate_raw(p, *b.args()[:-2], 0, 0) == OK
     p = K.make_problem(b.N, b.T, b.H, scale=0.088, beta_logit=True)
-    var, _ = K.plan(p)
-    assert var == "decomp"
+    assert ops.validate_raw(p, *b.args()[:-2], 0, 0) == OK
+    p = K.make_problem(b.N, b.T, b.H, scale=0.088, variant="decomp", beta_logit=True)
     assert ops.validate_raw(p, *b.args()[:-2], 0, 0) == WS
     d = DecodeBufs()
     dp = ops.make_decode_problem(d.N, d.T, d.H, d.P, scale=0.088, qk_l2norm=True, beta_logit=True)

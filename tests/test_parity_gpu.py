@@ -292,10 +292,11 @@ def _raw_inputs(p, seed):
     return p
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("flags", [(True, True), (True, False), (False, True)])
-def test_input_prologue(flags):
-    # q and k normalised and beta taken through a sigmoid inside the prepare
-    # launch, against the oracle doing the same in fp64
+def test_input_prologue(flags, variant):
+    # q and k normalised and beta taken through a sigmoid inside the kernels,
+    # against the oracle doing the same in fp64
     qk, bl = flags
     lens = [300, 0, 129, 64, 77]
     p = synth.make_problem(lens, 3, seed=23, init_state=True, ckpt=[5, 0, 129, 64, 70])
@@ -304,8 +305,8 @@ def test_input_prologue(flags):
     else:
         p.beta = np.random.default_rng(25).normal(0, 1.5, p.beta.shape).astype(np.float32)
     ref = oracle.prefill_problem(p, qk_l2norm=qk, beta_logit=bl)
-    gpu = run_gpu(p, variant="decomp", qk_l2norm=qk, beta_logit=bl)
-    _report(f"prologue qk={qk} logit={bl}", assert_parity(gpu, ref, "prologue"))
+    gpu = run_gpu(p, variant=variant, qk_l2norm=qk, beta_logit=bl)
+    _report(f"prologue qk={qk} logit={bl} {variant}", assert_parity(gpu, ref, "prologue"))
 
 
 def test_packed_recurrence_order_longest_first():
@@ -373,7 +374,7 @@ def test_auto_schedule_table():
     def expect(N, T, H, **kw):
         pairs = N * H
         vs = 4 if pairs * 2 < cus // 2 else 2
-        if T // N <= 128 and pairs * vs <= cus and not kw:
+        if T // N <= 128 and pairs * vs <= cus:
             return ("fused", vs)
         return ("decomp", 2)
 
@@ -414,9 +415,9 @@ def _random_case(seed):
         offs[sort_rows] = np.sort(offs[sort_rows], axis=1)
     variant = "fused" if rng.random() < 0.4 else "decomp"
     vs = int(rng.choice([2, 4] if variant == "fused" else [1, 2, 4, 8]))
-    # the input prologue (two-launch schedule only): raw q, k and beta logits
-    qk = variant == "decomp" and rng.random() < 0.3
-    bl = variant == "decomp" and rng.random() < 0.3
+    # the input prologue: raw q, k and beta logits
+    qk = bool(rng.random() < 0.3)
+    bl = bool(rng.random() < 0.3)
     beta = p.beta
     if qk:
         p = _raw_inputs(p, 9200 + seed)
