@@ -309,16 +309,26 @@ def test_input_prologue(flags, variant):
     _report(f"prologue qk={qk} logit={bl} {variant}", assert_parity(gpu, ref, "prologue"))
 
 
-def test_packed_recurrence_order_longest_first():
-    # the plan launch ranks the packed sequences by slot count, longest first
-    # and ties by index; the header holds N + 1 slot offsets, then that order
-    lens = [100, 3000, 64, 3000, 1, 0, 700, 129]
-    p = synth.make_problem(lens, 2, seed=17, init_state=True)
+ORDER_CASES = {
+    "8": [100, 3000, 64, 3000, 1, 0, 700, 129],
+    # many ties and empty sequences; checkpoints add one slot per sequence
+    "64": [int(x) for x in np.random.default_rng(19).integers(0, 300, size=64)],
+    "65": [int(x) for x in np.random.default_rng(20).integers(0, 300, size=65)],
+}
+
+
+@pytest.mark.parametrize("case", sorted(ORDER_CASES))
+def test_packed_recurrence_order_longest_first(case):
+    # packed sequences are ranked by slot count, longest first and ties by
+    # index; the header holds N + 1 slot offsets, then that order
+    lens = ORDER_CASES[case]
+    ckpt = [L // 2 for L in lens] if case == "64" else None
+    p = synth.make_problem(lens, 2, seed=17, init_state=True, ckpt=ckpt)
     ref = oracle.prefill_problem(p)
     gpu = run_gpu(p, variant="decomp", keep_workspace=True)
-    assert_parity(gpu, ref, "ordered")
+    _report(f"ordered N={p.N}", assert_parity(gpu, ref, "ordered"))
     hdr = gpu["workspace"][: 4 * (2 * p.N + 1)].view(np.int32)
-    slots = [(L + 63) // 64 for L in lens]
+    slots = [(L + 63) // 64 + (1 if ckpt else 0) for L in lens]
     assert list(hdr[: p.N + 1]) == [0] + list(np.cumsum(slots))
     assert list(hdr[p.N + 1:]) == sorted(range(p.N), key=lambda n: (-slots[n], n))
 
