@@ -84,7 +84,9 @@ typedef enum {
                                     the shape the host knows (N, H, T_total / N): the one-launch
                                     schedule for short sequences (a mean of at most 128 tokens)
                                     whose workgroups all fit on the device at once, else the
-                                    two-launch schedule when the workspace holds it */
+                                    two-launch schedule when the workspace holds it, with four
+                                    workgroups per (sequence, head) when they all fit at once
+                                    and the workspace is past 176 MiB, else two */
   KDA_VARIANT_DECOMP = 1,        /* two launches through the workspace: a chunk-parallel
                                     prepare, then the recurrence (FlashInfer PR #4633,
                                     Description: the "decomp" variant) */

@@ -67,6 +67,11 @@ kda_status check_problem(const kda_problem* p) {
   return KDA_OK;
 }
 
+// workspace size past which the slots no longer stay in MI355X's 256 MB
+// Infinity Cache between the two launches (measured: a 160 MiB workspace
+// still behaves as cached, a 192 MiB one does not)
+constexpr size_t kDecompCacheBytes = size_t(176) << 20;
+
 int device_cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -93,7 +98,7 @@ size_t decomp_bytes(const kda_problem* p) {
 // and a slice of the state's columns, and repeats the chunk preparation; two
 // workgroups per pair, four when there are too few pairs to occupy half the
 // CUs.  DECOMP: the recurrence workgroup holds two slot buffers in LDS, so one
-// runs per CU; two workgroups per pair.  AUTO takes DECOMP
+// runs per CU; two workgroups per pair, or four (below).  AUTO takes DECOMP
 // whenever the workspace holds it (value_split 1 and 8 are DECOMP-only, 2 and 4
 // exist in both).
 // workgroups per pair of the one-launch schedule
@@ -133,10 +138,16 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
   } else if (p->value_split) {
     *vsplit = p->value_split;
   } else {
-    // measured on MI355X (256 CUs): two workgroups per pair is best from 12 to
-    // 384 pairs (B1 and B8 at T = 8192, B32 at T = 512); more splits add slot
-    // copies faster than they remove work per workgroup
-    *vsplit = 2;
+    // measured on MI355X (256 CUs, 256 MB Infinity Cache), H = 12 unless
+    // stated, ms per call, two / four workgroups per pair: while the
+    // workspace stays in the Infinity Cache two are best (B1 T8192 0.251 /
+    // 0.260, B1 T8192 H20 0.287 / 0.289, B4 T2048 0.103 / 0.105); once it
+    // does not, four are, when they all fit at once (B2 T8192 0.335 / 0.307,
+    // B1 T32768 1.070 / 0.984, B5 T8192 0.465 / 0.432, B1 T8192 H64 0.462 /
+    // 0.436).  Past the CU count two (B8 T8192 0.614 / 0.751); one and eight
+    // are slower everywhere.
+    const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
+    *vsplit = (cus > 0 && pairs * 4 <= cus && decomp_bytes(p) > kDecompCacheBytes) ? 4 : 2;
   }
 }
 

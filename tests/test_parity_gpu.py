@@ -376,7 +376,9 @@ def test_split_stages_equal_one_call():
 def test_auto_schedule_table():
     # AUTO takes the one-launch schedule for short sequences (mean <= 128
     # tokens) whose workgroups all fit on the device at once, else the
-    # two-launch schedule; its results are those of the schedule it names
+    # two-launch schedule (four workgroups per pair when they fit at once and
+    # the workspace is past 176 MiB); its results are those of the schedule
+    # it names
     import torch
     import kda_gated_delta_chunked_amd as K
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -386,16 +388,21 @@ def test_auto_schedule_table():
         vs = 4 if pairs * 2 < cus // 2 else 2
         if T // N <= 128 and pairs * vs <= cus:
             return ("fused", vs)
-        return ("decomp", 2)
+        ws = K.workspace_size(K.make_problem(N, T, H, scale=0.088, variant="decomp"))
+        return ("decomp", 4 if pairs * 4 <= cus and ws > (176 << 20) else 2)
 
     for N, T, H, kw in [(1, 64, 12, {}), (8, 8 * 64, 12, {}), (8, 8 * 128, 12, {}),
                         (8, 8 * 192, 12, {}), (16, 16 * 128, 12, {}), (32, 32 * 64, 12, {}),
-                        (8, 8 * 8192, 12, {}), (8, 8 * 64, 12, {"qk_l2norm": True})]:
+                        (8, 8 * 8192, 12, {}), (8, 8 * 64, 12, {"qk_l2norm": True}),
+                        (1, 8192, 12, {}), (2, 2 * 8192, 12, {}), (1, 32768, 12, {})]:
         got = K.plan(K.make_problem(N, T, H, scale=0.088, **kw))
         assert got == expect(N, T, H, **kw), (N, T, H, kw, got)
     if cus == 256:
         assert K.plan(K.make_problem(8, 8 * 128, 12, scale=0.088)) == ("fused", 2)
         assert K.plan(K.make_problem(16, 16 * 128, 12, scale=0.088))[0] == "decomp"
+        assert K.plan(K.make_problem(1, 8192, 12, scale=0.088)) == ("decomp", 2)
+        assert K.plan(K.make_problem(2, 2 * 8192, 12, scale=0.088)) == ("decomp", 4)
+        assert K.plan(K.make_problem(8, 8 * 8192, 12, scale=0.088)) == ("decomp", 2)
     p, ref = _workload_ref("packed_128x8")
     auto = run_gpu(p, variant="auto")
     want = run_gpu(p, variant=K.plan(K.make_problem(p.N, p.T_total, p.H, scale=p.scale))[0])
