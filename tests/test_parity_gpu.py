@@ -410,6 +410,21 @@ def test_auto_schedule_table():
     _report("packed_128x8 auto", assert_parity(auto, ref, "packed_128x8 auto"))
 
 
+def test_auto_four_workgroups_full_size():
+    # B2 T8192 H12: the workspace (192 MiB) is past the Infinity Cache bound,
+    # so AUTO runs the recurrence with four workgroups per pair
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    p = synth.make_problem([8192] * 2, 12, seed=1006, fixed=True, init_state=True, name="b2_t8192")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = K.plan(K.make_problem(p.N, p.T_total, p.H, scale=p.scale))
+    if cus == 256:
+        assert plan == ("decomp", 4)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant="auto")
+    _report(f"b2_t8192 auto {plan}", assert_parity(gpu, ref, "b2_t8192"))
+
+
 def _random_case(seed):
     """A random small problem: ragged or fixed layout, empty sequences, an
     initial state or none, 0 to 4 checkpoint offsets per sequence (some out
