@@ -131,6 +131,35 @@ __device__ __forceinline__ void acc_pair_split(const f32x4& a, const f32x4& b, b
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   split8(x, hi, lo);
 }
+// Workspace stores of the prepare.  With NT they are non-temporal
+// (streamed): for a workspace too large to stay in the Infinity Cache until
+// the recurrence reads it, that keeps the write stream from displacing what
+// the caches still serve; a workspace that does stay there is written
+// normally, so that the recurrence finds it in the cache.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <bool NT, class T>
+__device__ __forceinline__ void ws_put(unsigned char* p, const T& v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+  else *reinterpret_cast<T*>(p) = v;
+}
+template <bool NT>
+__device__ __forceinline__ void ws_store(unsigned char* p, const uint4& v) {
+  ws_put<NT>(p, (u32x4){v.x, v.y, v.z, v.w});
+}
+template <bool NT>
+__device__ __forceinline__ void ws_store(unsigned char* p, const uint2& v) {
+  ws_put<NT>(p, (u32x2){v.x, v.y});
+}
+template <bool NT>
+__device__ __forceinline__ void ws_store(unsigned char* p, const bf16x8& v) {
+  ws_put<NT>(p, v);
+}
+template <bool NT>
+__device__ __forceinline__ void ws_store(unsigned char* p, float v) {
+  ws_put<NT>(p, v);
+}
+
 // key channel of accumulator row R of the state: R = 32 b + 16 h + 4 g + e
 // holds channel 32 b + 8 g + 4 h + e, so that kidx(b, g, e) maps to channel
 // 32 b + 8 g + e
@@ -297,6 +326,7 @@ __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   __shared__ __attribute__((aligned(16))) float sF[F_ROWS * DK];
   __shared__ __attribute__((aligned(16))) float sE[P_E_FLOATS];
@@ -426,11 +456,11 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     sF[F_W30 * DK + d] = __expf(b1 + b2);
     // Gam in the state's row order
     const int sd = state_row_channel(d);
-    reinterpret_cast<float*>(slot + SL_GAM)[d] =
+    ws_store<NT>(slot + SL_GAM + 4 * d,
         __expf(sF[F_BT * DK + sd] + sF[(F_BT + 1) * DK + sd] + sF[(F_BT + 2) * DK + sd] +
-               sF[(F_BT + 3) * DK + sd]);
+               sF[(F_BT + 3) * DK + sd]));
   } else if (tid < DK + CH) {
-    reinterpret_cast<float*>(slot + SL_BETA)[tid - DK] = sB[tid - DK];
+    ws_store<NT>(slot + SL_BETA + 4 * (tid - DK), sB[tid - DK]);
   } else if (tid == DK + CH) {
     // the recurrence's compute waves take the segment geometry and the
     // checkpoints it completes from here, with no scalar memory access
@@ -505,8 +535,8 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
         qt[e] = Qf[e];
       }
     }
-    *reinterpret_cast<bf16x8*>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(kt);
-    *reinterpret_cast<bf16x8*>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16) = to_bf16x8(qt);
+    ws_store<NT>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16, to_bf16x8(kt));
+    ws_store<NT>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16, to_bf16x8(qt));
     // k exp(bt - Gl) of this block, as bf16, for the later waves' off-diagonal
     // products (those round it again after the factor W, when W is not 1)
     if (i < 3) *reinterpret_cast<bf16x8*>(sEb + (i * 16 + q) * P_EP + ch0) = to_bf16x8(kb);
@@ -550,8 +580,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
       else sX[(i * 4 + (m & 3)) * 64 + lane] = half;
       if (i == 3) {
         const f32x4 tl = mfma(klo, eye[hh], z4);
-        *reinterpret_cast<uint2*>(slot + SL_KL + m * 512 + lane * 8) =
-            make_uint2(pack2(tl[0], tl[1]), pack2(tl[2], tl[3]));
+        ws_store<NT>(slot + SL_KL + m * 512 + lane * 8, make_uint2(pack2(tl[0], tl[1]), pack2(tl[2], tl[3])));
       }
     }
   }
@@ -584,8 +613,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const int m = 4 * (i & 1) + s4;
     const uint2 other = sX[((i ^ 1) * 4 + s4) * 64 + lane];
     const uint2 lo = (i & 1) ? other : kh_keep[s4], hi = (i & 1) ? kh_keep[s4] : other;
-    *reinterpret_cast<uint4*>(slot + SL_KH + ((m * 2 + (i >> 1)) * 64 + lane) * 16) =
-        make_uint4(lo.x, lo.y, hi.x, hi.y);
+    ws_store<NT>(slot + SL_KH + ((m * 2 + (i >> 1)) * 64 + lane) * 16, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
 
   // (3) off-diagonal blocks (i, jb < i): right operand k exp(bt_jb - Gl_s) W_{i,jb}
@@ -627,9 +655,9 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const int f = tri_frag(i, tb);
     const uint4 mv = __builtin_bit_cast(uint4, acc_pair(macc[2 * tb], macc[2 * tb + 1]));
     if (tri_half(f))
-      *reinterpret_cast<uint2*>(slot + SL_M + tri_off(f) + lane * 8) = make_uint2(mv.x, mv.y);
+      ws_store<NT>(slot + SL_M + tri_off(f) + lane * 8, make_uint2(mv.x, mv.y));
     else
-      *reinterpret_cast<uint4*>(slot + SL_M + tri_off(f) + lane * 16) = mv;
+      ws_store<NT>(slot + SL_M + tri_off(f) + lane * 16, mv);
   }
   lds_barrier();
 
@@ -716,9 +744,9 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const int f = tri_frag(w, tb);
     const uint4 nv = __builtin_bit_cast(uint4, to_bf16x8(x));
     if (tri_half(f))
-      *reinterpret_cast<uint2*>(slot + SL_N + tri_off(f) + lane * 8) = make_uint2(nv.x, nv.y);
+      ws_store<NT>(slot + SL_N + tri_off(f) + lane * 8, make_uint2(nv.x, nv.y));
     else
-      *reinterpret_cast<uint4*>(slot + SL_N + tri_off(f) + lane * 16) = nv;
+      ws_store<NT>(slot + SL_N + tri_off(f) + lane * 16, nv);
   }
 }
 
@@ -1135,7 +1163,7 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
-                         hipStream_t stream) {
+                         bool stream_ws, hipStream_t stream) {
   hipError_t err;
   if (stages & 1) {
     if (a.cu_seqlens) {
@@ -1144,7 +1172,10 @@ hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots,
     }
     const int64_t blocks = prepare_slots * a.H;
     if (blocks > 0) {
-      hipLaunchKernelGGL(kda_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      if (stream_ws)
+        hipLaunchKernelGGL(kda_prepare_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(kda_prepare_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }

@@ -90,8 +90,10 @@ inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64
 // slots the prepare launch covers (fixed layout: N * slots_per_seq; packed:
 // slot_bound).
 // stages: bit 0 = the prepare launch (and the slot plan), bit 1 = the recurrence.
+// stream_ws: the prepare writes the workspace with non-temporal stores (for a
+// workspace that does not stay in the Infinity Cache until the recurrence).
 hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
-                         hipStream_t stream);
+                         bool stream_ws, hipStream_t stream);
 
 // State-pool decode: N requests advance by T tokens each from the pool
 // states their indices name (kda_decode.hip).
