@@ -306,6 +306,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.N = p->num_seqs;
     a.H = p->num_heads;
     a.num_pairs = p->num_seqs * p->num_heads;
+    a.T_total = p->total_tokens;
     a.T_fixed = cu_seqlens ? 0 : p->total_tokens / p->num_seqs;
     a.scale = p->scale;
     a.prologue = p->prologue;

@@ -21,6 +21,20 @@
 
 namespace kda {
 
+// Token range of a sequence from its two cu_seqlens entries b = cu[n] and
+// e = cu[n + 1], kept inside [0, T_total]: b is clamped into [0, T_total] and
+// e into [b, T_total].  Offsets that break the contract (start at 0, end at
+// T_total, non-decreasing; lmdeploy PR #5050, Modification, leaves them to the
+// caller) then give a shorter or empty sequence, never an access outside the
+// q/k/v/g/beta/out tensors.
+__host__ __device__ inline void clamp_seq_range(int64_t b, int64_t e, int64_t T_total, int64_t* bos,
+                                                int64_t* len) {
+  b = b < 0 ? 0 : (b > T_total ? T_total : b);
+  e = e < b ? b : (e > T_total ? T_total : e);
+  *bos = b;
+  *len = e - b;
+}
+
 // On the device the C <= 64 offsets live one per lane of the wave (lane c
 // holds offset c, read once at kernel start) and are taken out with
 // readlane: the walks below then do no memory access, so they add no wait on

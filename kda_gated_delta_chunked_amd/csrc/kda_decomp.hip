@@ -49,10 +49,28 @@
 //   block (i,i):   exp(G_r - G_s) = exp(Gl_r) * exp(-Gl_s)
 //   block (i,j<i): exp(G_r - G_s) = exp(Gl_r) * exp(bt_j - Gl_s) * prod_{j<m<i} exp(bt_m)
 //
-// Precision: bf16 operands with fp32 accumulation, except the diagonal blocks
-// of M (hi + lo operands), U (hi + lo into M U and the state update), the last
-// 16 rows of K^ (hi + lo) and the identity part of T (U = Y + N Y in fp32); the
-// triangular solve is done in fp32.
+// Precision.  The matrix cores take fp16 operands with fp32 accumulation
+// (v_mfma_f32_16x16x32_f16) wherever the operand's range allows it: K~, Q~
+// and K^ (|k|, |q| <= 1 times factors <= 1), N (|N| <= 1: an entry of T is
+// the response of one write to an earlier one through contracting steps), the
+// gated products left of the diagonal block (both factors <= 1), and the
+// state, V, Y and U after multiplying them by a power of two 2^s kept per
+// compute wave.  The diagonal 16 x 16 blocks of A and M, whose right factor
+// reaches exp(80), take bf16 hi + lo operands; U is fed as fp16 hi + lo into
+// the state update; the identity part of T stays fp32 (U = Y + N Y); the
+// triangular solve is fp32.  fp16 keeps 11 significant bits against bf16's 8:
+// at slow decay (g near 0) the corrections K~ S and N Y are as large as the
+// writes themselves and their rounding no longer decays away, which with
+// bf16 operands put the state's error near 1e-3.
+//
+// The power of two: the recurrence multiplies its fp32 state by 2^s and feeds
+// 2^s V to the products, so every product of the segment is 2^s times the
+// unscaled one (exact).  s is reset, when the larger of max|2^s S| and
+// max|2^s V| leaves [4, 64], so that it lands in [16, 32): then |2^s X| <=
+// sqrt(128) 64, |2^s Y| < 2^9.6 and |2^s U| < 64 * 2^9.6 (rows of T sum at most
+// 64 terms of magnitude <= 1) stay below the fp16 limit of 65504, and the
+// values that matter stay far above its subnormal range.  The read-out takes
+// scale * 2^-s, and exported states 2^-s.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -65,20 +83,19 @@ namespace {
 constexpr int CH = 64;    // chunk rows
 constexpr int DK = 128;   // key channels = value channels
 
-// Slot layout (bytes).  Fragments are 64 lanes x 16 bytes = 1 KiB.
+// Slot layout (bytes).  Fragments are 64 lanes x 16 bytes = 1 KiB, fp16.
 constexpr int SL_KT = 0;        // K~  : row tile t (4) x key block b (4), A of K~ S
 constexpr int SL_QT = 16384;    // Q~  : token tile t (4) x key block b (4), B of S^T Q~^T
-constexpr int SL_KH = 32768;    // K^ hi: key tile m (8) x token block b (2), A of K^^T U
-constexpr int SL_KL = 49152;    // K^ lo, tokens 48..63: key tile m (8), 8 bytes per lane
-constexpr int SL_M = 53248;     // M  : token tile t x token block b <= t/2 (6 fragments, 5 KiB)
-constexpr int SL_N = 58368;     // N  : same tiling as M
-constexpr int SL_GAM = 63488;   // exp(G_end), 128 fp32
-constexpr int SL_BETA = 64000;  // beta per tile row, 64 fp32 (0 on empty rows)
+constexpr int SL_KH = 32768;    // K^  : key tile m (8) x token block b (2), A of K^^T U
+constexpr int SL_M = 49152;     // M  : token tile t x token block b <= t/2 (6 fragments, 5 KiB)
+constexpr int SL_N = 54272;     // N  : same tiling as M
+constexpr int SL_GAM = 59392;   // exp(G_end), 128 fp32
+constexpr int SL_BETA = 59904;  // beta per tile row, 64 fp32 (0 on empty rows)
 // segment header: int32 off (first tile row of the segment), int32 spare,
 // int64 tok0 (token of tile row 0), uint64 export mask (bit c: checkpoint c
 // of the sequence is the state after this segment)
-constexpr int SL_HDR = 64256;
-constexpr int SLOT_UNITS = 63;  // 1 KiB copy units per slot
+constexpr int SL_HDR = 60160;
+constexpr int SLOT_UNITS = 59;  // 1 KiB copy units per slot
 static_assert(SLOT_UNITS * 1024 == kDecompSlotBytes, "slot size");
 static_assert(SL_BETA + 256 <= SL_HDR && SL_HDR + 24 <= kDecompSlotBytes, "slot layout");
 
@@ -87,9 +104,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// two floats -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+__device__ __forceinline__ float h_lo(uint32_t p) { return (float)__builtin_bit_cast(f16x2, p)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t p) { return (float)__builtin_bit_cast(f16x2, p)[1]; }
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const f32x2 f = {a, b};
@@ -127,9 +157,33 @@ __device__ __forceinline__ bf16x8 acc_pair(const f32x4& a, const f32x4& b) {
   u.w = pack2(b[2], b[3]);
   return __builtin_bit_cast(bf16x8, u);
 }
-__device__ __forceinline__ void acc_pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+// the fp16 counterparts: eight floats -> f16x8, hi + lo pairs, accumulator pairs
+__device__ __forceinline__ f16x8 to_f16x8(const float (&x)[8]) {
+  uint4 u;
+  u.x = pack2h(x[0], x[1]);
+  u.y = pack2h(x[2], x[3]);
+  u.z = pack2h(x[4], x[5]);
+  u.w = pack2h(x[6], x[7]);
+  return __builtin_bit_cast(f16x8, u);
+}
+__device__ __forceinline__ f16x8 acc_pair_h(const f32x4& a, const f32x4& b) {
+  uint4 u;
+  u.x = pack2h(a[0], a[1]);
+  u.y = pack2h(a[2], a[3]);
+  u.z = pack2h(b[0], b[1]);
+  u.w = pack2h(b[2], b[3]);
+  return __builtin_bit_cast(f16x8, u);
+}
+__device__ __forceinline__ void acc_pair_split_h(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  split8(x, hi, lo);
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack2h(x[2 * e], x[2 * e + 1]);
+    l[e] = pack2h(x[2 * e] - h_lo(h[e]), x[2 * e + 1] - h_hi(h[e]));
+  }
+  hi = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(f16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 // Workspace stores of the prepare.  With NT they are non-temporal
 // (streamed): for a workspace too large to stay in the Infinity Cache until
@@ -197,10 +251,9 @@ __device__ __forceinline__ SeqInfo seq_info(const DecompArgs& a, int n) {
     e = b + a.T_fixed;
   }
   // keep every access inside [0, T_total) even for offsets that break the contract
-  b = b < 0 ? 0 : (b > a.T_total ? a.T_total : b);
-  e = e < b ? b : (e > a.T_total ? a.T_total : e);
-  s.bos = b;
-  s.len = (int)(e - b);
+  int64_t len;
+  clamp_seq_range(b, e, a.T_total, &s.bos, &len);
+  s.len = (int)len;
   s.ck = load_ckpt_list(a.ckpt_off, a.ckpt_per_seq, n, s.len);
   s.nseg = (s.len + CH - 1) / CH + count_cuts(s.ck);
   return s;
@@ -235,10 +288,9 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
     const int n = n0 + t;
     int cnt = 0;
     if (n < a.N) {
-      int64_t b = a.cu_seqlens[n], e = a.cu_seqlens[n + 1];
-      b = b < 0 ? 0 : (b > a.T_total ? a.T_total : b);
-      e = e < b ? b : (e > a.T_total ? a.T_total : e);
-      cnt = (int)((e - b + CH - 1) / CH) + extra;
+      int64_t b, len;
+      clamp_seq_range(a.cu_seqlens[n], a.cu_seqlens[n + 1], a.T_total, &b, &len);
+      cnt = (int)((len + CH - 1) / CH) + extra;
     }
     int x = cnt;
 #pragma unroll
@@ -320,10 +372,46 @@ __device__ __forceinline__ void unpack8(const uint2 (&u)[2], float (&x)[8]) {
   x[0] = lo_of(u[0].x); x[1] = hi_of(u[0].x); x[2] = lo_of(u[0].y); x[3] = hi_of(u[0].y);
   x[4] = lo_of(u[1].x); x[5] = hi_of(u[1].x); x[6] = lo_of(u[1].y); x[7] = hi_of(u[1].y);
 }
+// eight fp16 (two uint2) -> floats
+__device__ __forceinline__ void unpack8h(const uint2 (&u)[2], float (&x)[8]) {
+  x[0] = h_lo(u[0].x); x[1] = h_hi(u[0].x); x[2] = h_lo(u[0].y); x[3] = h_hi(u[0].y);
+  x[4] = h_lo(u[1].x); x[5] = h_hi(u[1].x); x[6] = h_lo(u[1].y); x[7] = h_hi(u[1].y);
+}
 // value of lane q - n of this 16-lane row (0 for q < n)
 template <int N>
 __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+// largest value over the wave of non-negative x, the same in every lane: the
+// 16-lane rows by DPP shifts (lane 15 of a row ends with the row's maximum),
+// then the four row results through scalar registers
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, row_shr<1>(x));
+  x = fmaxf(x, row_shr<2>(x));
+  x = fmaxf(x, row_shr<4>(x));
+  x = fmaxf(x, row_shr<8>(x));
+  const int xi = __float_as_int(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(xi, 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(xi, 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(xi, 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(xi, 63));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)))));
+}
+
+// 2^e for |e| <= 126, built from its exponent bits
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }
+
+// Operand scale exponent after seeing `big`, the largest of |2^s S| and
+// |2^s V| over the wave (the same in every lane): s stays while big lies in
+// [4, 64] or is 0 (or not finite); otherwise the new s puts big in [16, 32),
+// limited to |s| <= 120.
+__device__ __forceinline__ int rescale_exponent(float big, int s) {
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_int(big));
+  if (b == 0u || b >= 0x7f800000u || (b >= 0x40800000u && b <= 0x42800000u)) return s;
+  const int e = (int)(b >> 23) - 127;   // big in [2^e, 2^(e + 1)) (e = -127: subnormal)
+  int ns = s + 4 - e;
+  ns = ns < -120 ? -120 : (ns > 120 ? 120 : ns);
+  return ns;
 }
 
 template <bool NT>
@@ -433,7 +521,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     inv_k = ssk > 0.f ? 1.f / __builtin_sqrtf(ssk) : 0.f;
     inv_q = ssq > 0.f ? 1.f / __builtin_sqrtf(ssq) : 0.f;
   }
-  const float qmul = a.scale * inv_q;
+  const float qmul = inv_q;   // the read-out scale is applied by the recurrence
   lds_barrier();
 
   // (1) per-channel block factors; Gam and beta go straight to the slot
@@ -476,8 +564,8 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 
   // (2) wave i: operands of row block i and the diagonal block (i, i).
   // Identity slices that transpose a K^ tile with one exact matrix product:
-  // lane 16 g + n holds 1.0 at element 4 h + n % 4 when n / 4 == g.
-  bf16x8 eye[2];
+  // lane 16 g + n holds 1.0 (fp16) at element 4 h + n % 4 when n / 4 == g.
+  f16x8 eye[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     uint32_t wv[4] = {0u, 0u, 0u, 0u};
@@ -485,13 +573,14 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     const bool on = (q >> 2) == g4;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (on && el == e) wv[e >> 1] |= 0x3f80u << (16 * (e & 1));
-    eye[hh] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+      if (on && el == e) wv[e >> 1] |= 0x3c00u << (16 * (e & 1));
+    eye[hh] = __builtin_bit_cast(f16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
   }
   const float beta_r = sB[r];
   // the diagonal block's products accumulate key block by key block, so its
-  // operands (Q hi/lo, right operand hi/lo) need not stay live
-  bf16x8 aK[4], aQ[4];
+  // bf16 hi / lo operands need not stay live; the fp16 row-block operands
+  // (aK, aQ) serve the off-diagonal blocks in step (3)
+  f16x8 aK[4], aQ[4];
   uint16_t* sEb = reinterpret_cast<uint16_t*>(sE);
   uint2* sX = reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(sE) + P_X_BYTES);
   uint2 kh_keep[4];
@@ -516,9 +605,8 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
       Kf[e] = kf[e] * ef;
       Qf[e] = qf[e] * ef;
     }
-    aK[b] = to_bf16x8(Kf);
-    bf16x8 aQl;
-    split8(Qf, aQ[b], aQl);
+    aK[b] = to_f16x8(Kf);
+    aQ[b] = to_f16x8(Qf);
     // K~ and Q~ fragments (row tile i, key block b)
     float kt[8], qt[8];
     if (i > 0) {
@@ -535,21 +623,26 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
         qt[e] = Qf[e];
       }
     }
-    ws_store<NT>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16, to_bf16x8(kt));
-    ws_store<NT>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16, to_bf16x8(qt));
-    // k exp(bt - Gl) of this block, as bf16, for the later waves' off-diagonal
+    ws_store<NT>(slot + SL_KT + ((i * 4 + b) * 64 + lane) * 16, __builtin_bit_cast(uint4, to_f16x8(kt)));
+    ws_store<NT>(slot + SL_QT + ((i * 4 + b) * 64 + lane) * 16, __builtin_bit_cast(uint4, to_f16x8(qt)));
+    // k exp(bt - Gl) of this block, as fp16, for the later waves' off-diagonal
     // products (those round it again after the factor W, when W is not 1)
-    if (i < 3) *reinterpret_cast<bf16x8*>(sEb + (i * 16 + q) * P_EP + ch0) = to_bf16x8(kb);
-    // diagonal-block right operand k exp(-Gl) = k exp(bt - Gl) exp(-bt), hi + lo
+    if (i < 3) *reinterpret_cast<f16x8*>(sEb + (i * 16 + q) * P_EP + ch0) = to_f16x8(kb);
+    // diagonal block: right operand k exp(-Gl) = k exp(bt - Gl) exp(-bt) (up
+    // to exp(80): bf16), all operands hi + lo
     load8_f32(sF, fac, (F_IBD + i) * DK + ch0);
     float kr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) kr[e] = kb[e] * fac[e];
-    bf16x8 bD, bDl;
+    bf16x8 bD, bDl, aKh, aKl, aQh, aQl;
     split8(kr, bD, bDl);
-    adiag = mfma(bD, aK[b], adiag);
-    mdiag = mfma(bD, aQ[b], mdiag);
-    mdiag = mfma(bDl, aQ[b], mdiag);
+    split8(Kf, aKh, aKl);
+    split8(Qf, aQh, aQl);
+    adiag = mfma(bD, aKh, adiag);
+    adiag = mfma(bDl, aKh, adiag);
+    adiag = mfma(bD, aKl, adiag);
+    mdiag = mfma(bD, aQh, mdiag);
+    mdiag = mfma(bDl, aQh, mdiag);
     mdiag = mfma(bD, aQl, mdiag);
     // K^ = k exp(G_end - G_r) = k exp(bt_i - Gl) R_i; transposed into K^^T
     // fragments by products with the identity slices (exact: one nonzero
@@ -564,8 +657,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kh[e] = kb[e];
     }
-    bf16x8 khi, klo;
-    split8(kh, khi, klo);
+    const f16x8 khi = to_f16x8(kh);
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -575,17 +667,13 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
       // 8 from its partner i ^ 1.  Wave i stores the whole fragments of key
       // tiles 4 (i & 1) .. + 3 after the next barrier: it keeps its halves of
       // those and hands the partner its halves of the others through LDS.
-      const uint2 half = make_uint2(pack2(th[0], th[1]), pack2(th[2], th[3]));
+      const uint2 half = make_uint2(pack2h(th[0], th[1]), pack2h(th[2], th[3]));
       if ((m >> 2) == (i & 1)) kh_keep[m & 3] = half;
       else sX[(i * 4 + (m & 3)) * 64 + lane] = half;
-      if (i == 3) {
-        const f32x4 tl = mfma(klo, eye[hh], z4);
-        ws_store<NT>(slot + SL_KL + m * 512 + lane * 8, make_uint2(pack2(tl[0], tl[1]), pack2(tl[2], tl[3])));
-      }
     }
   }
 
-  // diagonal block: A_ii^T (bf16) and M_ii^T (hi + lo), lane holds row r, s = 16 i + 4 g4 + e
+  // diagonal block: A_ii^T and M_ii^T (hi + lo operands), lane holds row r, s = 16 i + 4 g4 + e
   f32x4 macc[4];
   {
     const f32x4 aacc = adiag;
@@ -627,18 +715,17 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int ch0 = 32 * b + 8 * g4;
-      float ks[8], wf[8];
-      {
-        const uint4 kv = *reinterpret_cast<const uint4*>(sEb + (jb * 16 + q) * P_EP + ch0);
-        const uint2 kv2[2] = {make_uint2(kv.x, kv.y), make_uint2(kv.z, kv.w)};
-        unpack8(kv2, ks);
-      }
+      f16x8 bb = *reinterpret_cast<const f16x8*>(sEb + (jb * 16 + q) * P_EP + ch0);
       if (wrow >= 0) {
+        const uint4 kv = __builtin_bit_cast(uint4, bb);
+        const uint2 kv2[2] = {make_uint2(kv.x, kv.y), make_uint2(kv.z, kv.w)};
+        float ks[8], wf[8];
+        unpack8h(kv2, ks);
         load8_f32(sF, wf, wrow * DK + ch0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) ks[e] *= wf[e];
+        bb = to_f16x8(ks);
       }
-      const bf16x8 bb = to_bf16x8(ks);
       aacc = mfma(bb, aK[b], aacc);
       m1 = mfma(bb, aQ[b], m1);
     }
@@ -653,7 +740,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   for (int tb = 0; tb < 2; ++tb) {
     if (2 * tb > i) continue;
     const int f = tri_frag(i, tb);
-    const uint4 mv = __builtin_bit_cast(uint4, acc_pair(macc[2 * tb], macc[2 * tb + 1]));
+    const uint4 mv = __builtin_bit_cast(uint4, acc_pair_h(macc[2 * tb], macc[2 * tb + 1]));
     if (tri_half(f))
       ws_store<NT>(slot + SL_M + tri_off(f) + lane * 8, make_uint2(mv.x, mv.y));
     else
@@ -742,7 +829,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
                         s0 + 16 < r ? v1.x : 0.f, s0 + 17 < r ? v1.y : 0.f,
                         s0 + 18 < r ? v1.z : 0.f, s0 + 19 < r ? v1.w : 0.f};
     const int f = tri_frag(w, tb);
-    const uint4 nv = __builtin_bit_cast(uint4, to_bf16x8(x));
+    const uint4 nv = __builtin_bit_cast(uint4, to_f16x8(x));
     if (tri_half(f))
       ws_store<NT>(slot + SL_N + tri_off(f) + lane * 8, make_uint2(nv.x, nv.y));
     else
@@ -907,7 +994,9 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   // that is 8 g4 + srow(m, e)
   const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q + (size_t)(8 * g4) * DK;
   auto srow = [](int m, int e) { return 32 * (m >> 1) + 4 * (m & 1) + e; };
+  // S holds 2^sexp times the state (sexp is the wave's operand scale exponent)
   f32x4 S[8];
+  int sexp = 0;
   if (a.s0 && a.state_bf16) {
     const uint16_t* s0 = reinterpret_cast<const uint16_t*>(a.s0);
 #pragma unroll
@@ -924,25 +1013,27 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   // state store into dst at element offset e0 (fp32, or bf16 rounded to
-  // nearest even when the states are bf16)
+  // nearest even when the states are bf16); the power of two comes off
+  // exactly
   auto store_state = [&](float* dst, size_t e0) {
     // the lane's offsets are formed here from an opaque lane index, so the 32
     // store addresses are not kept live in registers across the segment loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const size_t o = e0 + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 8 * DK;
+    const float unscale = pow2f(-sexp);
     if (a.state_bf16) {
       uint16_t* rowp = reinterpret_cast<uint16_t*>(dst) + o;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rowp[srow(m, e) * DK] = (uint16_t)pack2(S[m][e], 0.f);
+        for (int e = 0; e < 4; ++e) rowp[srow(m, e) * DK] = (uint16_t)pack2(S[m][e] * unscale, 0.f);
     } else {
       float* rowp = dst + o;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rowp[srow(m, e) * DK] = S[m][e];
+        for (int e = 0; e < 4; ++e) rowp[srow(m, e) * DK] = S[m][e] * unscale;
     }
   };
   // checkpoint c of this sequence (layout [N, C, H, K, V]): element offset
@@ -982,8 +1073,8 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     const int qq = lq & 15, gg = lq >> 4;
     // slot byte offsets: K~ from `kcur`, the rest from `cur` (shifted by KB)
     auto frag = [&](int byte_off) {
-      return __builtin_bit_cast(bf16x8, byte_off < SL_QT ? kcur[(byte_off >> 4) + lq]
-                                                         : cur[((byte_off - KB) >> 4) + lq]);
+      return __builtin_bit_cast(f16x8, byte_off < SL_QT ? kcur[(byte_off >> 4) + lq]
+                                                        : cur[((byte_off - KB) >> 4) + lq]);
     };
     auto f4 = [&](int byte_off) {
       return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(cur) + byte_off - KB);
@@ -993,9 +1084,9 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       const char* base = reinterpret_cast<const char*>(cur) + region - KB + tri_off(f);
       if (tri_half(f)) {
         const uint2 lo = *reinterpret_cast<const uint2*>(base + lq * 8);
-        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, 0u, 0u));
+        return __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, 0u, 0u));
       }
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(base + lq * 16));
+      return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(base + lq * 16));
     };
     const uint16_t* vblk = reinterpret_cast<const uint16_t*>(cur + (SLOT_UNITS - KB / 1024) * 64);
 
@@ -1007,7 +1098,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   do {                                              \
     if (BATCHED) __builtin_amdgcn_sched_barrier(0); \
   } while (0)
-    bf16x8 fk[16], fq[16];
+    f16x8 fk[16], fq[16];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1018,9 +1109,9 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     float4 bt4[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) bt4[t] = f4(SL_BETA + (16 * t + 4 * gg) * 4);
-    bf16x8 Sb[4];
+    f16x8 Sb[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) Sb[b] = acc_pair(S[2 * b], S[2 * b + 1]);
+    for (int b = 0; b < 4; ++b) Sb[b] = acc_pair_h(S[2 * b], S[2 * b + 1]);
     KDA_FENCE();
     // X = K~ S, key blocks 0-1; the rest of K~ is read meanwhile
     f32x4 X[4], O[4];
@@ -1053,9 +1144,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) vv[4 * t + e] = vblk[(16 * t + 4 * gg + e) * VW + 16 * w + qq];
-    bf16x8 fn[6];
+    // N: read here when the wave reads in batches; without batches (more
+    // waves, fewer registers each) only after the scale check below, so that
+    // its registers are free for a recomputation
+    f16x8 fn[6];
+    if constexpr (BATCHED) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) fn[i] = trifrag(SL_N, i);
+      for (int i = 0; i < 6; ++i) fn[i] = trifrag(SL_N, i);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[0], fq[t * 4], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -1063,16 +1159,64 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
       for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[b], fq[t * 4 + b], O[t]);
     KDA_FENCE();
-    // Y = beta (V - X), kept in U; U = Y + N Y.  Rows before the segment have
-    // beta = 0 (their V read is a copy of row `off`), so they give U = 0.
+    // Operand scale check, while the products above run: the largest of
+    // |2^s S| and |2^s V| over the wave must lie in [4, 64] (or be 0).  When
+    // it does not, s is reset so that it lands in [16, 32) -- the state is
+    // multiplied by the change of 2^s (exact) and X, O are formed again.
+    {
+      float mx = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(S[m][e]));
+      // |V| as bf16 bits: for non-negative values their order is the values' order
+      uint32_t vmax = 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vmax = max(vmax, (uint32_t)vv[i] & 0x7fffu);
+      const float big = wave_max_nonneg(fmaxf(mx, bf2f(vmax) * pow2f(sexp)));
+      const int nexp = rescale_exponent(big, sexp);
+      if (nexp != sexp) {
+        const int dexp = nexp - sexp;
+        sexp = nexp;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[m][e] = __builtin_ldexpf(S[m][e], dexp);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Sb[b] = acc_pair_h(S[2 * b], S[2 * b + 1]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          X[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        // K~ and Q~ read again (the buffers hold them until the next
+        // barrier), one key block at a time
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            X[t] = mfma(frag(SL_KT + (t * 4 + b) * 1024), Sb[b], X[t]);
+            O[t] = mfma(Sb[b], frag(SL_QT + (t * 4 + b) * 1024), O[t]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if constexpr (!BATCHED) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) fn[i] = trifrag(SL_N, i);
+    }
+    const float sig = pow2f(sexp);
+    // Y = beta (2^s V - X), kept in U; U = Y + N Y.  Rows before the segment
+    // have beta = 0 (their V read is a copy of row `off`), so they give U = 0.
     f32x4 U[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float bv[4] = {bt4[t].x, bt4[t].y, bt4[t].z, bt4[t].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) U[t][e] = bv[e] * (__uint_as_float((uint32_t)vv[4 * t + e] << 16) - X[t][e]);
+      for (int e = 0; e < 4; ++e) U[t][e] = bv[e] * (bf2f(vv[4 * t + e]) * sig - X[t][e]);
     }
-    const bf16x8 Y0 = acc_pair(U[0], U[1]), Y1 = acc_pair(U[2], U[3]);
+    const f16x8 Y0 = acc_pair_h(U[0], U[1]), Y1 = acc_pair_h(U[2], U[3]);
     U[0] = mfma(fn[tri_frag(0, 0)], Y0, U[0]);
     U[1] = mfma(fn[tri_frag(1, 0)], Y0, U[1]);
     U[2] = mfma(fn[tri_frag(2, 0)], Y0, U[2]);
@@ -1080,15 +1224,15 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     U[2] = mfma(fn[tri_frag(2, 1)], Y1, U[2]);
     U[3] = mfma(fn[tri_frag(3, 1)], Y1, U[3]);
     // M and the first half of K^, read while N Y runs
-    bf16x8 fm[6], fh[16];
+    f16x8 fm[6], fh[16];
 #pragma unroll
     for (int i = 0; i < 6; ++i) fm[i] = trifrag(SL_M, i);
 #pragma unroll
     for (int i = 0; i < 8; ++i) fh[i] = frag(SL_KH + i * 1024);
     KDA_FENCE();
-    bf16x8 Uh[2], Ul[2];
-    acc_pair_split(U[0], U[1], Uh[0], Ul[0]);
-    acc_pair_split(U[2], U[3], Uh[1], Ul[1]);
+    f16x8 Uh[2], Ul[2];
+    acc_pair_split_h(U[0], U[1], Uh[0], Ul[0]);
+    acc_pair_split_h(U[2], U[3], Uh[1], Ul[1]);
     // O^T += U^T M^T
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -1096,24 +1240,20 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       for (int b = 0; b < 2; ++b) {
         if (2 * b > t) continue;
         O[t] = mfma(Uh[b], fm[tri_frag(t, b)], O[t]);
-        O[t] = mfma(Ul[b], fm[tri_frag(t, b)], O[t]);
       }
-    // second half of K^, the K^ lo fragments and Gam, read while M U runs
+    // second half of K^ and Gam, read while M U runs
 #pragma unroll
     for (int i = 8; i < 16; ++i) fh[i] = frag(SL_KH + i * 1024);
-    uint2 kl[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-      kl[m] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur) + SL_KL - KB + m * 512 + lq * 8);
     float4 gm[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
     KDA_FENCE();
-    // Q~ and M carry the read-out scale
+    // read-out: scale * 2^-s
+    const float osc = a.scale * pow2f(-sexp);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      opk[2 * t] = pack2(O[t][0], O[t][1]);
-      opk[2 * t + 1] = pack2(O[t][2], O[t][3]);
+      opk[2 * t] = pack2(O[t][0] * osc, O[t][1] * osc);
+      opk[2 * t + 1] = pack2(O[t][2] * osc, O[t][3] * osc);
     }
     // S <- diag(Gam) S + K^^T U
 #pragma unroll
@@ -1122,12 +1262,10 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       S[m][1] *= gm[m].y;
       S[m][2] *= gm[m].z;
       S[m][3] *= gm[m].w;
-      const bf16x8 klf = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, kl[m].x, kl[m].y));
       S[m] = mfma(fh[2 * m], Uh[0], S[m]);
       S[m] = mfma(fh[2 * m], Ul[0], S[m]);
       S[m] = mfma(fh[2 * m + 1], Uh[1], S[m]);
       S[m] = mfma(fh[2 * m + 1], Ul[1], S[m]);
-      S[m] = mfma(klf, Uh[1], S[m]);
     }
 #undef KDA_FENCE
     poff = off;

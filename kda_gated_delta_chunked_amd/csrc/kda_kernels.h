@@ -36,6 +36,7 @@ struct FusedArgs {
   int N;
   int H;
   int num_pairs;              // N * H
+  int64_t T_total;
   int64_t T_fixed;
   float scale;
   int prologue;               // bit 0: L2-normalise q and k; bit 1: beta is a logit
@@ -47,7 +48,7 @@ hipError_t launch_fused(const FusedArgs& a, int vsplit, hipStream_t stream);
 // Two-launch schedule.  The workspace holds a header of (N + 1) int32 slot
 // offsets and N int32 sequence indices in recurrence order (packed layout),
 // followed by one slot of kDecompSlotBytes per (segment, head).
-constexpr int kDecompSlotBytes = 64512;
+constexpr int kDecompSlotBytes = 60416;
 
 struct DecompArgs {
   const uint16_t* q;

@@ -269,6 +269,7 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
                         ckpt_per_seq=C,
                         state_dtype="bf16" if state_dtype == torch.bfloat16 else "fp32",
                         qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+    out_given, final_given = out, final_state
     if out is None:
         out = torch.empty_like(v)
     elif out.shape != q.shape:
@@ -277,6 +278,7 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         final_state = torch.empty(state_shape, dtype=state_dtype, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    own_ws = False
     with torch.cuda.device(dev):
         if workspace is None:
             # a workspace only for the two-launch schedule (AUTO: when the
@@ -284,10 +286,21 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
             need = workspace_size(prob)
             if need and variant != "fused" and (variant != "auto" or plan(prob)[0] == "decomp"):
                 workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+                own_ws = True
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         st = prefill_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                          _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(ckpt_offsets),
                          _ptr(ckpt_state), _ptr(workspace), ws_bytes, int(stream.cuda_stream))
+        # Blocks allocated here belong to the current stream in torch's caching
+        # allocator.  When the call runs on another stream, tell the allocator
+        # that stream uses them, so that a block (above all the workspace,
+        # dropped on return) is not handed to a new allocation on the current
+        # stream while the kernels still read or write it.
+        if stream != torch.cuda.current_stream(dev):
+            for t, mine in ((workspace, own_ws), (out, out_given is None),
+                            (final_state, final_given is None)):
+                if mine and t is not None:
+                    t.record_stream(stream)
     _check(st, "kda_prefill")
     return out, final_state
 

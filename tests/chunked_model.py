@@ -3,8 +3,9 @@
 This is not the oracle and not the GPU code.  It restates the chunked algebra
 the HIP kernels implement, so a CPU test can show that (a) in fp64 the chunked
 form reproduces the token recurrence to rounding (any chunk size, any tail),
-and (b) with bf16 rounding placed where the kernels feed the matrix cores,
-the result still meets the parity tolerances.
+and (b) with the rounding the kernels apply where they feed the matrix cores
+(fp16 or bf16 operands, some as hi + lo pairs; see KERNEL_RECIPE), the result
+still meets the parity tolerances.
 
 Within a chunk of c <= C rows that starts from state S0 (rows r = 0..c-1):
 
@@ -21,7 +22,8 @@ The gated products are formed the way the kernels form them: rows are grouped
 in 16-row blocks, block i has reference point ref_i = G_{16i-1} (ref_0 = 0),
 and exp(G_r - G_s) = exp(G_r - ref_i) * exp(ref_i - G_s) with r in block i.
 For s in an earlier block both factors are <= 1; within the block the right
-factor is at most exp(5 * 16) when g >= -5, which fp32 holds.
+factor is at most exp(5 * 16) when g >= -5, which fp32 and bf16 hold (fp16,
+whose largest value is about exp(11), does not: those blocks use bf16).
 """
 from __future__ import annotations
 
@@ -43,33 +45,30 @@ def split_hi_lo(x):
     return hi, lo
 
 
-# Where bf16 rounding is injected in "emulate" mode.
-DEFAULT_RECIPE = {
-    "gate_operands": True,   # exp-scaled operands of A and M
-    "k_q_tilde": True,       # K*exp(G), Q*exp(G) as matrix operands
-    "state_operand": True,   # S0 as matrix operand (X and O)
-    "n_matrix": True,        # N = T - I
-    "y_operand": True,       # Y in N Y (identity part stays fp32)
-    "m_matrix": True,        # M
-    "u_operand_out": True,   # U in M U
-    "khat": "hilo",          # "hilo" | "bf16" | "exact": K*exp(G_c - G) in the state update
-    "u_state": "hilo",       # "hilo" | "bf16" | "exact": U in the state update
-}
+def f16(x):
+    """Round to fp16 (nearest even, with subnormals) and return as float32."""
+    return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
 
 
-def _op(x, on, dt):
-    return bf16(x) if on else x.astype(dt)
+def _parts(x, mode, dt):
+    """x as the list of matrix-core operands a mode feeds: one rounded copy,
+    or a hi + lo pair (lo = the rounding remainder, rounded again)."""
+    x = np.asarray(x, dt)
+    if mode == "exact":
+        return [x]
+    if mode in ("bf16", "fp16"):
+        return [(bf16 if mode == "bf16" else f16)(x)]
+    if mode in ("bf16hl", "fp16hl"):
+        rnd = bf16 if mode == "bf16hl" else f16
+        hi = rnd(x)
+        return [hi, rnd(x.astype(np.float32) - hi)]
+    raise ValueError(mode)
 
 
-def _mm_split(a, b, mode_a, mode_b, dt):
-    """a @ b with a / b given as hi+lo bf16 pairs, plain bf16, or exact."""
-    def parts(x, mode):
-        if mode == "hilo":
-            return list(split_hi_lo(x))
-        if mode == "bf16":
-            return [bf16(x)]
-        return [x.astype(dt)]
-    pa, pb = parts(a, mode_a), parts(b, mode_b)
+def _mm(a, b, modes, dt):
+    """a @ b with each operand rounded as its mode says; of the hi/lo cross
+    terms only lo x lo is dropped (as on the matrix cores)."""
+    pa, pb = _parts(a, modes[0], dt), _parts(b, modes[1], dt)
     out = pa[0] @ pb[0]
     if len(pb) > 1:
         out = out + pa[0] @ pb[1]
@@ -78,27 +77,95 @@ def _mm_split(a, b, mode_a, mode_b, dt):
     return out
 
 
-def _state_update(khat, U, rc, dt):
-    """khat^T U with the recipe's rounding; "hilo_lastN" splits only the last N
-    rows of khat (the least-decayed ones) into hi+lo."""
-    mode = rc["khat"]
-    if isinstance(mode, str) and mode.startswith("hilo_last"):
-        n = int(mode[len("hilo_last"):])
-        c = khat.shape[0]
-        lo_rows = max(c - n, 0)
-        hi, lo = split_hi_lo(khat)
-        lo[:lo_rows] = 0
-        return _mm_split(hi.T, U, "exact", rc["u_state"], dt) + _mm_split(lo.T, U, "exact", "bf16", dt)
-    return _mm_split(khat.T, U, mode, rc["u_state"], dt)
+# Where rounding is injected in "emulate" mode: the operand rounding of each
+# matrix product, as (left, right) modes.
+#   a_off / m_off    gated K K^T / Q K^T, blocks left of the diagonal block
+#                    (both factors <= 1)
+#   a_diag / m_diag  their diagonal 16-row blocks (right factor up to e^80)
+#   x    K~ S            o1   Q~ S             ny   N Y
+#   o2   M U             su   K^^T U (the state update)
+# scale_cols: the state, V and everything derived from them are fed to the
+# matrix cores multiplied by a power of two 2^s shared by groups of this many
+# columns (one wave's columns); s is kept across segments and reset when the
+# scaled magnitude leaves [2^2, 2^6] (0: no scaling).
+KERNEL_RECIPE = {
+    "a_off": ("fp16", "fp16"), "a_diag": ("bf16hl", "bf16hl"),
+    "m_off": ("fp16", "fp16"), "m_diag": ("bf16hl", "bf16hl"),
+    "x": ("fp16", "fp16"), "o1": ("fp16", "fp16"), "ny": ("fp16", "fp16"),
+    "o2": ("fp16", "fp16"), "su": ("fp16", "fp16hl"),
+    "scale_cols": 16, "fold_scale": False, "solve": "exact",
+}
+# The one-launch schedule: the same operands; its triangular solve merges the
+# diagonal 16 x 16 inverses with fp16 matrix products.
+FUSED_RECIPE = dict(KERNEL_RECIPE, solve="merge_fp16")
+# The recipe the kernels used before: bf16 operands throughout, U hi + lo into
+# M U and the state update, the last 16 rows of K^ hi + lo, the diagonal
+# blocks of M hi + lo, the read-out scale folded into Q~ and M (the two-launch
+# schedule's exact solve; the one-launch schedule merged with bf16 products).
+BF16_RECIPE = {
+    "a_off": ("bf16", "bf16"), "a_diag": ("bf16", "bf16"),
+    "m_off": ("bf16", "bf16"), "m_diag": ("bf16hl", "bf16hl"),
+    "x": ("bf16", "bf16"), "o1": ("bf16", "bf16"), "ny": ("bf16", "bf16"),
+    "o2": ("bf16", "bf16hl"), "su": ("bf16hl_last16", "bf16hl"),
+    "scale_cols": 0, "fold_scale": True, "solve": "exact",
+}
+SCALE_LO, SCALE_HI, SCALE_MID = 2.0, 6.0, 4
 
 
-def chunk_step(S, q, k, v, g, beta, scale, C_end=None, *, emulate=False, recipe=None):
+def _state_update(khat, U, mode, dt):
+    """khat^T U; "bf16hl_last16" rounds khat to bf16 and adds the lo part of
+    its last 16 rows only."""
+    if mode[0] == "bf16hl_last16":
+        hi = bf16(khat)
+        lo = bf16(np.asarray(khat, np.float32) - hi)
+        lo[:max(khat.shape[0] - 16, 0)] = 0
+        return _mm(hi.T, U, ("exact", mode[1]), dt) + _mm(lo.T, U, ("exact", "bf16"), dt)
+    return _mm(khat.T, U, mode, dt)
+
+
+def _solve_merge(Lm, rnd):
+    """(I + L)^-1 the way the one-launch schedule forms it: the four 16 x 16
+    diagonal blocks inverted in fp32, then block merges on the matrix cores
+    with rounded operands (rnd) and fp32 accumulation:
+      T10 = -T11 (L10 T00),  T32 = -T33 (L32 T22),
+      T[32:64, 0:32] = -T[32:64, 32:64] (L[32:64, 0:32] T[0:32, 0:32])."""
+    f = np.float32
+    T = np.zeros((64, 64), f)
+    for i in range(4):
+        b = slice(16 * i, 16 * i + 16)
+        T[b, b] = np.linalg.inv(np.eye(16) + Lm[b, b].astype(np.float64)).astype(f)
+    for i, j in ((1, 0), (3, 2)):
+        bi, bj = slice(16 * i, 16 * i + 16), slice(16 * j, 16 * j + 16)
+        P = rnd(Lm[bi, bj]) @ rnd(T[bj, bj])
+        T[bi, bj] = -(rnd(T[bi, bi]) @ rnd(P))
+    Q = rnd(Lm[32:64, 0:32]) @ rnd(T[0:32, 0:32])
+    T[32:64, 0:32] = -(rnd(T[32:64, 32:64]) @ rnd(Q))
+    return T
+
+
+def _update_scale(s, S, v, cols):
+    """Per group of `cols` columns: keep the exponent s while the scaled
+    magnitude max(|S|, |V|) 2^s stays in [2^2, 2^6] (or is zero), else reset
+    it so that the magnitude lands in [2^4, 2^5)."""
+    s = s.copy()
+    for c0 in range(0, S.shape[1], cols):
+        sl = slice(c0, c0 + cols)
+        m = max(float(np.max(np.abs(S[:, sl]), initial=0.0)), float(np.max(np.abs(v[:, sl]), initial=0.0)))
+        ms = m * 2.0 ** s[c0]
+        if m > 0 and (ms > 2.0 ** SCALE_HI or ms < 2.0 ** SCALE_LO):
+            s[sl] = SCALE_MID - np.floor(np.log2(m))
+    return s
+
+
+def chunk_step(S, q, k, v, g, beta, scale, C_end=None, *, emulate=False, recipe=None, sexp=None):
     """One chunk from state S.  q,k [c,K] v [c,V] g [c,K] beta [c].
 
     Returns (O [c,V], S_new, U).  With C_end = p < c also returns the state
     after the first p rows as a fourth value (the masked partial update).
+    In emulate mode with a scaling recipe, `sexp` holds the per-column scale
+    exponents carried between chunks (updated in place).
     """
-    rc = recipe or DEFAULT_RECIPE
+    rc = recipe or KERNEL_RECIPE
     dt = np.float32 if emulate else np.float64
     c, K = k.shape
     S = S.astype(dt)
@@ -107,48 +174,53 @@ def chunk_step(S, q, k, v, g, beta, scale, C_end=None, *, emulate=False, recipe=
     G = np.cumsum(g, axis=0, dtype=dt)
     nb = (c + SUB - 1) // SUB
     refs = [np.zeros(K, dt)] + [G[SUB * i - 1] for i in range(1, nb)]
+    fold = emulate and rc["fold_scale"]
+    qs = q * scale if fold else q
     A = np.zeros((c, c), dt)
     M = np.zeros((c, c), dt)
     for i in range(nb):
         r0, r1 = SUB * i, min(SUB * (i + 1), c)
         lf = np.exp(G[r0:r1] - refs[i])
         rf = np.exp(refs[i] - G[:r1])
-        kl, ql, kr = k[r0:r1] * lf, q[r0:r1] * lf, k[:r1] * rf
-        gm = rc["gate_operands"] if emulate else False
-        if gm is True or gm == "bf16":
-            A[r0:r1, :r1] = bf16(kl) @ bf16(kr).T
-            M[r0:r1, :r1] = bf16(ql) @ bf16(kr).T
-        elif gm == "diag_hilo":
-            # earlier blocks: plain bf16; the block's own rows: hi+lo
-            A[r0:r1, :r1] = bf16(kl) @ bf16(kr).T
-            M[r0:r1, :r0] = bf16(ql) @ bf16(kr[:r0]).T
-            M[r0:r1, r0:r1] = _mm_split(ql, kr[r0:r1].T, "hilo", "hilo", dt)
-        elif gm == "hilo":
-            A[r0:r1, :r1] = bf16(kl) @ bf16(kr).T
-            M[r0:r1, :r1] = _mm_split(ql, kr.T, "hilo", "hilo", dt)
+        kl, ql, kr = k[r0:r1] * lf, qs[r0:r1] * lf, k[:r1] * rf
+        if emulate:
+            if r0 > 0:
+                A[r0:r1, :r0] = _mm(kl, kr[:r0].T, rc["a_off"], dt)
+                M[r0:r1, :r0] = _mm(ql, kr[:r0].T, rc["m_off"], dt)
+            A[r0:r1, r0:r1] = _mm(kl, kr[r0:r1].T, rc["a_diag"], dt)
+            M[r0:r1, r0:r1] = _mm(ql, kr[r0:r1].T, rc["m_diag"], dt)
         else:
             A[r0:r1, :r1] = kl @ kr.T
             M[r0:r1, :r1] = ql @ kr.T
     A = np.tril(A, -1)
     M = np.tril(M, 0)
     Lm = beta[:, None] * A
-    T = np.linalg.inv(np.eye(c, dtype=dt) + Lm) if not emulate else \
-        np.linalg.inv((np.eye(c) + Lm.astype(np.float64))).astype(dt)
+    if not emulate:
+        T = np.linalg.inv(np.eye(c, dtype=dt) + Lm)
+    elif rc.get("solve", "exact") != "exact" and c == 64:
+        T = _solve_merge(Lm, f16 if rc["solve"] == "merge_fp16" else bf16)
+    else:
+        T = np.linalg.inv((np.eye(c) + Lm.astype(np.float64))).astype(dt)
     Nm = np.tril(T, -1)
     eG = np.exp(G)
-    kt, qt = k * eG, q * eG
+    kt, qt = k * eG, qs * eG
     khat = k * np.exp(G[c - 1] - G)
     gam = np.exp(G[c - 1])
     if emulate:
-        S_op = _op(S, rc["state_operand"], dt)
-        X = v - _op(kt, rc["k_q_tilde"], dt) @ S_op
-        Y = beta[:, None] * X
-        U = Y + _op(Nm, rc["n_matrix"], dt) @ _op(Y, rc["y_operand"], dt)
-        mu_m = rc["m_matrix"] if isinstance(rc["m_matrix"], str) else ("bf16" if rc["m_matrix"] else "exact")
-        mu_u = rc["u_operand_out"] if isinstance(rc["u_operand_out"], str) else \
-            ("bf16" if rc["u_operand_out"] else "exact")
-        O = scale * (_op(qt, rc["k_q_tilde"], dt) @ S_op + _mm_split(M, U, mu_m, mu_u, dt))
-        S_new = gam[:, None] * S + _state_update(khat, U, rc, dt)
+        # the state, V and what derives from them go to the matrix cores
+        # multiplied by 2^s per column (exact: a power of two)
+        sig = np.ones(S.shape[1], dt)
+        if rc["scale_cols"]:
+            sexp[:] = _update_scale(sexp, S, v, rc["scale_cols"])
+            sig = (2.0 ** sexp).astype(dt)
+        Ss, vs = S * sig, v * sig
+        X = _mm(kt, Ss, rc["x"], dt)
+        Y = beta[:, None] * (vs - X)
+        U = Y + _mm(Nm, Y, rc["ny"], dt)
+        O = _mm(qt, Ss, rc["o1"], dt) + _mm(M, U, rc["o2"], dt)
+        O = O / sig if fold else O * (scale / sig)
+        S_new = gam[:, None] * S + _state_update(khat, U, rc["su"], dt) / sig
+        U = U / sig
     else:
         X = v - kt @ S
         Y = beta[:, None] * X
@@ -163,7 +235,7 @@ def chunk_step(S, q, k, v, g, beta, scale, C_end=None, *, emulate=False, recipe=
     mask = (np.arange(c) < p)[:, None]
     khat_p = np.where(mask, k * np.exp(G[p - 1] - G), 0)
     if emulate:
-        S_p = np.exp(G[p - 1])[:, None] * S + _state_update(khat_p, U, rc, dt)
+        S_p = np.exp(G[p - 1])[:, None] * S + _state_update(khat_p, U * sig, rc["su"], dt) / sig
     else:
         S_p = np.exp(G[p - 1])[:, None] * S + khat_p.T @ U
     return O, S_new, U, S_p
@@ -195,13 +267,15 @@ def prefill(q, k, v, g, beta, *, scale, cu_seqlens, initial_state=None, ckpt_off
             cuts = sorted(cuts + [p])
         for h in range(H):
             S = np.zeros((K, V), dt) if initial_state is None else initial_state[n, h].astype(dt)
+            sexp = np.zeros(V)   # per-column operand scale exponents (emulate mode)
             if p == 0:
                 ck[n, h] = S
             for c0, c1 in zip(cuts[:-1], cuts[1:]):
                 sl = slice(bos + c0, bos + c1)
                 want = ckpt_mode == "masked" and p is not None and c0 < p < c1
                 res = chunk_step(S, q[sl, h], k[sl, h], v[sl, h], g[sl, h], beta[sl, h], scale,
-                                 C_end=(p - c0) if want else None, emulate=emulate, recipe=recipe)
+                                 C_end=(p - c0) if want else None, emulate=emulate, recipe=recipe,
+                                 sexp=sexp)
                 out[sl, h] = res[0]
                 if want:
                     ck[n, h] = res[3]

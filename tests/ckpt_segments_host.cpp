@@ -1,5 +1,5 @@
-// Host build of the segment-boundary helpers (kda_ckpt.h) for
-// tests/test_ckpt_segments.py.
+// Host build of the segment-boundary and sequence-range helpers (kda_ckpt.h)
+// for tests/test_ckpt_segments.py.
 #include "kda_ckpt.h"
 
 extern "C" int kda_test_segments(const int32_t* offs, int C, int len, int* lo_hi, int cap) {
@@ -32,4 +32,8 @@ extern "C" int kda_test_honoured(const int32_t* offs, int C, int len, int* mask)
     ++n;
   });
   return n;
+}
+
+extern "C" void kda_test_seq_range(int64_t b, int64_t e, int64_t T_total, int64_t* bos_len) {
+  kda::clamp_seq_range(b, e, T_total, &bos_len[0], &bos_len[1]);
 }

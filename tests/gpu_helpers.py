@@ -102,14 +102,68 @@ def metrics(gpu, ref):
     return m
 
 
-def assert_parity(gpu, ref, what=""):
+def _worst_state_pair(g, r):
+    """Largest relative L2 over the (sequence[, checkpoint], head) blocks of
+    states shaped [..., 128, 128]; reference blocks holding NaN (nothing
+    exported there) are skipped.  Returns (error, index)."""
+    g = np.asarray(g, np.float64).reshape(-1, 128 * 128)
+    r = np.asarray(r, np.float64).reshape(-1, 128 * 128)
+    worst, where = 0.0, None
+    for i in range(r.shape[0]):
+        if np.isnan(r[i]).any():
+            continue
+        e = rel_l2(g[i], r[i])
+        if not e <= worst:      # NaN counts as the worst
+            worst, where = e, i
+    return worst, where
+
+
+def pair_metrics(gpu, ref, cu_seqlens=None):
+    """Worst figures over the (sequence, head) pairs: the state's relative L2
+    (final, and each exported checkpoint), and, when cu_seqlens is given, the
+    output's relative L2 of each sequence and head.  One pair off by 5e-3
+    among B8 H12's 96 would show as about 5e-4 over the whole tensor; here it
+    shows as itself."""
+    H = gpu["final"].shape[1]
+    m = {}
+    e, i = _worst_state_pair(gpu["final"], ref["final"])
+    m["worst_final_rel_l2"] = e
+    m["worst_final_pair"] = None if i is None else divmod(i, H)
+    if ref.get("ckpt") is not None and gpu.get("ckpt") is not None:
+        e, i = _worst_state_pair(gpu["ckpt"], ref["ckpt"])
+        m["worst_ckpt_rel_l2"] = e
+        m["worst_ckpt_pair"] = None if i is None else divmod(i, H)
+    if cu_seqlens is not None:
+        worst, where = 0.0, None
+        for n in range(len(cu_seqlens) - 1):
+            b, e_ = int(cu_seqlens[n]), int(cu_seqlens[n + 1])
+            if e_ <= b:
+                continue
+            for h in range(H):
+                err = rel_l2(gpu["out"][b:e_, h], ref["out"][b:e_, h])
+                if not err <= worst:
+                    worst, where = err, (n, h)
+        m["worst_out_rel_l2"] = worst
+        m["worst_out_pair"] = where
+    return m
+
+
+def assert_parity(gpu, ref, what="", cu_seqlens=None):
+    """Gates over the whole tensors and per (sequence, head) pair: output
+    max-abs <= 2e-2 and relative L2 <= 5e-3 (per pair when cu_seqlens is
+    given), final and checkpoint state relative L2 <= 1e-3 for every pair."""
     assert np.all(np.isfinite(gpu["out"])), f"{what}: non-finite or unwritten outputs"
     assert np.all(np.isfinite(gpu["final"])), f"{what}: non-finite or unwritten final state"
     m = metrics(gpu, ref)
+    m.update(pair_metrics(gpu, ref, cu_seqlens))
     assert m["out_max_abs"] <= OUT_MAX_ABS, f"{what}: {m}"
     assert m["out_rel_l2"] <= OUT_REL_L2, f"{what}: {m}"
     assert m["final_rel_l2"] <= STATE_REL_L2, f"{what}: {m}"
+    assert m["worst_final_rel_l2"] <= STATE_REL_L2, f"{what}: {m}"
+    if cu_seqlens is not None:
+        assert m["worst_out_rel_l2"] <= OUT_REL_L2, f"{what}: {m}"
     if "ckpt_rel_l2" in m:
-        assert np.all(np.isfinite(gpu["ckpt"])), f"{what}: unwritten checkpoint"
+        assert np.all(np.isfinite(gpu["ckpt"][np.isfinite(ref["ckpt"])])), f"{what}: unwritten checkpoint"
         assert m["ckpt_rel_l2"] <= STATE_REL_L2, f"{what}: {m}"
+        assert m["worst_ckpt_rel_l2"] <= STATE_REL_L2, f"{what}: {m}"
     return m

@@ -147,9 +147,9 @@ def test_prefill_rejects_on_the_host_without_a_device():
 
 def decomp_bytes(N, T, H, C=1):
     """The documented workspace formula: 2 N + 1 int32 rounded up to 256
-    bytes, then 64,512 bytes per (segment slot, head) for floor(T / 64) + N +
+    bytes, then 60,416 bytes per (segment slot, head) for floor(T / 64) + N +
     N C slots (C checkpoint offsets per sequence, at least 1)."""
-    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + N + N * max(C, 1)) * H * 64512
+    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + N + N * max(C, 1)) * H * 60416
 
 
 def test_workspace_grows_with_checkpoints_per_sequence():

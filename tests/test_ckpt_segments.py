@@ -78,3 +78,25 @@ def test_random(lib):
         assert s == segs, (offs, L)
         assert ends == [b for _, b in segs], (offs, L)
         assert all(0 < b - a <= 64 for a, b in segs)
+
+
+def test_sequence_range_stays_inside_the_tensors(lib):
+    # cu_seqlens that break the contract (negative, past T_total, decreasing)
+    # give a shorter or empty range inside [0, T_total], never one outside;
+    # well-formed entries pass through unchanged
+    out = np.zeros(2, np.int64)
+    P = ctypes.c_void_p
+    f = lib.kda_test_seq_range
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
+    rng = np.random.default_rng(4)
+    for _ in range(2000):
+        T = int(rng.integers(0, 1000))
+        b, e = (int(x) for x in rng.integers(-50, T + 50, size=2))
+        f(b, e, T, P(out.ctypes.data))
+        bos, ln = int(out[0]), int(out[1])
+        assert 0 <= bos <= T and 0 <= ln and bos + ln <= T, (b, e, T, bos, ln)
+        if 0 <= b <= e <= T:
+            assert (bos, ln) == (b, e - b)
+        else:
+            # the clamped range is the part of [b, e) inside [0, T] (empty when there is none)
+            assert bos == min(max(b, 0), T) and ln == max(min(e, T) - bos, 0), (b, e, T)

@@ -75,8 +75,11 @@ def _check(p, pool, idx, T, gout, gpool, what, **prologue):
     return ref
 
 
+# the last shape is the size the decode bench line is measured at (1024
+# requests x 12 heads, one token, a pool of 1100 entries)
 @pytest.mark.parametrize("N,T,H,P,empty", [(1, 1, 1, 1, 0), (37, 1, 3, 50, 5), (8, 4, 12, 9, 1),
-                                           (5, 7, 2, 5, 0), (256, 1, 12, 300, 16)])
+                                           (5, 7, 2, 5, 0), (256, 1, 12, 300, 16),
+                                           (1024, 1, 12, 1100, 32)])
 def test_decode_matches_oracle(N, T, H, P, empty):
     p, pool, idx = _case(N, T, H, P, seed=100 + N + T, empty=empty)
     gout, gpool = _run(p, pool, idx, T)

@@ -16,14 +16,15 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import assert_parity, metrics, rel_l2, run_gpu, to_device
+from gpu_helpers import assert_parity, metrics, pair_metrics, rel_l2, run_gpu, to_device
 from kda_gated_delta_chunked_amd import synth
 
 pytestmark = pytest.mark.gpu
 
 
 def _report(name, m):
-    print(f"[parity] {name}: " + " ".join(f"{k}={v:.3e}" for k, v in m.items()), flush=True)
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}"
+                                         for k, v in m.items()), flush=True)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,7 +59,7 @@ def test_tails_fixed(T, variant):
     p = synth.make_problem([T, T], 2, seed=100 + T, fixed=True, init_state=True)
     ref = oracle.prefill_problem(p)
     gpu = run_gpu(p, variant=variant)
-    _report(f"fixed B2 T{T} {variant}", assert_parity(gpu, ref, f"T={T}"))
+    _report(f"fixed B2 T{T} {variant}", assert_parity(gpu, ref, f"T={T}", p.cu_seqlens))
 
 
 @pytest.mark.parametrize("variant,vsplit", SPLITS)
@@ -68,7 +69,7 @@ def test_packed_ragged_with_empty_and_ckpt(variant, vsplit):
     p = synth.make_problem(lens, 3, seed=7, init_state=True, ckpt=offs)
     ref = oracle.prefill_problem(p)
     gpu = run_gpu(p, variant=variant, value_split=vsplit)
-    _report(f"packed ragged {variant} vs{vsplit}", assert_parity(gpu, ref, "packed"))
+    _report(f"packed ragged {variant} vs{vsplit}", assert_parity(gpu, ref, "packed", p.cu_seqlens))
     # zero-length sequences keep the initial state bit for bit; offset 0 exports it
     for n, L in enumerate(lens):
         if L == 0:
@@ -115,24 +116,62 @@ def test_gate_extremes_and_beta_zero(variant):
     # g at the lower bound (-5): everything decays fast, normal gates apply
     p = synth.make_problem([300, 70], 2, seed=11, init_state=True, gate="min")
     ref = oracle.prefill_problem(p)
-    _report(f"gate=min {variant}", assert_parity(run_gpu(p, variant=variant), ref, "gate=min"))
-    # g = 0: nothing decays, so the bf16 rounding of the state operand in
-    # V - K exp(G) S, of N and of Y accumulates over all 370 tokens instead of
-    # being forgotten.  The rounding model of the kernel (tests/chunked_model.py,
-    # emulate=True with the kernel's recipe) predicts a final-state relative L2
-    # of 9.85e-4 on this input; the bound for this degenerate gate is 2e-3.
+    _report(f"gate=min {variant}", assert_parity(run_gpu(p, variant=variant), ref, "gate=min",
+                                                 p.cu_seqlens))
+    # g = 0 (inside the bound [-5, 0], which includes 0): nothing decays, so
+    # every rounding that reaches the state stays in it; the normal gates apply
     p = synth.make_problem([300, 70], 2, seed=11, init_state=True, gate="zero")
     ref = oracle.prefill_problem(p)
-    gpu = run_gpu(p, variant=variant)
-    m = metrics(gpu, ref)
-    _report(f"gate=zero {variant}", m)
-    assert m["out_rel_l2"] <= 5e-3 and m["out_max_abs"] <= 2e-2 and m["final_rel_l2"] <= 2e-3, m
+    _report(f"gate=zero {variant}", assert_parity(run_gpu(p, variant=variant), ref, "gate=zero",
+                                                  p.cu_seqlens))
     # beta = 0 and g = 0: the state must come back unchanged, bit for bit
     p = synth.make_problem([150], 2, seed=12, init_state=True, gate="zero", beta_mode="zero")
     gpu = run_gpu(p, variant=variant)
     assert np.array_equal(gpu["final"], p.initial_state)
     ref = oracle.prefill_problem(p)
     assert_parity(gpu, ref, "beta=0")
+
+
+def _slow_decay(p, kind, seed):
+    """Replace the gate by a slowly decaying one: "zero" (g = 0), "weak"
+    (uniform in (-0.02, 0]) or "skew" (a per-channel rate log-uniform in
+    [1e-4, 5], times a per-token factor in [0.5, 1])."""
+    rng = np.random.default_rng(seed)
+    if kind == "zero":
+        p.g = np.zeros_like(p.g)
+    elif kind == "weak":
+        p.g = (-0.02 * rng.random(p.g.shape)).astype(np.float32)
+    else:
+        rate = -np.exp(rng.uniform(np.log(1e-4), np.log(5.0), size=(1,) + p.g.shape[1:]))
+        p.g = np.clip(rate * rng.uniform(0.5, 1.0, size=p.g.shape), -5.0, 0.0).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("kind", ["zero", "weak", "skew"])
+def test_slow_decay_full_length(kind, variant):
+    # B1 T8192 H2 with a gate that forgets slowly or not at all: the state's
+    # rounding is carried over all 128 chunks, and every (sequence, head)
+    # must still meet the 1e-3 state gate (lmdeploy PR #5050, Modification:
+    # FP32 state, gate bound [-5, 0] with 0 included)
+    p = synth.make_problem([8192], 2, seed=31, fixed=True, init_state=True)
+    p = _slow_decay(p, kind, 32)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant=variant)
+    _report(f"slow decay {kind} B1 T8192 {variant}", assert_parity(gpu, ref, f"slow {kind}", p.cu_seqlens))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("kind", ["zero", "weak", "skew"])
+def test_slow_decay_packed_ragged_with_checkpoints(kind, variant):
+    lens = [3000, 0, 1, 2047, 64, 700, 129]
+    offs = [1500, 0, 1, 2000, 64, 350, 65]
+    p = synth.make_problem(lens, 2, seed=33, init_state=True, ckpt=offs)
+    p = _slow_decay(p, kind, 34)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant=variant)
+    _report(f"slow decay {kind} packed {variant}",
+            assert_parity(gpu, ref, f"slow {kind} packed", p.cu_seqlens))
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -152,13 +191,19 @@ def test_deterministic(variant):
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["final"], b["final"])
 
 
+# the pages' six shapes (FlashInfer PR #4633, Performance), the packed and
+# checkpoint workloads, and the packed shapes of FlashInfer PR #4262's B200 table
+FULL_SIZE = ["b1_t512", "b1_t8192", "b8_t1024", "b32_t512", "b6_t8192", "b8_t8192",
+             "packed_8x1024", "packed_32_rand", "ckpt_16_rand", "packed_512x32", "packed_128x8",
+             "mixed_6"]
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("name", ["b1_t8192", "b8_t8192", "packed_32_rand", "ckpt_16_rand",
-                                  "packed_512x32", "packed_128x8", "mixed_6"])
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_full_size_workloads(name, variant):
     p, ref = _workload_ref(name)
     gpu = run_gpu(p, variant=variant)
-    _report(f"{name} {variant}", assert_parity(gpu, ref, name))
+    _report(f"{name} {variant}", assert_parity(gpu, ref, name, p.cu_seqlens))
 
 
 def test_decomp_matches_fused_on_packed_layout_as_separate_runs():
@@ -191,7 +236,7 @@ def _honoured(offs, L):
     return out
 
 
-def _check_multi_ckpt(p, offs, gpu, qk_l2norm=False, beta_logit=False):
+def _check_multi_ckpt(p, offs, gpu, qk_l2norm=False, beta_logit=False, bound=1e-3):
     # each honoured slot holds the state after that many tokens (the oracle
     # run with that one offset); the others keep their NaN sentinel
     for c in range(offs.shape[1]):
@@ -202,8 +247,10 @@ def _check_multi_ckpt(p, offs, gpu, qk_l2norm=False, beta_logit=False):
                              qk_l2norm=qk_l2norm, beta_logit=beta_logit)
         for n, L in enumerate(p.seq_lens):
             if c in _honoured(list(offs[n]), L):
-                err = rel_l2(gpu["ckpt"][n, c], ref["ckpt"][n])
-                assert err <= 1e-3, (n, c, offs[n, c], err)
+                # every head of the exported state
+                for h in range(p.H):
+                    err = rel_l2(gpu["ckpt"][n, c, h], ref["ckpt"][n, h])
+                    assert err <= bound, (n, c, h, offs[n, c], err)
             else:
                 assert np.all(np.isnan(gpu["ckpt"][n, c])), (n, c, offs[n, c])
 
@@ -307,6 +354,44 @@ def test_input_prologue(flags, variant):
     ref = oracle.prefill_problem(p, qk_l2norm=qk, beta_logit=bl)
     gpu = run_gpu(p, variant=variant, qk_l2norm=qk, beta_logit=bl)
     _report(f"prologue qk={qk} logit={bl} {variant}", assert_parity(gpu, ref, "prologue"))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("mode", ["bf16_states", "prologue", "three_checkpoints"])
+def test_full_size_state_variants(mode, variant):
+    # the checkpoint workload at full size (16 sequences of 512..8192 tokens,
+    # H = 12; its workspace is past the Infinity Cache bound, so the prepare
+    # streams it) with BF16 states, with the input prologue (raw q and k, beta
+    # logits), or with three offsets per sequence: the seeded one, a chunk
+    # boundary and the end
+    p0 = synth.workload("ckpt_16_rand")
+    lens = list(p0.seq_lens)
+    if mode == "bf16_states":
+        from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32, f32_from_bf16_bits
+        p0.initial_state = f32_from_bf16_bits(bf16_bits_from_f32(p0.initial_state))
+        ref = oracle.prefill_problem(p0)
+        gpu = run_gpu(p0, variant=variant, state_bf16=True)
+        m = metrics(gpu, ref)
+        m.update(pair_metrics(gpu, ref, p0.cu_seqlens))
+        _report(f"ckpt_16_rand bf16 states {variant}", m)
+        assert np.all(np.isfinite(gpu["out"])) and np.all(np.isfinite(gpu["final"]))
+        assert m["out_max_abs"] <= 2e-2 and m["worst_out_rel_l2"] <= 5e-3, m
+        assert m["worst_final_rel_l2"] <= BF16_STATE_REL_L2, m
+        assert m["worst_ckpt_rel_l2"] <= BF16_STATE_REL_L2, m
+    elif mode == "prologue":
+        p = _raw_inputs(p0, 26)
+        ref = oracle.prefill_problem(p, qk_l2norm=True, beta_logit=True)
+        gpu = run_gpu(p, variant=variant, qk_l2norm=True, beta_logit=True)
+        _report(f"ckpt_16_rand prologue {variant}", assert_parity(gpu, ref, "prologue", p.cu_seqlens))
+    else:
+        offs = np.stack([p0.ckpt_offsets, [64 * (L // 128) for L in lens], lens], axis=1).astype(np.int32)
+        ref = oracle.prefill_problem(p0)
+        p0.ckpt_offsets = offs
+        gpu = run_gpu(p0, variant=variant)
+        _report(f"ckpt_16_rand 3 offsets {variant}",
+                assert_parity({"out": gpu["out"], "final": gpu["final"]},
+                              {"out": ref["out"], "final": ref["final"]}, "3 offsets", p0.cu_seqlens))
+        _check_multi_ckpt(p0, offs, gpu)
 
 
 ORDER_CASES = {
@@ -466,7 +551,7 @@ def test_random_problems(seed):
     gpu = run_gpu(p, variant=variant, value_split=vs, qk_l2norm=qk, beta_logit=bl)
     what = (f"seed {seed}: lens {list(p.seq_lens)} H {p.H} {variant} vs{vs} "
             f"C {0 if offs is None else offs.shape[1]} prologue {int(qk)}{int(bl)}")
-    assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref, what)
+    assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref, what, p.cu_seqlens)
     if offs is not None:
         _check_multi_ckpt(p, offs, gpu, qk_l2norm=qk, beta_logit=bl)
 
