@@ -76,7 +76,9 @@ typedef enum {
   KDA_ERR_OVERLAP = -4,          /* buffers overlap other than the allowed exact aliases */
   KDA_ERR_WORKSPACE_TOO_SMALL = -5,
   KDA_ERR_TOO_LARGE = -6,        /* T_total * H * 128 exceeds 2^31 - 1 */
-  KDA_ERR_HIP = -7               /* a HIP runtime call or launch failed */
+  KDA_ERR_HIP = -7,              /* a HIP runtime call or launch failed */
+  KDA_ERR_SCRATCH_TOO_SMALL = -8 /* kda_prefill_noalloc: the problem's workspace exceeds
+                                    KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum {
@@ -172,6 +174,28 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
                        const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
                        float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * prefill as kda_prefill, with the DECOMP workspace taken from a static device
+ * buffer of KDA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends (its device address is looked up on the first
+ * call on each device).  The call allocates nothing.
+ *   - Sizes: a problem whose workspace (kda_prefill_workspace_size) exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_SCRATCH_TOO_SMALL before
+ *     anything is enqueued, unless its variant is KDA_VARIANT_FUSED (no
+ *     workspace).  With AUTO the schedule is the one kda_plan names.
+ *   - Sharing: all calls on one GPU share that GPU's buffer.  It keeps the last
+ *     call's contents, and nothing in it needs to start at zero (the prepare
+ *     launch writes every byte the recurrence reads).  Calls that overlap in
+ *     time on one GPU (two streams, or two threads) race on it; serialise them.
+ *   - Everything else (arguments, errors, aliasing, streams) is as kda_prefill. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+kda_status kda_prefill_noalloc(const kda_problem* p, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const float* g, const float* beta,
+                               const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                               float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
+                               void* stream);
 
 /* ---------------------------------------------------------------------------
  * State-pool decode.  A serving step advances each of N requests by T tokens

@@ -7,8 +7,10 @@ seeded synthetic workloads used by the tests and the benchmark.
 """
 from .ops import (DecodeProblem, KDAError, Problem, decode, decode_raw, decode_validate_raw,
                   load_library, library_path, make_decode_problem, make_problem, periodic_offsets,
-                  plan, prefill, prefill_raw, validate_raw, workspace_size)
+                  plan, prefill, prefill_noalloc_raw, prefill_raw, validate_raw,
+                  workspace_size)
 
 __all__ = ["DecodeProblem", "KDAError", "Problem", "decode", "decode_raw", "decode_validate_raw",
            "load_library", "library_path", "make_decode_problem", "make_problem",
-           "periodic_offsets", "plan", "prefill", "prefill_raw", "validate_raw", "workspace_size"]
+           "periodic_offsets", "plan", "prefill", "prefill_noalloc_raw", "prefill_raw",
+           "validate_raw", "workspace_size"]

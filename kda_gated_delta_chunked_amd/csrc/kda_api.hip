@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_kernels.h"
@@ -151,6 +152,38 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's scratch: the DECOMP workspace lives in a
+// file-scope device array, one copy per GPU, held until the process ends.  In
+// host code `scratch` only names the symbol: its device address (different on
+// every GPU) comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is handed to kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)KDA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+// device address of this GPU's `scratch` (the current device's)
+kda_status scratch_address(void** addr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KDA_ERR_HIP;
+    g_scratch_addr[dev] = ptr;
+  }
+  *addr = g_scratch_addr[dev];
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,6 +198,8 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case KDA_ERR_TOO_LARGE: return "problem exceeds the int32 flat-index bound";
     case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_SCRATCH_TOO_SMALL:
+      return "problem needs more workspace than the allocation-free entry point's static scratch";
   }
   return "unknown status";
 }
@@ -313,6 +348,26 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     err = kda::launch_fused(a, vsplit, st_);
   }
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_prefill_noalloc(const kda_problem* p, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const float* g, const float* beta,
+                               const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                               float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
+                               void* stream) {
+  const kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  // FUSED needs no workspace; AUTO and DECOMP may take the two-launch
+  // schedule, whose workspace must fit the static scratch
+  const size_t need = p->variant == KDA_VARIANT_FUSED ? 0 : decomp_bytes(p);
+  if (need > kNoallocScratchBytes) return KDA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if (need) {
+    const kda_status sa = scratch_address(&ws);
+    if (sa != KDA_OK) return sa;
+  }
+  return kda_prefill(p, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, ckpt_offsets,
+                     ckpt_state, ws, need ? kNoallocScratchBytes : 0, stream);
 }
 
 kda_status kda_decode_validate(const kda_decode_problem* p, const void* q, const void* k,

@@ -17,7 +17,10 @@ from . import build as _build
 KDA_OK = 0
 STATUS_NAMES = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
                 -3: "KDA_ERR_ALIGNMENT", -4: "KDA_ERR_OVERLAP",
-                -5: "KDA_ERR_WORKSPACE_TOO_SMALL", -6: "KDA_ERR_TOO_LARGE", -7: "KDA_ERR_HIP"}
+                -5: "KDA_ERR_WORKSPACE_TOO_SMALL", -6: "KDA_ERR_TOO_LARGE", -7: "KDA_ERR_HIP",
+                -8: "KDA_ERR_SCRATCH_TOO_SMALL"}
+# bytes of the static device scratch kda_prefill_noalloc uses (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 VARIANTS = {"auto": 0, "decomp": 1, "fused": 2}
 HEAD_DIM = 128
 
@@ -122,6 +125,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_validate.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_prefill_noalloc.restype = ctypes.c_int
     lib.kda_plan.argtypes = [PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.kda_plan.restype = ctypes.c_int
     DP = ctypes.POINTER(DecodeProblem)
@@ -163,6 +168,17 @@ def prefill_raw(problem: Problem, q, k, v, g, beta, cu_seqlens, initial_state, o
                            beta or None, cu_seqlens or None, initial_state or None, out or None,
                            final_state or None, ckpt_offsets or None, ckpt_state or None,
                            workspace or None, int(workspace_bytes), stream or None)
+
+
+def prefill_noalloc_raw(problem: Problem, q, k, v, g, beta, cu_seqlens, initial_state, out,
+                        final_state, ckpt_offsets, ckpt_state, stream) -> int:
+    """Call ``kda_prefill_noalloc`` (the workspace is the library's static
+    device scratch) with raw integer pointers (0 for NULL); returns the status."""
+    lib = load_library()
+    return lib.kda_prefill_noalloc(ctypes.byref(problem), q or None, k or None, v or None,
+                                   g or None, beta or None, cu_seqlens or None,
+                                   initial_state or None, out or None, final_state or None,
+                                   ckpt_offsets or None, ckpt_state or None, stream or None)
 
 
 def validate_raw(problem: Problem, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
