@@ -26,14 +26,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill tokens/sec and ms/call, H=12 K=V=128 bf16 at B8 T8192; MFMA util %"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, vendor figure
-# The pages' number for this shape (110-SM SM120, no initial state): 0.881 ms
-PAGES_TOKENS_PER_S = 8 * 8192 / 0.881e-3
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / fp16 matrix, vendor figure
+# Context only (another vendor's part, no initial state): FlashInfer PR #4633,
+# Performance, gives 0.881 ms for this shape on a 110-SM SM120 device.  The
+# stated baseline of this bench is the fp64 oracle (cpu_baseline).
+PAGES_CONTEXT = {"source": "FlashInfer PR #4633, Performance (110-SM SM120, BF16, no initial state)",
+                 "ms": 0.881}
 CSRC = os.path.join(ROOT, "kda_gated_delta_chunked_amd", "csrc")
 KERNEL_SOURCES = {"fused": os.path.join(CSRC, "kda_fused.hip"), "decomp": os.path.join(CSRC, "kda_decomp.hip"),
                   "decode": os.path.join(CSRC, "kda_decode.hip")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-MFMA_FLOPS = 16 * 16 * 32 * 2    # one v_mfma_f32_16x16x32_bf16
+MFMA_FLOPS = 16 * 16 * 32 * 2    # one v_mfma_f32_16x16x32_f16 or _bf16
 
 
 def stage_bytes(p):
@@ -83,16 +86,21 @@ def segments(p) -> int:
     return segs
 
 
-def executed_mfma_flops(p, variant: str, vsplit: int) -> float:
-    """Flops of the v_mfma_f32_16x16x32_bf16 instructions the kernels issue
-    (hi/lo passes included), from their schedules."""
+def modelled_mfma_flops(p, variant: str, vsplit: int) -> float:
+    """Flops of the 16x16x32 MFMA instructions the kernels issue (hi/lo passes
+    included), counted from their schedules (a model: the committed rocprofv3
+    SQ counters give the measured figure).  Per segment and head:
+    * FUSED, per workgroup: 156 for the gate products (4 diagonal blocks x 4
+      key blocks x 6, 6 blocks left of them x 4 x 2) and the solve merges
+      (12), plus 76 per 16-column tile of the recurrence;
+    * DECOMP: the prepare's 176 (4 diagonal blocks x 4 x 6, 6 off-diagonal
+      x 4 x 2, 32 transposes of K^) and the recurrence's 76 per 16 columns,
+      8 column tiles per (sequence, head).  The recurrence's 76: K~ S 16,
+      Q~ S 16, N Y 6, M U 6, K^^T U with U hi + lo 32."""
     segs = segments(p)
     if variant == "fused":
-        # per workgroup and segment: 112 for the gate products, 90 per 16-column tile
-        return float((112 + 90 * (128 // vsplit // 16)) * MFMA_FLOPS) * segs * p.H * vsplit
-    # prepare: 4 diagonal blocks x 16, 6 off-diagonal x 8, 40 transposes of K^;
-    # recurrence: 90 per 16 columns, 8 column tiles per (sequence, head)
-    return float((152 + 8 * 90) * MFMA_FLOPS) * segs * p.H
+        return float((156 + 76 * (128 // vsplit // 16)) * MFMA_FLOPS) * segs * p.H * vsplit
+    return float((176 + 8 * 76) * MFMA_FLOPS) * segs * p.H
 
 
 # headers every kernel source includes: a change there changes the kernel too
@@ -108,18 +116,24 @@ def kernel_sha(variant: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, variant: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel source; else None."""
+def measured_counters(workload: str, variant: str, kernel: str) -> dict:
+    """Per-launch figures of `kernel` from the committed rocprofv3 --pmc
+    summary (HBM bytes, MFMA busy fraction, MFMA flops), if they were taken on
+    the current kernel source; else {}."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     e = t.get(workload, {}).get(kernel)
     if not e or e.get("source_sha256") != kernel_sha(variant):
-        return None
-    return e.get("hbm_bytes_per_launch")
+        return {}
+    return e
+
+
+def measured_traffic(workload: str, variant: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counters, or None."""
+    return measured_counters(workload, variant, kernel).get("hbm_bytes_per_launch")
 
 
 def _cpu_model() -> str:
@@ -404,17 +418,21 @@ def main() -> int:
             "achieved_GBps": round(alg_b / (ms_launch * 1e-3) / 1e9, 1),
             "frac_hbm": round(alg_b / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kernels_ms": {kk: round(e["ms"], 4) for kk, e in kernels.items()}}
-    ex_fl = executed_mfma_flops(p, variant, vsplit)
+    ex_fl = modelled_mfma_flops(p, variant, vsplit)
     alg_fl = algorithmic_flops(p)
-    mfma = {"executed_tflops": round(ex_fl / (ms_launch * 1e-3) / 1e12, 1),
-            "executed_util": round(ex_fl / (ms_launch * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
+    mfma = {"modelled_executed_tflops": round(ex_fl / (ms_launch * 1e-3) / 1e12, 1),
+            "modelled_executed_util": round(ex_fl / (ms_launch * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4),
             "algorithmic_tflops": round(alg_fl / (ms_launch * 1e-3) / 1e12, 1),
-            "algorithmic_util": round(alg_fl / (ms_launch * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
-            "peak_tflops": BF16_MFMA_PEAK_TFLOPS}
+            "algorithmic_util": round(alg_fl / (ms_launch * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4),
+            "peak_tflops": MFMA_PEAK_TFLOPS,
+            # measured by rocprofv3 on the current kernel source (committed
+            # profiles), per kernel: MFMA busy fraction of the SIMD cycles
+            "measured_busy": {kk: measured_counters(args.workload, variant, kk).get("mfma_busy")
+                              for kk in kernels}}
     res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": round(value / PAGES_TOKENS_PER_S, 3) if args.workload == "b8_t8192" else None,
+           "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": args.workload, "B": p.N if p.fixed else None,
                       "T": int(p.seq_lens[0]) if p.fixed else None, "num_seqs": p.N,
@@ -423,6 +441,8 @@ def main() -> int:
                       "checkpoints": p.ckpt_offsets is not None,
                       "variant": variant, "value_split": vsplit},
            "roofline": roof, "path": path, "mfma": mfma, "timing": timing}
+    if args.workload == "b8_t8192":
+        res["context"] = dict(PAGES_CONTEXT, ratio_ms=round(PAGES_CONTEXT["ms"] / ms_step, 3))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)
