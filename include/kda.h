@@ -144,7 +144,12 @@ typedef enum {
 enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
 
 /* Bytes of caller workspace kda_prefill needs for this problem (host only, no
- * device access).  FUSED needs none (0).  DECOMP, and AUTO so that it may
+ * device access).  The two-launch schedule's prepare and recurrence share one
+ * caller-owned scratch arena, which is what makes graph capture possible
+ * (FlashInfer PR #4633, Description: decomp shares a scratch arena between its
+ * two launches; capture goes through a caller-owned workspace).  lmdeploy PR
+ * #5050, Modification, has the backend allocate its workspace; here the caller
+ * does, so that nothing is allocated inside a call.  FUSED needs none (0).  DECOMP, and AUTO so that it may
  * pick DECOMP, need a header of 2 N + 1 int32 rounded up to 256 bytes plus
  * 60,416 bytes per (segment slot, head), with floor(T_total / 64) + N + N C
  * segment slots (C = ckpt_per_seq, at least 1): about 0.94 KiB per
@@ -247,12 +252,20 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
                       const uint16_t* v, const float* g, const float* beta, float* state_pool,
                       const int32_t* state_indices, uint16_t* out, void* stream);
 
-/* Static string for a status code. */
-const char* kda_status_string(kda_status s);
+/* Static string for a status code (a kda_status value; any other int gives
+ * "unknown status").  Errors are reported, never retried or rerouted through
+ * another path (lmdeploy PR #5050, Modification: native execution errors are
+ * propagated), and argument errors are found before anything is enqueued
+ * (same passage: requests fail before any state is touched). */
+const char* kda_status_string(int status);
 
 /* Schedule and workgroups per (sequence, head) kda_prefill would use for this
  * problem on the current device, given a workspace of at least
- * kda_prefill_workspace_size bytes (host only; reads the device's CU count). */
+ * kda_prefill_workspace_size bytes (host only; reads the device's CU count).
+ * The choice comes from a table of measured rows keyed on the compute-unit
+ * count, not on the device's name (FlashInfer PR #4633, Description: neither
+ * the two-launch nor the one-launch kernel is faster everywhere, so a table
+ * keyed on SM count picks per call, and a query reports the choice). */
 kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split);
 
 #ifdef __cplusplus

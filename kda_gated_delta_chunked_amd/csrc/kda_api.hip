@@ -188,8 +188,10 @@ kda_status scratch_address(void** addr) {
 
 extern "C" {
 
-const char* kda_status_string(kda_status s) {
-  switch (s) {
+const char* kda_status_string(int status) {
+  // an int, not the enum: any value may come in, and reading an int that no
+  // enumerator names through the enum type would be undefined in C++
+  switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration";

@@ -1112,6 +1112,11 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     f16x8 Sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) Sb[b] = acc_pair_h(S[2 * b], S[2 * b + 1]);
+    float4 gm[8];
+    if constexpr (BATCHED) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
+    }
     KDA_FENCE();
     // X = K~ S, key blocks 0-1; the rest of K~ is read meanwhile
     f32x4 X[4], O[4];
@@ -1128,6 +1133,21 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     for (int b = 2; b < 4; ++b)
 #pragma unroll
       for (int t = 0; t < 4; ++t) X[t] = mfma(fk[t * 4 + b], Sb[b], X[t]);
+    // the decayed state diag(Gam) S, the state update's accumulator input,
+    // formed while the products run (off the chain of the update; S itself
+    // stays for the scale check).  Without batches (three waves per SIMD,
+    // fewer registers each) it is formed at the update instead.
+    f32x4 Sd[8];
+    auto decay = [&]() {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        Sd[m][0] = S[m][0] * gm[m].x;
+        Sd[m][1] = S[m][1] * gm[m].y;
+        Sd[m][2] = S[m][2] * gm[m].z;
+        Sd[m][3] = S[m][3] * gm[m].w;
+      }
+    };
+    if constexpr (BATCHED) decay();
     KDA_FENCE();
     // the rest of Q~, the V block and N, read while O^T = S^T Q~^T runs
     const int4 hd = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(cur) + SL_HDR - KB);
@@ -1181,7 +1201,10 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) S[m][e] = __builtin_ldexpf(S[m][e], dexp);
+          for (int e = 0; e < 4; ++e) {
+            S[m][e] = __builtin_ldexpf(S[m][e], dexp);
+            if constexpr (BATCHED) Sd[m][e] = __builtin_ldexpf(Sd[m][e], dexp);
+          }
 #pragma unroll
         for (int b = 0; b < 4; ++b) Sb[b] = acc_pair_h(S[2 * b], S[2 * b + 1]);
 #pragma unroll
@@ -1241,12 +1264,9 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
         if (2 * b > t) continue;
         O[t] = mfma(Uh[b], fm[tri_frag(t, b)], O[t]);
       }
-    // second half of K^ and Gam, read while M U runs
+    // second half of K^, read while M U runs
 #pragma unroll
     for (int i = 8; i < 16; ++i) fh[i] = frag(SL_KH + i * 1024);
-    float4 gm[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
     KDA_FENCE();
     // read-out: scale * 2^-s
     const float osc = a.scale * pow2f(-sexp);
@@ -1256,13 +1276,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       opk[2 * t + 1] = pack2(O[t][2] * osc, O[t][3] * osc);
     }
     // S <- diag(Gam) S + K^^T U
+    if constexpr (!BATCHED) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) gm[m] = f4(SL_GAM + (16 * m + 4 * gg) * 4);
+      decay();
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      S[m][0] *= gm[m].x;
-      S[m][1] *= gm[m].y;
-      S[m][2] *= gm[m].z;
-      S[m][3] *= gm[m].w;
-      S[m] = mfma(fh[2 * m], Uh[0], S[m]);
+      S[m] = mfma(fh[2 * m], Uh[0], Sd[m]);
       S[m] = mfma(fh[2 * m], Ul[0], S[m]);
       S[m] = mfma(fh[2 * m + 1], Uh[1], S[m]);
       S[m] = mfma(fh[2 * m + 1], Ul[1], S[m]);

@@ -103,7 +103,9 @@ def periodic_offsets(seq_lens, every: int):
 
 
 def library_path() -> str:
-    return _build.LIB_PATH
+    """The libkda.so to load: $KDA_LIBRARY when set (another build of the same
+    sources, such as one with host sanitizers), else the in-tree build."""
+    return os.environ.get("KDA_LIBRARY") or _build.LIB_PATH
 
 
 def load_library(path: Optional[str] = None):
@@ -111,8 +113,10 @@ def load_library(path: Optional[str] = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or _build.LIB_PATH
+    p = path or library_path()
     if not os.path.exists(p):
+        if p != _build.LIB_PATH:
+            raise OSError(f"libkda not found at {p}")
         _build.build()
     lib = ctypes.CDLL(p)
     P = ctypes.c_void_p

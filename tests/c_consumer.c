@@ -108,6 +108,6 @@ int main(void) {
   d.pool_size = 0;
   printf("decode.empty_pool %d\n", (int)kda_decode_validate(&d, q, k, v, g, beta, s0, (const int32_t*)addr(8), out));
 
-  for (int s = -7; s <= 0; ++s) printf("status.%d %s\n", s, kda_status_string((kda_status)s));
+  for (int s = -8; s <= 0; ++s) printf("status.%d %s\n", s, kda_status_string(s));
   return 0;
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = K.load_library()
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = lib.kda_status_string(code)
         assert s and s != b"unknown status"
     assert lib.kda_status_string(-99) == b"unknown status"

@@ -74,5 +74,5 @@ def test_validation_results_from_c(consumer_output):
 
 def test_status_strings_from_c(consumer_output):
     lib = K.load_library()
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert consumer_output[f"status.{s}"] == lib.kda_status_string(s).decode()
