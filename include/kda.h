@@ -28,8 +28,8 @@
  *   q, k, v        bf16  [T_total, H, 128]
  *   g              fp32  [T_total, H, 128]   lower_bound <= g <= 0
  *   beta           fp32  [T_total, H]
- *   cu_seqlens     int32 [N + 1], or NULL for a fixed batch of N sequences of
- *                  T_total / N tokens.  Contract when given (not checked on the
+ *   cu_seqlens     int32 [N + 1] (int64 with kda_problem.cu_seqlens_int64), or
+ *                  NULL for a fixed batch of N sequences of T_total / N tokens.  Contract when given (not checked on the
  *                  device, as in lmdeploy PR #5050, Modification: offset values
  *                  stay the caller's responsibility so nothing synchronises):
  *                  cu[0] = 0, cu[N] = T_total, non-decreasing.
@@ -84,7 +84,7 @@ typedef enum {
 typedef enum {
   KDA_VARIANT_AUTO = 0,          /* pick the schedule from a table keyed on the CU count and
                                     the shape the host knows (N, H, T_total / N): the one-launch
-                                    schedule for short sequences (a mean of at most 128 tokens)
+                                    schedule for short sequences (a mean of at most 64 tokens)
                                     whose workgroups all fit on the device at once, else the
                                     two-launch schedule when the workspace holds it, with four
                                     workgroups per (sequence, head) when they all fit at once
@@ -125,6 +125,20 @@ typedef struct {
                                 (the BF16 state of FlashInfer PR #4262's benchmark) */
   int32_t prologue;          /* kda_prologue flags, 0 = none: inputs as given.  Both
                                 schedules apply them */
+  int32_t cu_seqlens_int64;  /* 0: cu_seqlens holds int32 offsets; 1: int64 offsets.  Both are
+                                read as they are on the device (FlashInfer PR #4262, Dispatch
+                                contract: packed offsets come as int32 or int64, and a captured
+                                graph takes them with no conversion) */
+  const int32_t* seq_order;  /* packed layout only, optional: device int32 [N], the order in
+                                which the two-launch schedule's recurrence takes the sequences
+                                (FlashInfer PR #4262, Dispatch contract: an optional int32
+                                seq_order orders packed sequences for tail utilisation).  NULL:
+                                longest first (up to 1024 sequences), chosen on the device.  It
+                                must hold a permutation of 0..N-1 with N <= 65536; the plan
+                                launch checks that on the device and takes the identity order
+                                when it does not.  Results do not depend on the order.  The
+                                fixed layout and FUSED (whose workgroups all run at once when
+                                AUTO picks it) do not use it */
 } kda_problem;
 
 /* Input prologue, done in the kernels before anything else reads q, k or
@@ -165,7 +179,7 @@ kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes);
  * (FlashInfer PR #4633, Description: the flat output is bounded on the host).
  * Pointers are compared, never dereferenced, so host addresses may be used. */
 kda_status kda_validate(const kda_problem* p, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const int32_t* cu_seqlens,
+                        const float* g, const float* beta, const void* cu_seqlens,
                         const float* initial_state, const void* out, const float* final_state,
                         const int32_t* ckpt_offsets, const float* ckpt_state,
                         const void* workspace, size_t workspace_bytes);
@@ -176,7 +190,7 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
  * KDA_ERR_HIP, which reports a failed launch. */
 kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, const float* g, const float* beta,
-                       const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                       const void* cu_seqlens, const float* initial_state, uint16_t* out,
                        float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
                        void* workspace, size_t workspace_bytes, void* stream);
 
@@ -198,7 +212,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
 #define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
 kda_status kda_prefill_noalloc(const kda_problem* p, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const float* g, const float* beta,
-                               const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                               const void* cu_seqlens, const float* initial_state, uint16_t* out,
                                float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
                                void* stream);
 

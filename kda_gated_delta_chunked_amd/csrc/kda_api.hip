@@ -61,6 +61,7 @@ kda_status check_problem(const kda_problem* p) {
   if (p->ckpt_per_seq < 0) return KDA_ERR_INVALID_ARG;
   if (p->state_dtype != KDA_STATE_F32 && p->state_dtype != KDA_STATE_BF16) return KDA_ERR_UNSUPPORTED;
   if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
+  if (p->cu_seqlens_int64 != 0 && p->cu_seqlens_int64 != 1) return KDA_ERR_INVALID_ARG;
   if (p->ckpt_per_seq > kMaxCkptPerSeq) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
@@ -112,17 +113,18 @@ int fused_vsplit(const kda_problem* p, int cus) {
 // The schedule table, keyed on the CU count and on what the host knows of the
 // shape (N, H and the mean sequence length T_total / N).  The one-launch
 // schedule wins when all its workgroups run at once (pairs x workgroups per
-// pair <= CUs) and the sequences are short (a mean of at most two 64-token
-// chunks): the per-segment chain is then too short to repay the prepare
+// pair <= CUs) and the sequences are short (a mean of at most one 64-token
+// chunk): the per-segment chain is then too short to repay the prepare
 // launch and its workspace round trip.  Measured on MI355X (256 CUs), H = 12,
-// in us per call, DECOMP / FUSED: B1 T64 26.4 / 18.9, B8 T64 28.6 / 21.7,
-// B8 T128 32.9 / 31.4, packed 8 x 128 30.8 / 25.5; past either bound DECOMP
-// wins: B8 T192 39.2 / 40.7, B16 T128 45.3 / 53.7, B32 T64 49.9 / 52.6.
+// per-sequence initial states, in us per call, DECOMP / FUSED: B1 T64
+// 20.9 / 16.7, B8 T64 22.9 / 19.6; past either bound DECOMP wins or ties:
+// B8 T128 27.6 / 31.8, packed 8 x 128 32.6 / 32.2, B8 T192 34.0 / 43.8,
+// B16 T128 40.6 / 59.5, B32 T64 45.4 / 55.0.
 bool fused_is_faster(const kda_problem* p, int cus) {
   if (cus <= 0 || p->value_split == 1 || p->value_split == 8) return false;
   const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
   const int64_t mean_len = p->total_tokens / p->num_seqs;
-  return mean_len <= 2 * 64 && pairs * fused_vsplit(p, cus) <= cus;
+  return mean_len <= 64 && pairs * fused_vsplit(p, cus) <= cus;
 }
 
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
@@ -215,7 +217,7 @@ kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes) {
 }
 
 kda_status kda_validate(const kda_problem* p, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const int32_t* cu_seqlens,
+                        const float* g, const float* beta, const void* cu_seqlens,
                         const float* initial_state, const void* out, const float* final_state,
                         const int32_t* ckpt_offsets, const float* ckpt_state,
                         const void* workspace, size_t workspace_bytes) {
@@ -226,8 +228,10 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
   if (!cu_seqlens && (T % N) != 0) return KDA_ERR_INVALID_ARG;
   if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
   if ((ckpt_offsets == nullptr) != (ckpt_state == nullptr)) return KDA_ERR_INVALID_ARG;
+  // seq_order orders a packed batch's sequences
+  if (p->seq_order && !cu_seqlens) return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
-                        ckpt_offsets, ckpt_state, workspace};
+                        ckpt_offsets, ckpt_state, workspace, p->seq_order};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
   // DECOMP (named, or implied by a DECOMP-only value_split) needs its
@@ -243,7 +247,8 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
       (uint64_t)N * H * kHeadDim * kHeadDim * (p->state_dtype == KDA_STATE_BF16 ? 2 : 4);
   const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
   const Range rg = range_of(g, tok_f32), rb = range_of(beta, (uint64_t)T * H * 4);
-  const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4);
+  const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * (p->cu_seqlens_int64 ? 8 : 4));
+  const Range rord = range_of(p->seq_order, (uint64_t)N * 4);
   const Range rs0 = range_of(initial_state, state);
   const Range rout = range_of(out, tok_bf16), rfin = range_of(final_state, state);
   const Range roff = range_of(ckpt_offsets, (uint64_t)N * ckpt_count(p) * 4);
@@ -251,18 +256,18 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
   const Range rws = range_of(workspace, workspace_bytes);
 
   // out: may be exactly v; must not touch any other buffer
-  for (const Range& r : {rq, rk, rg, rb, rcu, rs0, rfin, roff, rck, rws})
+  for (const Range& r : {rq, rk, rg, rb, rcu, rs0, rfin, roff, rck, rws, rord})
     if (overlaps(rout, r)) return KDA_ERR_OVERLAP;
   if (overlaps(rout, rv) && !exact(rout, rv)) return KDA_ERR_OVERLAP;
   // final state: may be exactly the initial state
-  for (const Range& r : {rq, rk, rv, rg, rb, rcu, roff, rck, rws})
+  for (const Range& r : {rq, rk, rv, rg, rb, rcu, roff, rck, rws, rord})
     if (overlaps(rfin, r)) return KDA_ERR_OVERLAP;
   if (overlaps(rfin, rs0) && !exact(rfin, rs0)) return KDA_ERR_OVERLAP;
   // checkpoint buffer: no overlap with anything
-  for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff, rws})
+  for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff, rws, rord})
     if (overlaps(rck, r)) return KDA_ERR_OVERLAP;
   // workspace: written by the call, so it overlaps no other buffer either
-  for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff})
+  for (const Range& r : {rq, rk, rv, rg, rb, rcu, rs0, roff, rord})
     if (overlaps(rws, r)) return KDA_ERR_OVERLAP;
   return KDA_OK;
 }
@@ -277,7 +282,7 @@ kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split
 
 kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, const float* g, const float* beta,
-                       const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                       const void* cu_seqlens, const float* initial_state, uint16_t* out,
                        float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
                        void* workspace, size_t workspace_bytes, void* stream) {
   const kda_status st = kda_validate(p, q, k, v, g, beta, cu_seqlens, initial_state, out,
@@ -300,6 +305,8 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.g = g;
     a.beta = beta;
     a.cu_seqlens = cu_seqlens;
+    a.cu64 = p->cu_seqlens_int64;
+    a.seq_order = p->seq_order;
     a.s0 = initial_state;
     a.out = out;
     a.final_state = final_state;
@@ -333,6 +340,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.g = g;
     a.beta = beta;
     a.cu_seqlens = cu_seqlens;
+    a.cu64 = p->cu_seqlens_int64;
     a.s0 = initial_state;
     a.out = out;
     a.final_state = final_state;
@@ -354,7 +362,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
 
 kda_status kda_prefill_noalloc(const kda_problem* p, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const float* g, const float* beta,
-                               const int32_t* cu_seqlens, const float* initial_state, uint16_t* out,
+                               const void* cu_seqlens, const float* initial_state, uint16_t* out,
                                float* final_state, const int32_t* ckpt_offsets, float* ckpt_state,
                                void* stream) {
   const kda_status st = check_problem(p);

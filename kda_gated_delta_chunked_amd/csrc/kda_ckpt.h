@@ -35,6 +35,11 @@ __host__ __device__ inline void clamp_seq_range(int64_t b, int64_t e, int64_t T_
   *len = e - b;
 }
 
+// Entry n of cu_seqlens, held as int32 or (cu64) int64.
+__host__ __device__ inline int64_t cu_at(const void* cu, int cu64, int64_t n) {
+  return cu64 ? static_cast<const int64_t*>(cu)[n] : (int64_t)static_cast<const int32_t*>(cu)[n];
+}
+
 // On the device the C <= 64 offsets live one per lane of the wave (lane c
 // holds offset c, read once at kernel start) and are taken out with
 // readlane: the walks below then do no memory access, so they add no wait on

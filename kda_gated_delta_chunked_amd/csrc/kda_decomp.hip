@@ -244,8 +244,8 @@ __device__ __forceinline__ SeqInfo seq_info(const DecompArgs& a, int n) {
   SeqInfo s;
   int64_t b, e;
   if (a.cu_seqlens) {
-    b = a.cu_seqlens[n];
-    e = a.cu_seqlens[n + 1];
+    b = cu_at(a.cu_seqlens, a.cu64, n);
+    e = cu_at(a.cu_seqlens, a.cu64, n + 1);
   } else {
     b = (int64_t)n * a.T_fixed;
     e = b + a.T_fixed;
@@ -270,17 +270,22 @@ __device__ __forceinline__ void seg_range(const SeqInfo& s, int j, int& lo, int&
 // owns ceil(L_n / 64) slots, plus C when C checkpoint offsets per sequence are
 // requested (each may cut a chunk in two).  base[N] is the total.
 //
-// It also writes the order in which the recurrence takes the sequences:
-// longest first (ties by index), so that when there are more workgroups than
-// the device holds at once, the long chains start first and short ones fill
-// the tail.  Up to kOrderMax sequences are ranked; beyond that the order is
-// the identity.
+// It also writes the order in which the recurrence takes the sequences: the
+// caller's seq_order when given and a permutation of 0..N-1 (checked here,
+// for N <= kSeqOrderMax), else longest first (ties by index), so that when
+// there are more workgroups than the device holds at once, the long chains
+// start first and short ones fill the tail.  Up to kOrderMax sequences are
+// ranked; beyond that, and for a seq_order that is no permutation, the order
+// is the identity.
 
 constexpr int kOrderMax = 1024;
+constexpr int kSeqOrderMax = 65536;
 
 __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t nslots[kOrderMax];
+  __shared__ uint32_t seen[kSeqOrderMax / 32];
+  __shared__ int order_bad;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int extra = a.ckpt_off ? a.ckpt_per_seq : 0;
   int64_t carry = 0;
@@ -289,7 +294,8 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
     int cnt = 0;
     if (n < a.N) {
       int64_t b, len;
-      clamp_seq_range(a.cu_seqlens[n], a.cu_seqlens[n + 1], a.T_total, &b, &len);
+      clamp_seq_range(cu_at(a.cu_seqlens, a.cu64, n), cu_at(a.cu_seqlens, a.cu64, n + 1), a.T_total,
+                      &b, &len);
       cnt = (int)((len + CH - 1) / CH) + extra;
     }
     int x = cnt;
@@ -308,12 +314,36 @@ __global__ __launch_bounds__(1024) void kda_plan_kernel(DecompArgs a) {
     }
     if (n < a.N) a.seg_base[n] = (int32_t)(carry + woff + x - cnt);
     if (a.N <= kOrderMax) nslots[t] = cnt;
-    else if (a.order && n < a.N) a.order[n] = n;
     __syncthreads();
     carry += tot;
   }
   if (t == 0) a.seg_base[a.N] = (int32_t)carry;
-  if (a.order && a.N <= kOrderMax && t < a.N) {
+  if (!a.order) return;
+  if (a.seq_order && a.N <= kSeqOrderMax) {
+    // the caller's order, if it names every sequence once: N entries in
+    // [0, N), all distinct
+    for (int i = t; i < (a.N + 31) / 32; i += 1024) seen[i] = 0u;
+    if (t == 0) order_bad = 0;
+    __syncthreads();
+    for (int n = t; n < a.N; n += 1024) {
+      const int x = a.seq_order[n];
+      if (x < 0 || x >= a.N) {
+        order_bad = 1;
+      } else {
+        const uint32_t bit = 1u << (x & 31);
+        if (atomicOr(&seen[x >> 5], bit) & bit) order_bad = 1;
+      }
+    }
+    __syncthreads();
+    const bool ok = order_bad == 0;
+    for (int n = t; n < a.N; n += 1024) a.order[n] = ok ? a.seq_order[n] : n;
+    return;
+  }
+  if (a.N > kOrderMax) {
+    for (int n = t; n < a.N; n += 1024) a.order[n] = n;
+    return;
+  }
+  if (t < a.N) {
     // rank = sequences that come before this one
     const int mine = nslots[t];
     int rank = 0;

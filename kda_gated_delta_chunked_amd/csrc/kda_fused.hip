@@ -265,7 +265,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fused_kernel(FusedArgs a) {
   int64_t bos, len;
   if (a.cu_seqlens) {
     // clamped into [0, T_total] even for offsets that break the contract
-    clamp_seq_range(a.cu_seqlens[n], a.cu_seqlens[n + 1], a.T_total, &bos, &len);
+    clamp_seq_range(cu_at(a.cu_seqlens, a.cu64, n), cu_at(a.cu_seqlens, a.cu64, n + 1), a.T_total, &bos,
+                    &len);
   } else {
     len = a.T_fixed;
     bos = (int64_t)n * len;

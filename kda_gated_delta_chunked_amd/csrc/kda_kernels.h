@@ -25,7 +25,8 @@ struct FusedArgs {
   const uint16_t* v;
   const float* g;
   const float* beta;
-  const int32_t* cu_seqlens;  // NULL: N sequences of T_fixed tokens
+  const void* cu_seqlens;     // int32 or int64 [N + 1] (cu64); NULL: N sequences of T_fixed tokens
+  int cu64;
   const float* s0;            // NULL: zero initial state
   uint16_t* out;
   float* final_state;         // may be NULL
@@ -56,7 +57,9 @@ struct DecompArgs {
   const uint16_t* v;
   const float* g;
   const float* beta;
-  const int32_t* cu_seqlens;  // NULL: N sequences of T_fixed tokens
+  const void* cu_seqlens;     // int32 or int64 [N + 1] (cu64); NULL: N sequences of T_fixed tokens
+  int cu64;
+  const int32_t* seq_order;   // caller's recurrence order (packed layout), or NULL
   const float* s0;            // NULL: zero initial state
   uint16_t* out;
   float* final_state;         // may be NULL

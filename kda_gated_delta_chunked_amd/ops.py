@@ -46,7 +46,8 @@ class Problem(ctypes.Structure):
                 ("gate_lower_bound", ctypes.c_float), ("variant", ctypes.c_int32),
                 ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("ckpt_per_seq", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
-                ("prologue", ctypes.c_int32)]
+                ("prologue", ctypes.c_int32), ("cu_seqlens_int64", ctypes.c_int32),
+                ("seq_order", ctypes.c_void_p)]
 
 
 STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
@@ -77,13 +78,16 @@ def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: flo
                  value_split: int = 0, head_dim_k: int = HEAD_DIM,
                  head_dim_v: int = HEAD_DIM, stages: str | int = "both",
                  ckpt_per_seq: int = 0, state_dtype: str = "fp32", qk_l2norm: bool = False,
-                 beta_logit: bool = False) -> Problem:
+                 beta_logit: bool = False, cu_seqlens_int64: bool = False,
+                 seq_order: int = 0) -> Problem:
+    """Mirror of kda_problem; seq_order is a raw device pointer (0 = none)."""
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     st = STAGES[stages] if isinstance(stages, str) else int(stages)
     return Problem(int(num_seqs), int(total_tokens), int(num_heads), int(head_dim_k),
                    int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st,
                    int(ckpt_per_seq), STATE_DTYPES[state_dtype],
-                   (1 if qk_l2norm else 0) | (2 if beta_logit else 0))
+                   (1 if qk_l2norm else 0) | (2 if beta_logit else 0),
+                   1 if cu_seqlens_int64 else 0, int(seq_order) or None)
 
 
 def periodic_offsets(seq_lens, every: int):
@@ -203,7 +207,7 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
             out=None, final_state=None, output_final_state: bool = True, ckpt_offsets=None,
             ckpt_state=None, gate_lower_bound: float = -5.0, variant: str = "auto",
             value_split: int = 0, workspace=None, stream=None, state_dtype=None,
-            qk_l2norm: bool = False, beta_logit: bool = False):
+            qk_l2norm: bool = False, beta_logit: bool = False, seq_order=None):
     """KDA multi-token recurrent prefill on the GPU.
 
     q, k, v: bf16 [T, H, 128] (packed, with cu_seqlens int32 [N+1]) or
@@ -220,6 +224,9 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
     sequence (``periodic_offsets`` builds a checkpoint every n tokens).
     workspace: a device buffer of at least ``workspace_size`` bytes; when None
     and the schedule may use one, a buffer is taken from torch's allocator.
+    cu_seqlens may be int32 or int64.  seq_order: optional int32 [N], the
+    order in which the recurrence takes packed sequences (a permutation; see
+    kda_problem.seq_order).
     """
     import torch
 
@@ -259,7 +266,9 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
         state_dtype = torch.bfloat16 if given and given[0].dtype == torch.bfloat16 else torch.float32
     if state_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("states must be float32 or bfloat16")
-    for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int32), ("initial_state", initial_state,
+    cu64 = cu_seqlens is not None and cu_seqlens.dtype == torch.int64
+    for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int64 if cu64 else torch.int32),
+                        ("seq_order", seq_order, torch.int32), ("initial_state", initial_state,
                         state_dtype), ("ckpt_offsets", ckpt_offsets, torch.int32),
                         ("ckpt_state", ckpt_state, state_dtype), ("out", out, torch.bfloat16),
                         ("final_state", final_state, state_dtype)):
@@ -288,7 +297,10 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
                         variant=variant, value_split=value_split, head_dim_k=D, head_dim_v=D,
                         ckpt_per_seq=C,
                         state_dtype="bf16" if state_dtype == torch.bfloat16 else "fp32",
-                        qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+                        qk_l2norm=qk_l2norm, beta_logit=beta_logit, cu_seqlens_int64=cu64,
+                        seq_order=_ptr(seq_order))
+    if seq_order is not None and tuple(seq_order.shape) != (N,):
+        raise ValueError(f"seq_order must be [{N}]")
     out_given, final_given = out, final_state
     if out is None:
         out = torch.empty_like(v)

@@ -46,6 +46,8 @@ int main(void) {
   FIELD(kda_problem, ckpt_per_seq);
   FIELD(kda_problem, state_dtype);
   FIELD(kda_problem, prologue);
+  FIELD(kda_problem, cu_seqlens_int64);
+  FIELD(kda_problem, seq_order);
   printf("sizeof.kda_decode_problem %zu\n", sizeof(kda_decode_problem));
   FIELD(kda_decode_problem, num_seqs);
   FIELD(kda_decode_problem, tokens_per_seq);

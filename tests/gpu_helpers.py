@@ -32,7 +32,7 @@ def to_device(p: synth.Problem):
 def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=None,
             sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False,
             keep_workspace: bool = False, state_bf16: bool = False, qk_l2norm: bool = False,
-            beta_logit: bool = False):
+            beta_logit: bool = False, cu64: bool = False, seq_order=None):
     """Run kda_prefill through the C ABI on a fresh set of device buffers.
 
     Outputs are pre-filled with NaN so that any element the kernel fails to
@@ -41,7 +41,8 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
     Returns numpy dict(out fp32, final, ckpt), and the workspace bytes under
     "workspace" when keep_workspace is set.  With state_bf16 the states are
     bf16 tensors (the initial state must hold bf16 values) and come back as
-    fp32 arrays of their bf16 values."""
+    fp32 arrays of their bf16 values.  cu64 passes the sequence offsets as
+    int64; seq_order (int32 numpy [N]) is the caller's recurrence order."""
     import torch
     import kda_gated_delta_chunked_amd as K
     d = d or to_device(p)
@@ -64,15 +65,20 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
         C = 1 if d["offs"].dim() == 1 else int(d["offs"].shape[1])
         shape = (N, H, 128, 128) if d["offs"].dim() == 1 else (N, C, H, 128, 128)
         ck = torch.full(shape, float("nan"), dtype=sdt, device=dev)
+    cu = d["cu"]
+    if cu is not None and cu64:
+        cu = cu.to(torch.int64)
+    order = None if seq_order is None else torch.from_numpy(np.asarray(seq_order, np.int32)).to(dev)
     prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split,
                           ckpt_per_seq=C, state_dtype="bf16" if state_bf16 else "fp32",
-                          qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+                          qk_l2norm=qk_l2norm, beta_logit=beta_logit, cu_seqlens_int64=cu64,
+                          seq_order=0 if order is None else order.data_ptr())
     need = K.workspace_size(prob)
     ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev) if need else None
     stream = torch.cuda.current_stream(dev)
     v_ptr = out.data_ptr() if out_alias_v else d["v"].data_ptr()
     st = K.prefill_raw(prob, d["q"].data_ptr(), d["k"].data_ptr(), v_ptr, d["g"].data_ptr(),
-                       d["beta"].data_ptr(), 0 if d["cu"] is None else d["cu"].data_ptr(),
+                       d["beta"].data_ptr(), 0 if cu is None else cu.data_ptr(),
                        0 if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
                        0 if d["offs"] is None else d["offs"].data_ptr(),
                        0 if ck is None else ck.data_ptr(), 0 if ws is None else ws.data_ptr(), need,

@@ -351,3 +351,26 @@ def test_prologue_rules():
     assert ops.decode_validate_raw(dp, *d.args()) == OK
     dp.prologue = 8
     assert ops.decode_validate_raw(dp, *d.args()) == INVALID
+
+
+def test_int64_offsets_and_sequence_order_rules():
+    b = Bufs()
+    # int64 offsets take (N + 1) * 8 bytes: a buffer starting right after
+    # the int32 extent overlaps them
+    p64 = prob_for(b, cu_seqlens_int64=True)
+    assert validate(p64, b) == OK
+    far = 1 << 48          # cu alone at the top, out right after its int32 extent
+    assert validate(prob_for(b), b, cu=far, out=far + 16) == OK
+    assert validate(p64, b, cu=far, out=far + 16) == OVERLAP
+    bad = prob_for(b)
+    bad.cu_seqlens_int64 = 2
+    assert validate(bad, b) == INVALID
+    # seq_order: packed layout only, 16-byte aligned, read-only (no overlap with
+    # what the call writes)
+    order = 1 << 50
+    assert validate(prob_for(b, seq_order=order), b) == OK
+    assert validate(prob_for(b, seq_order=order), b, cu=0) == INVALID
+    assert validate(prob_for(b, seq_order=order + 4), b) == ALIGN
+    assert validate(prob_for(b, seq_order=b.addr["out"]), b) == OVERLAP
+    assert validate(prob_for(b, seq_order=b.addr["fin"] + 64), b) == OVERLAP
+    assert validate(prob_for(b, seq_order=b.addr["q"]), b) == OK   # both only read
