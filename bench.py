@@ -249,6 +249,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b8_t8192")
     ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--chain-parts", type=int, default=0,
+                    help="pieces of each (sequence, head)'s recurrence; 0 = library's choice")
     ap.add_argument("--variant", default="auto", choices=["auto", "decomp", "fused"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--timing-calls", type=int, default=50,
@@ -300,8 +302,8 @@ def main() -> int:
     fin = torch.empty((p.N, p.H, 128, 128), dtype=torch.float32, device=dev)
     ck = None if offs is None else torch.empty_like(fin)
     prob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, variant=args.variant,
-                          value_split=args.value_split)
-    variant, vsplit = K.plan(prob)
+                          value_split=args.value_split, chain_parts=args.chain_parts)
+    variant, vsplit, pieces = K.plan(prob)
     ws_bytes = K.workspace_size(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream(dev)
@@ -388,7 +390,7 @@ def main() -> int:
     if variant == "decomp":
         for st, kname in (("prepare", "kda_prepare_kernel"), ("recurrence", "kda_recurrence_kernel")):
             sprob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, variant="decomp",
-                                   value_split=vsplit, stages=st)
+                                   value_split=vsplit, stages=st, chain_parts=pieces)
 
             def one(sprob=sprob):
                 rc = K.prefill_raw(sprob, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), ptr(s0),
@@ -439,7 +441,7 @@ def main() -> int:
                       "total_tokens": p.T_total, "H": p.H, "K": 128, "V": 128,
                       "initial_state": p.initial_state is not None,
                       "checkpoints": p.ckpt_offsets is not None,
-                      "variant": variant, "value_split": vsplit},
+                      "variant": variant, "value_split": vsplit, "chain_parts": pieces},
            "roofline": roof, "path": path, "mfma": mfma, "timing": timing}
     if args.workload == "b8_t8192":
         res["context"] = dict(PAGES_CONTEXT, ratio_ms=round(PAGES_CONTEXT["ms"] / ms_step, 3))

@@ -139,7 +139,23 @@ typedef struct {
                                 when it does not.  Results do not depend on the order.  The
                                 fixed layout and FUSED (whose workgroups all run at once when
                                 AUTO picks it) do not use it */
+  int32_t chain_parts;       /* two-launch schedule: pieces each (sequence, head)'s chain of
+                                segments is cut into, 0..KDA_MAX_CHAIN_PARTS.  0 = automatic
+                                (kda_plan reports the choice), 1 = no split.  With P >= 2 the
+                                recurrence runs as two launches: the first runs piece 0 from
+                                the initial state and pieces 1..P-2 both from a zero state and
+                                from the identity with V = 0 (the state update is affine in the
+                                state, so these two give each piece's map S -> T S + B); a scan
+                                composes the maps into each piece's incoming state; the second
+                                runs pieces 1..P-1 from those states with outputs and
+                                checkpoints.  It trades about 3x the recurrence's work for a
+                                chain P times shorter, for problems with too few pairs to fill
+                                the device (FlashInfer PR #4633, Performance: the B1 T8192 row
+                                is the recurrence's chain alone).  Results equal the unsplit
+                                recurrence's up to rounding.  FUSED takes 0 or 1 only */
 } kda_problem;
+
+#define KDA_MAX_CHAIN_PARTS 16
 
 /* Input prologue, done in the kernels before anything else reads q, k or
  * beta (FlashInfer PR #4262, Dispatch contract, lists kernels with q/k
@@ -167,7 +183,12 @@ enum { KDA_STAGE_PREPARE = 1, KDA_STAGE_RECURRENCE = 2 };
  * pick DECOMP, need a header of 2 N + 1 int32 rounded up to 256 bytes plus
  * 60,416 bytes per (segment slot, head), with floor(T_total / 64) + N + N C
  * segment slots (C = ckpt_per_seq, at least 1): about 0.94 KiB per
- * token-head.  The workspace is scratch:
+ * token-head.  A chain split of P pieces adds 3 x 64 KiB per (sequence, head,
+ * piece), with P = chain_parts when given, else, for AUTO and DECOMP, the
+ * most pieces AUTO may pick: min(16, 1 + floor(128 / (N H)),
+ * floor(ceil((T_total / N) / 64) / 8)) when that is at least 3 (else none).
+ * A smaller workspace that still holds the slots runs AUTO unsplit.  The
+ * workspace is scratch:
  * it carries nothing between calls, may be reused by any later call on the
  * same stream, and must not be used by two calls in flight at once. */
 kda_status kda_prefill_workspace_size(const kda_problem* p, size_t* bytes);
@@ -273,14 +294,16 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
  * (same passage: requests fail before any state is touched). */
 const char* kda_status_string(int status);
 
-/* Schedule and workgroups per (sequence, head) kda_prefill would use for this
- * problem on the current device, given a workspace of at least
- * kda_prefill_workspace_size bytes (host only; reads the device's CU count).
- * The choice comes from a table of measured rows keyed on the compute-unit
- * count, not on the device's name (FlashInfer PR #4633, Description: neither
- * the two-launch nor the one-launch kernel is faster everywhere, so a table
- * keyed on SM count picks per call, and a query reports the choice). */
-kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split);
+/* Schedule, workgroups per (sequence, head) and chain pieces (1 = no split;
+ * chain_parts may be NULL) kda_prefill would use for this problem on the
+ * current device, given a workspace of at least kda_prefill_workspace_size
+ * bytes (host only; reads the device's CU count).  The choice comes from a
+ * table of measured rows keyed on the compute-unit count, not on the device's
+ * name (FlashInfer PR #4633, Description: neither the two-launch nor the
+ * one-launch kernel is faster everywhere, so a table keyed on SM count picks
+ * per call, and a query reports the choice). */
+kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split,
+                    int32_t* chain_parts);
 
 #ifdef __cplusplus
 }

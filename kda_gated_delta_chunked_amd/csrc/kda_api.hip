@@ -63,6 +63,8 @@ kda_status check_problem(const kda_problem* p) {
   if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
   if (p->cu_seqlens_int64 != 0 && p->cu_seqlens_int64 != 1) return KDA_ERR_INVALID_ARG;
   if (p->ckpt_per_seq > kMaxCkptPerSeq) return KDA_ERR_UNSUPPORTED;
+  if (p->chain_parts < 0 || p->chain_parts > KDA_MAX_CHAIN_PARTS) return KDA_ERR_INVALID_ARG;
+  if (p->chain_parts > 1 && p->variant == KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;
   // the flat output index T_total * H * 128 must fit in int32
   if (p->total_tokens * (int64_t)p->num_heads * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if ((int64_t)p->num_seqs * p->num_heads > kInt32Max / 8) return KDA_ERR_TOO_LARGE;
@@ -88,13 +90,41 @@ int device_cu_count() {
   return cus;
 }
 
-size_t decomp_bytes(const kda_problem* p) {
+// DECOMP workspace bytes with the chain area for `pieces` (none below 2)
+size_t decomp_bytes(const kda_problem* p, int pieces) {
   size_t header = 0, bytes = 0;
   int64_t slots = 0;
-  kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, ckpt_count(p), &header,
-                              &slots, &bytes);
+  kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, ckpt_count(p), pieces,
+                              &header, &slots, &bytes);
   return bytes;
 }
+
+// Chain split.  The recurrence of a (sequence, head) pair is a chain of
+// segments, one after the other; with few pairs most CUs idle while it runs.
+// Cut into P pieces, the pieces after the first are run from a zero state and
+// from the identity (their affine map), a scan composes the maps, and every
+// piece is run again from its true incoming state.  The first split launch
+// holds pairs x (P - 1) groups of 2 x vsplit workgroups.
+// (pairs x pieces) the first split launch fits on a 256-CU device at one
+// workgroup per pair and column group: the workspace is sized for at most this
+constexpr int64_t kChainGroupBudget = 128;
+// fewest 64-token chunks per piece (shorter pieces do not repay the scan)
+constexpr int64_t kMinChunksPerPiece = 8;
+
+// pieces the workspace query provides for: chain_parts when given, else the
+// most that AUTO could pick from what the host knows (N, H, T_total / N)
+int chain_cap(const kda_problem* p) {
+  if (p->variant == KDA_VARIANT_FUSED) return 1;
+  if (p->chain_parts) return p->chain_parts;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
+  const int64_t chunks = (p->total_tokens / p->num_seqs + 63) / 64;
+  int64_t cap = 1 + kChainGroupBudget / pairs;
+  cap = cap < KDA_MAX_CHAIN_PARTS ? cap : KDA_MAX_CHAIN_PARTS;
+  cap = cap < chunks / kMinChunksPerPiece ? cap : chunks / kMinChunksPerPiece;
+  return cap >= 3 ? (int)cap : 1;
+}
+
+size_t decomp_bytes(const kda_problem* p) { return decomp_bytes(p, chain_cap(p)); }
 
 // Schedule choice.  FUSED: each workgroup carries one (sequence, head) pair
 // and a slice of the state's columns, and repeats the chunk preparation; two
@@ -127,10 +157,69 @@ bool fused_is_faster(const kda_problem* p, int cus) {
   return mean_len <= 64 && pairs * fused_vsplit(p, cus) <= cus;
 }
 
-void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit) {
+// Cost model of the recurrence, in segment times of the unsplit two-
+// workgroup schedule, fitted to MI355X measurements (256 CUs; H = 12 unless
+// stated; recurrence us unsplit -> split, vsplit, pieces):
+//   B1 T8192      223 -> 98   (2, 6) / 98 (2, 11) / 96 (1, 11)
+//   B2 T8192      227 -> 147  (2, 6); 168 (2, 5); 175 (2, 11)
+//   B1 T32768     875 -> 305  (2, 11); 343 (2, 6)
+//   B1 T2048       61 -> 51   (2, 5)
+//   B1 T8192 H32  226 -> 178  (2, 3); 188 (2, 5)
+//   B4 T2048       61 -> 91   (2, 3)  (the split loses: kept unsplit)
+// A run of L segments costs L x seg_cost(vsplit) per round of workgroups;
+// workgroups are dealt to the 8 XCDs round-robin by group and one runs per
+// CU, so a launch of G groups of W workgroups takes ceil(ceil(G / 8) W /
+// (CUs / 8)) rounds.  The split adds its scan (P - 2 steps) and two launches.
+double seg_cost(int vsplit) { return vsplit == 1 ? 1.6 : (vsplit == 2 ? 1.0 : 1.05); }
+constexpr double kScanStepCost = 1.2;   // one scan step (2.1 us), in segment times (1.74 us)
+constexpr double kSplitCost = 6.0;      // the extra launches and per-run start-up
+
+int64_t rounds(int64_t groups, int per_group, int cus) {
+  const int64_t per_xcd = (groups + 7) / 8 * per_group, slots = cus / 8;
+  return (per_xcd + slots - 1) / slots;
+}
+
+double split_cost(int64_t pairs, int64_t chunks, int vsplit, int P, int cus) {
+  const int64_t groups = pairs * (P - 1), L = (chunks + P - 1) / P;
+  return seg_cost(vsplit) * (double)L * (double)(rounds(groups, 2 * vsplit, cus) + rounds(groups, vsplit, cus)) +
+         kScanStepCost * (P - 2) + kSplitCost;
+}
+
+// Chain pieces (and the workgroups per pair they run with) for the two-launch
+// schedule: chain_parts when given; else (AUTO) the split, up to chain_cap
+// pieces, whose modelled cost is below 0.9 of the unsplit run's -- over
+// vsplit 1, 2 and 4 when value_split is automatic -- and whose chain area the
+// workspace holds.  Fewer than 3 pieces run nothing side by side.
+int chain_pieces(const kda_problem* p, int cus, size_t ws_bytes, int32_t* vsplit) {
+  if (p->chain_parts) return p->chain_parts;
+  const int cap = chain_cap(p);
+  if (cap < 3 || cus < 8) return 1;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
+  const int64_t chunks = (p->total_tokens / p->num_seqs + 63) / 64;
+  const double unsplit = seg_cost(*vsplit) * (double)chunks * (double)rounds(pairs, *vsplit, cus);
+  double best = 0.9 * unsplit;
+  int best_p = 1, best_vs = *vsplit;
+  for (int vs : {2, 1, 4}) {
+    if (p->value_split && vs != p->value_split) continue;
+    for (int P = 3; P <= cap; ++P) {
+      const double c = split_cost(pairs, chunks, vs, P, cus);
+      if (c < best && ws_bytes >= decomp_bytes(p, P)) {
+        best = c;
+        best_p = P;
+        best_vs = vs;
+      }
+    }
+  }
+  *vsplit = best_vs;
+  return best_p;
+}
+
+void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit,
+            int32_t* pieces) {
   int32_t var = p->variant;
+  *pieces = 1;
   if (var == KDA_VARIANT_AUTO) {
-    var = ws_bytes >= decomp_bytes(p) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
+    var = ws_bytes >= decomp_bytes(p, 1) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
     if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
       var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
     if (var == KDA_VARIANT_DECOMP && fused_is_faster(p, cus)) var = KDA_VARIANT_FUSED;
@@ -150,8 +239,9 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
     // 0.436).  Past the CU count two (B8 T8192 0.614 / 0.751); one and eight
     // are slower everywhere.
     const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
-    *vsplit = (cus > 0 && pairs * 4 <= cus && decomp_bytes(p) > kDecompCacheBytes) ? 4 : 2;
+    *vsplit = (cus > 0 && pairs * 4 <= cus && decomp_bytes(p, 1) > kDecompCacheBytes) ? 4 : 2;
   }
+  if (var == KDA_VARIANT_DECOMP) *pieces = chain_pieces(p, cus, ws_bytes, vsplit);
 }
 
 // ---------------------------------------------------------------------------
@@ -236,9 +326,11 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
     if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
   // DECOMP (named, or implied by a DECOMP-only value_split) needs its
   // workspace; AUTO falls back to FUSED when the workspace is smaller
-  int32_t var = 0, vs = 0;
-  choose(p, 0, workspace ? workspace_bytes : 0, &var, &vs);
-  if (var == KDA_VARIANT_DECOMP && (!workspace || workspace_bytes < decomp_bytes(p)))
+  // (with no device known AUTO splits no chain here; a given chain_parts
+  // needs its chain area)
+  int32_t var = 0, vs = 0, pieces = 1;
+  choose(p, 0, workspace ? workspace_bytes : 0, &var, &vs, &pieces);
+  if (var == KDA_VARIANT_DECOMP && (!workspace || workspace_bytes < decomp_bytes(p, pieces)))
     return KDA_ERR_WORKSPACE_TOO_SMALL;
 
   const uint64_t tok_bf16 = (uint64_t)T * H * kHeadDim * 2;
@@ -272,11 +364,14 @@ kda_status kda_validate(const kda_problem* p, const void* q, const void* k, cons
   return KDA_OK;
 }
 
-kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split) {
+kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split,
+                    int32_t* chain_parts) {
   if (!variant || !value_split) return KDA_ERR_INVALID_ARG;
   const kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
-  choose(p, device_cu_count(), decomp_bytes(p), variant, value_split);
+  int32_t pieces = 1;
+  choose(p, device_cu_count(), decomp_bytes(p), variant, value_split, &pieces);
+  if (chain_parts) *chain_parts = pieces;
   return KDA_OK;
 }
 
@@ -289,15 +384,15 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
                                      final_state, ckpt_offsets, ckpt_state, workspace,
                                      workspace_bytes);
   if (st != KDA_OK) return st;
-  int32_t variant = 0, vsplit = 0;
-  choose(p, device_cu_count(), workspace ? workspace_bytes : 0, &variant, &vsplit);
+  int32_t variant = 0, vsplit = 0, pieces = 1;
+  choose(p, device_cu_count(), workspace ? workspace_bytes : 0, &variant, &vsplit, &pieces);
   const hipStream_t st_ = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (variant == KDA_VARIANT_DECOMP) {
     size_t header = 0, bytes = 0;
     int64_t slots = 0;
-    kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, ckpt_count(p), &header,
-                              &slots, &bytes);
+    kda::decomp_workspace_layout(p->num_seqs, p->total_tokens, p->num_heads, ckpt_count(p), 1,
+                                 &header, &slots, &bytes);
     kda::DecompArgs a;
     a.q = q;
     a.k = k;
@@ -325,6 +420,10 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.slots_per_seq = cu_seqlens ? 0 : (a.T_fixed + 63) / 64 + (ckpt_offsets ? a.ckpt_per_seq : 0);
     a.slot_bound = slots;
     a.scale = p->scale;
+    // the chain area follows the slots (bytes = header + slot area)
+    a.pieces = pieces;
+    a.pass = 0;
+    a.chain = pieces >= 2 ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bytes) : nullptr;
     const int64_t prepare_slots = cu_seqlens ? slots : (int64_t)p->num_seqs * a.slots_per_seq;
     const int stages = p->stages ? p->stages : (KDA_STAGE_PREPARE | KDA_STAGE_RECURRENCE);
     // measured on MI355X, ms per call, normal / non-temporal workspace
@@ -368,8 +467,10 @@ kda_status kda_prefill_noalloc(const kda_problem* p, const uint16_t* q, const ui
   const kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
   // FUSED needs no workspace; AUTO and DECOMP may take the two-launch
-  // schedule, whose workspace must fit the static scratch
-  const size_t need = p->variant == KDA_VARIANT_FUSED ? 0 : decomp_bytes(p);
+  // schedule, whose workspace must fit the static scratch (without the chain
+  // area, unless chain_parts asks for it, AUTO then splits no chain)
+  size_t need = p->variant == KDA_VARIANT_FUSED ? 0 : decomp_bytes(p);
+  if (need > kNoallocScratchBytes && p->chain_parts < 2) need = decomp_bytes(p, 1);
   if (need > kNoallocScratchBytes) return KDA_ERR_SCRATCH_TOO_SMALL;
   void* ws = nullptr;
   if (need) {

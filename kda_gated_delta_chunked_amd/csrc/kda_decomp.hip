@@ -902,27 +902,71 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   __shared__ __attribute__((aligned(16))) uint4 ktA[KT3 ? KTU * 64 : 1];
   __shared__ __attribute__((aligned(16))) uint4 ktB[KT3 ? KTU * 64 : 1];
   __shared__ __attribute__((aligned(16))) uint4 ktC[KT3 ? KTU * 64 : 1];
-  constexpr int PARTS = 8 / WAVES;
+  constexpr int VG = 8 / WAVES;  // column groups (workgroups) per run
   const int H = a.H;
+  // What the workgroup runs over its range of segments (all of them without
+  // the chain split):
+  //   MAIN  from the initial state, with outputs and checkpoints
+  //   ZERO  from a zero state, no outputs: the piece's affine part
+  //   EYE   from the identity with V = 0, no outputs: the piece's transition
+  //   CONT  from the state the chain scan left for the piece, with outputs
+  // The state update is affine in the state entering a piece (the decay and
+  // the delta rule's correction are linear maps of S, V enters additively),
+  // so the state leaving it is T_p S + B_p with T_p from EYE and B_p from ZERO.
+  enum { MAIN, ZERO, EYE, CONT };
   // workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8): keep
-  // the column groups of a (sequence, head) on one XCD so they share L2
+  // the workgroups that read one piece's slots (its column groups, and in the
+  // first split launch both ZERO and EYE) on one XCD so they share L2
   const int bx = blockIdx.x, xcd = bx & 7, rest = bx >> 3;
-  const int pair = (rest / PARTS) * 8 + xcd, part = rest % PARTS;
-  if (pair >= a.N * H) return;
+  int pair, cg, piece = 0, role = MAIN;
+  if (a.pass == 0) {
+    pair = (rest / VG) * 8 + xcd;
+    cg = rest % VG;
+    if (pair >= a.N * H) return;
+  } else {
+    // pass 1: pieces 0 .. P-2 (piece 0 as MAIN, the others as ZERO and EYE);
+    // pass 2: pieces 1 .. P-1 as CONT
+    const int per = a.pieces - 1, W = a.pass == 1 ? 2 * VG : VG;
+    const int slot = rest % W, gi = (rest / W) * 8 + xcd;
+    if (gi >= a.N * H * per) return;
+    pair = gi / per;
+    piece = gi - pair * per;
+    cg = slot % VG;
+    if (a.pass == 1) {
+      if (piece == 0 && slot >= VG) return;
+      role = piece == 0 ? MAIN : (slot < VG ? ZERO : EYE);
+    } else {
+      ++piece;
+      role = CONT;
+    }
+  }
   const int rank = pair / H, h = pair - rank * H;
   const int n = a.order ? a.order[rank] : rank;
+  const int64_t spair = (int64_t)n * H + h;  // the pair's index in the state layouts
+  const bool emit = role == MAIN || role == CONT;
+  // V's weight: EYE runs with V = 0 (the V block is still copied; finite
+  // bf16 values times 0 give 0)
+  const float vmul = role == EYE ? 0.f : 1.f;
   // the wave index as a scalar: the role branch below is then uniform, so the
   // compiler keeps the two roles' code paths (and their memory counters) apart
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, q = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const SeqInfo si = seq_info(a, n);
-  const int64_t base = a.cu_seqlens ? (int64_t)a.seg_base[n] : (int64_t)n * a.slots_per_seq;
+  int64_t base = a.cu_seqlens ? (int64_t)a.seg_base[n] : (int64_t)n * a.slots_per_seq;
   int nseg = si.nseg;
   if (base + nseg > a.slot_bound) nseg = base >= a.slot_bound ? 0 : (int)(a.slot_bound - base);
+  // the piece's segments [j0, j1) (all of them without the split)
+  int j0 = 0;
+  if (a.pass != 0) {
+    j0 = (int)((int64_t)piece * nseg / a.pieces);
+    const int j1 = (int)((int64_t)(piece + 1) * nseg / a.pieces);
+    base += j0;
+    nseg = j1 - j0;
+  }
   auto geometry = [&](int jseg, int& off, int64_t& tok0) {
     int lo, hi;
-    seg_range(si, jseg, lo, hi);
+    seg_range(si, j0 + jseg, lo, hi);
     off = CH - (hi - lo);
     tok0 = si.bos + lo - off;
   };
@@ -942,7 +986,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       constexpr int LPR = VW / 8, RPI = 64 / LPR;  // lanes per row, rows per unit
       for (int k = cw; k < VUNITS; k += KW) {
         const int row = max(k * RPI + lane / LPR, off);
-        const uint16_t* vsrc = a.v + ((size_t)(tok0 + row) * H + h) * DK + VW * part + 8 * (lane % LPR);
+        const uint16_t* vsrc = a.v + ((size_t)(tok0 + row) * H + h) * DK + VW * cg + 8 * (lane % LPR);
         __builtin_amdgcn_global_load_lds(vsrc, dst + (SLOT_UNITS - KB / 1024 + k) * 64, 16, 0, 0);
       }
     };
@@ -1019,25 +1063,32 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   }
 
   // ---- compute waves
-  const int col0 = 16 * (part * WAVES + w);
+  const int col0 = 16 * (cg * WAVES + w);
   // accumulator row 16 m + 4 g4 + e holds key channel state_row_channel of it,
   // that is 8 g4 + srow(m, e)
-  const size_t sbase = ((size_t)n * H + h) * DK * DK + col0 + q + (size_t)(8 * g4) * DK;
+  const size_t sbase = (size_t)spair * DK * DK + col0 + q + (size_t)(8 * g4) * DK;
   auto srow = [](int m, int e) { return 32 * (m >> 1) + 4 * (m & 1) + e; };
   // S holds 2^sexp times the state (sexp is the wave's operand scale exponent)
   f32x4 S[8];
   int sexp = 0;
-  if (a.s0 && a.state_bf16) {
+  if (role == MAIN && a.s0 && a.state_bf16) {
     const uint16_t* s0 = reinterpret_cast<const uint16_t*>(a.s0);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[m][e] = bf2f(s0[sbase + (size_t)srow(m, e) * DK]);
-  } else if (a.s0) {
+  } else if ((role == MAIN && a.s0) || role == CONT) {
+    const float* src = role == MAIN ? a.s0 + sbase
+                                    : a.chain + chain_matrix(spair, a.pieces, piece, 0) + (sbase - (size_t)spair * DK * DK);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][e] = a.s0[sbase + (size_t)srow(m, e) * DK];
+      for (int e = 0; e < 4; ++e) S[m][e] = src[(size_t)srow(m, e) * DK];
+  } else if (role == EYE) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[m][e] = 8 * g4 + srow(m, e) == col0 + q ? 1.f : 0.f;
   } else {
 #pragma unroll
     for (int m = 0; m < 8; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -1045,14 +1096,14 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   // state store into dst at element offset e0 (fp32, or bf16 rounded to
   // nearest even when the states are bf16); the power of two comes off
   // exactly
-  auto store_state = [&](float* dst, size_t e0) {
+  auto store_state = [&](float* dst, size_t e0, bool bf16 = true) {
     // the lane's offsets are formed here from an opaque lane index, so the 32
     // store addresses are not kept live in registers across the segment loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const size_t o = e0 + ((size_t)n * H + h) * DK * DK + col0 + (ln & 15) + (ln >> 4) * 8 * DK;
+    const size_t o = e0 + (size_t)spair * DK * DK + col0 + (ln & 15) + (ln >> 4) * 8 * DK;
     const float unscale = pow2f(-sexp);
-    if (a.state_bf16) {
+    if (bf16 && a.state_bf16) {
       uint16_t* rowp = reinterpret_cast<uint16_t*>(dst) + o;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
@@ -1068,9 +1119,22 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   };
   // checkpoint c of this sequence (layout [N, C, H, K, V]): element offset
   auto ckpt_slot = [&](int c) { return ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DK; };
-  for_each_honoured(si.ck, [&](int c, int p) {
-    if (p == 0) store_state(a.ckpt, ckpt_slot(c));
-  });
+  // the piece's state transition, transposed (row = the state's column):
+  // each lane's four consecutive rows of a column go out as one 16-byte store
+  auto store_transition = [&](float* mat) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    float* colp = mat + (size_t)(col0 + (ln & 15)) * DK + (ln >> 4) * 8;
+    const float unscale = pow2f(-sexp);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      *reinterpret_cast<float4*>(colp + srow(m, 0)) =
+          make_float4(S[m][0] * unscale, S[m][1] * unscale, S[m][2] * unscale, S[m][3] * unscale);
+  };
+  if (role == MAIN)
+    for_each_honoured(si.ck, [&](int c, int p) {
+      if (p == 0) store_state(a.ckpt, ckpt_slot(c));
+    });
 
   uint32_t opk[8];
   int poff = CH;
@@ -1223,7 +1287,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       uint32_t vmax = 0u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) vmax = max(vmax, (uint32_t)vv[i] & 0x7fffu);
-      const float big = wave_max_nonneg(fmaxf(mx, bf2f(vmax) * pow2f(sexp)));
+      const float big = wave_max_nonneg(fmaxf(mx, bf2f(vmax) * (pow2f(sexp) * vmul)));
       const int nexp = rescale_exponent(big, sexp);
       if (nexp != sexp) {
         const int dexp = nexp - sexp;
@@ -1259,7 +1323,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #pragma unroll
       for (int i = 0; i < 6; ++i) fn[i] = trifrag(SL_N, i);
     }
-    const float sig = pow2f(sexp);
+    const float sig = pow2f(sexp) * vmul;
     // Y = beta (2^s V - X), kept in U; U = Y + N Y.  Rows before the segment
     // have beta = 0 (their V read is a copy of row `off`), so they give U = 0.
     f32x4 U[4];
@@ -1321,8 +1385,8 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 #undef KDA_FENCE
     poff = off;
     ptok = tok0;
-    store_out();
-    if (si.ck.C > 0) {
+    if (emit) store_out();
+    if (emit && si.ck.C > 0) {
       unsigned long long mask = ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane(hmask.y) << 32) |
                                 (uint32_t)__builtin_amdgcn_readfirstlane(hmask.x);
       while (mask) {
@@ -1337,15 +1401,159 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     step(jseg, opsA);
     if (jseg + 1 < nseg) step(jseg + 1, opsB);
   }
-  if (a.final_state) store_state(a.final_state, 0);
+  // the end state: the result, or what the chain scan takes (as offsets from
+  // the pair's own state offset, which store_state adds)
+  const size_t own = (size_t)spair * DK * DK;
+  if (role == EYE) {
+    store_transition(a.chain + chain_matrix(spair, a.pieces, piece, 2));
+  } else if (role == ZERO) {
+    store_state(a.chain, chain_matrix(spair, a.pieces, piece, 1) - own, false);
+  } else if (role == MAIN && a.pass == 1) {
+    store_state(a.chain, chain_matrix(spair, a.pieces, 1, 0) - own, false);
+  } else if (a.final_state && (a.pass == 0 || piece == a.pieces - 1)) {
+    store_state(a.final_state, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chain scan, between the split's two recurrence launches: the state entering
+// piece p + 1 is T_p S_p + B_p for p = 1 .. P-2 (S_1 from the first launch's
+// MAIN run; T_p stored transposed, B_p from ZERO).  Columns of the state are
+// independent, so one workgroup takes 16 columns of one (sequence, head) pair
+// through all the steps, on the fp32 matrix cores (16x16x4 products, fp32
+// accumulation; vector FMAs would be bound by LDS reads of the operands).
+// Wave w owns rows 32 w .. 32 w + 31 as two 16-row tiles, interleaved (tile t
+// row i is state row 32 w + 2 i + t), so one 8-byte LDS read gives a lane its
+// A operands for both tiles.  The steps are latency-bound: T_{p+1}^T streams
+// into one LDS buffer (direct global-to-LDS loads) while step p computes from
+// the other; the buffers are separate arrays and the steps alternate between
+// them by name, so the compiler sees that reads of one do not wait for the
+// copies into the other.
+constexpr int kScanCols = 16;
+constexpr int kScanThreads = 256;
+
+__global__ __launch_bounds__(kScanThreads) void kda_chain_scan_kernel(DecompArgs a) {
+  __shared__ __attribute__((aligned(16))) uint4 TA[DK * DK / 4];
+  __shared__ __attribute__((aligned(16))) uint4 TB[DK * DK / 4];
+  __shared__ __attribute__((aligned(16))) float Sc[DK * kScanCols];  // [k][16 columns]
+  // a pair's 8 column groups on one XCD (workgroups are dealt to the 8 XCDs
+  // round-robin), so that T_p^T is fetched into that XCD's L2 once
+  static_assert(DK / kScanCols == 8, "one column group per XCD slot");
+  const int bx = blockIdx.x, xcd = bx & 7, slot = bx >> 3;
+  const int64_t pair = (int64_t)(slot >> 3) * 8 + xcd;
+  const int c0 = (slot & 7) * kScanCols;
+  if (pair >= (int64_t)a.N * a.H || a.pieces < 3) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, q = lane & 15, g4 = lane >> 4;
+  // T_p^T (64 KiB): wave w brings 1 KiB units w, w + 4, ... into dst
+  auto fetch = [&](int p, uint4* dst) {
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.chain + chain_matrix(pair, a.pieces, p, 2));
+#pragma unroll
+    for (int i = 0; i < DK * DK * 4 / 1024 / (kScanThreads / 64); ++i) {
+      const int u = w + (kScanThreads / 64) * i;
+      __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
+    }
+  };
+  // the lane's output elements: column c0 + q, rows row(t, e) of tile t
+  auto row = [&](int tile, int e) { return 32 * w + 2 * (4 * g4 + e) + tile; };
+  auto load_b = [&](int p, f32x4& b0, f32x4& b1) {
+    const float* bp = a.chain + chain_matrix(pair, a.pieces, p, 1) + c0 + q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      b0[e] = bp[(size_t)row(0, e) * DK];
+      b1[e] = bp[(size_t)row(1, e) * DK];
+    }
+  };
+  auto step = [&](int p, const uint4* cur, uint4* nxt, f32x4& b0, f32x4& b1) {
+    f32x4 acc0 = b0, acc1 = b1;
+    if (p + 2 < a.pieces) {
+      fetch(p + 1, nxt);
+      load_b(p + 1, b0, b1);
+    }
+    const float* Tt = reinterpret_cast<const float*>(cur);
+    // all operands read first (96 registers), then the 64 products back to
+    // back: the reads' latency is paid once, not once per pair of k-steps
+    float2 av[DK / 4];
+    float bv[DK / 4];
+#pragma unroll
+    for (int ks = 0; ks < DK / 4; ++ks) {
+      const int k = 4 * ks + g4;
+      av[ks] = *reinterpret_cast<const float2*>(Tt + k * DK + 32 * w + 2 * q);
+      bv[ks] = Sc[k * kScanCols + q];
+    }
+#pragma unroll
+    for (int ks = 0; ks < DK / 4; ++ks) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks].x, bv[ks], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks].y, bv[ks], acc1, 0, 0, 0);
+    }
+    // every wave is done reading Sc and `cur` (its reads have returned: the
+    // products used them); the copies into `nxt` stay in flight, so no
+    // workgroup-scope fence, whose release would wait for them
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Sc[row(0, e) * kScanCols + q] = acc0[e];
+      Sc[row(1, e) * kScanCols + q] = acc1[e];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of T_{p+1}^T landed
+    lds_barrier();                       // every wave's part landed; Sc holds S_{p+1}
+    // S_{p+1} for the second launch, stored after the wait above so that it
+    // covers the copies only; the next step's wait finds these done
+    float* dst = a.chain + chain_matrix(pair, a.pieces, p + 1, 0) + c0 + q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[(size_t)row(0, e) * DK] = acc0[e];
+      dst[(size_t)row(1, e) * DK] = acc1[e];
+    }
+  };
+  fetch(1, TA);
+  f32x4 b0, b1;
+  load_b(1, b0, b1);
+  {
+    // S_1's 16 columns: thread t takes row t / 2, columns 8 (t & 1) .. + 7
+    const float4* s1 = reinterpret_cast<const float4*>(a.chain + chain_matrix(pair, a.pieces, 1, 0) +
+                                                       (size_t)(t >> 1) * DK + c0 + 8 * (t & 1));
+    const float4 x = s1[0], y = s1[1];
+    float4* sd = reinterpret_cast<float4*>(Sc + (t >> 1) * kScanCols + 8 * (t & 1));
+    sd[0] = x;
+    sd[1] = y;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();
+  for (int p = 1; p + 1 < a.pieces; p += 2) {
+    step(p, TA, TB, b0, b1);
+    if (p + 2 < a.pieces) step(p + 1, TB, TA, b0, b1);
+  }
 }
 
 template <int CW, int KW>
 hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
-  constexpr int PARTS = 8 / CW;
+  constexpr int VG = 8 / CW;
   const int64_t pairs = (int64_t)a.N * a.H;
-  const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * PARTS));
-  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), grid, dim3(64 * (CW + KW)), 0, stream, a);
+  if (a.pieces < 2) {
+    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * VG));
+    hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), grid, dim3(64 * (CW + KW)), 0, stream, a);
+    return hipGetLastError();
+  }
+  // the split: groups of (pair, piece), P - 1 per pair in each launch; a
+  // group of the first launch holds ZERO's and EYE's workgroups
+  const int64_t groups = pairs * (a.pieces - 1);
+  DecompArgs b = a;
+  b.pass = 1;
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), dim3((unsigned)(((groups + 7) / 8) * 8 * 2 * VG)),
+                     dim3(64 * (CW + KW)), 0, stream, b);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (a.pieces > 2) {
+    hipLaunchKernelGGL(kda_chain_scan_kernel, dim3((unsigned)(((pairs + 7) / 8) * 8 * (DK / kScanCols))),
+                       dim3(kScanThreads), 0, stream, b);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  b.pass = 2;
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), dim3((unsigned)(((groups + 7) / 8) * 8 * VG)),
+                     dim3(64 * (CW + KW)), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -78,16 +78,37 @@ struct DecompArgs {
   int64_t slots_per_seq;      // fixed layout: slots owned by each sequence
   int64_t slot_bound;         // slots the workspace holds
   float scale;
+  // chain split (pieces >= 2): each (sequence, head)'s segments are cut into
+  // `pieces` consecutive ranges; `chain` holds per pair and piece three fp32
+  // 128 x 128 matrices (chain_matrix).  pass 0: no split; 1 and 2: the two
+  // recurrence launches of the split (set by launch_decomp)
+  int pieces;
+  int pass;
+  float* chain;
 };
 
-// Workspace layout for (N, T_total, H): header bytes and slot capacity.
-inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64_t C,
+// The chain split's matrices of pair n * H + h, piece p: 0 = the state
+// entering the piece, 1 = the piece's end state from a zero start, 2 = the
+// transpose of the piece's state transition (its end state from the
+// identity with V = 0).  Element offset into the chain area.
+constexpr int kChainMatrices = 3;
+__host__ __device__ constexpr size_t chain_matrix(int64_t pair, int pieces, int p, int which) {
+  return (((size_t)pair * pieces + p) * kChainMatrices + which) * 128 * 128;
+}
+inline size_t chain_bytes(int64_t pairs, int pieces) {
+  return pieces >= 2 ? (size_t)pairs * pieces * kChainMatrices * 128 * 128 * 4 : 0;
+}
+
+// Workspace layout for (N, T_total, H) with `pieces` chain pieces: header
+// bytes, slot capacity and total bytes (the chain area, when pieces >= 2,
+// follows the slots).
+inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64_t C, int pieces,
                                     size_t* header, int64_t* slots, size_t* bytes) {
   *header = (size_t)(((2 * N + 1) * 4 + 255) / 256 * 256);
   // ceil(L/64) summed over sequences is at most floor(T/64) + N; C more per
   // sequence for the chunks cut at its C checkpoint offsets
   *slots = T_total / 64 + N + N * (C < 1 ? 1 : C);
-  *bytes = *header + (size_t)(*slots) * (size_t)H * kDecompSlotBytes;
+  *bytes = *header + (size_t)(*slots) * (size_t)H * kDecompSlotBytes + chain_bytes(N * H, pieces);
 }
 
 // vsplit = workgroups per (sequence, head): 1, 2, 4 or 8.  prepare_slots =
@@ -96,6 +117,8 @@ inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64
 // stages: bit 0 = the prepare launch (and the slot plan), bit 1 = the recurrence.
 // stream_ws: the prepare writes the workspace with non-temporal stores (for a
 // workspace that does not stay in the Infinity Cache until the recurrence).
+// With a.pieces >= 2 the recurrence runs as the chain split's two launches
+// with the scan of the piece transitions between them.
 hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
                          bool stream_ws, hipStream_t stream);
 

@@ -47,7 +47,7 @@ class Problem(ctypes.Structure):
                 ("value_split", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("ckpt_per_seq", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
                 ("prologue", ctypes.c_int32), ("cu_seqlens_int64", ctypes.c_int32),
-                ("seq_order", ctypes.c_void_p)]
+                ("seq_order", ctypes.c_void_p), ("chain_parts", ctypes.c_int32)]
 
 
 STAGES = {"both": 0, "prepare": 1, "recurrence": 2}
@@ -79,7 +79,7 @@ def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: flo
                  head_dim_v: int = HEAD_DIM, stages: str | int = "both",
                  ckpt_per_seq: int = 0, state_dtype: str = "fp32", qk_l2norm: bool = False,
                  beta_logit: bool = False, cu_seqlens_int64: bool = False,
-                 seq_order: int = 0) -> Problem:
+                 seq_order: int = 0, chain_parts: int = 0) -> Problem:
     """Mirror of kda_problem; seq_order is a raw device pointer (0 = none)."""
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     st = STAGES[stages] if isinstance(stages, str) else int(stages)
@@ -87,7 +87,7 @@ def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: flo
                    int(head_dim_v), float(scale), float(gate_lower_bound), v, int(value_split), st,
                    int(ckpt_per_seq), STATE_DTYPES[state_dtype],
                    (1 if qk_l2norm else 0) | (2 if beta_logit else 0),
-                   1 if cu_seqlens_int64 else 0, int(seq_order) or None)
+                   1 if cu_seqlens_int64 else 0, int(seq_order) or None, int(chain_parts))
 
 
 def periodic_offsets(seq_lens, every: int):
@@ -135,7 +135,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.kda_prefill_noalloc.restype = ctypes.c_int
-    lib.kda_plan.argtypes = [PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_plan.argtypes = [PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                             ctypes.POINTER(ctypes.c_int32)]
     lib.kda_plan.restype = ctypes.c_int
     DP = ctypes.POINTER(DecodeProblem)
     lib.kda_decode_validate.argtypes = [DP, P, P, P, P, P, P, P, P]
@@ -160,12 +161,15 @@ def workspace_size(problem: Problem) -> int:
     return int(n.value)
 
 
-def plan(problem: Problem) -> Tuple[str, int]:
+def plan(problem: Problem) -> Tuple[str, int, int]:
+    """(schedule, workgroups per pair, chain pieces) kda_prefill would use on
+    the current device."""
     lib = load_library()
-    var, vs = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(lib.kda_plan(ctypes.byref(problem), ctypes.byref(var), ctypes.byref(vs)), "kda_plan")
+    var, vs, parts = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.kda_plan(ctypes.byref(problem), ctypes.byref(var), ctypes.byref(vs),
+                        ctypes.byref(parts)), "kda_plan")
     name = {v: k for k, v in VARIANTS.items()}.get(var.value, str(var.value))
-    return name, int(vs.value)
+    return name, int(vs.value), int(parts.value)
 
 
 def prefill_raw(problem: Problem, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
@@ -207,7 +211,8 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
             out=None, final_state=None, output_final_state: bool = True, ckpt_offsets=None,
             ckpt_state=None, gate_lower_bound: float = -5.0, variant: str = "auto",
             value_split: int = 0, workspace=None, stream=None, state_dtype=None,
-            qk_l2norm: bool = False, beta_logit: bool = False, seq_order=None):
+            qk_l2norm: bool = False, beta_logit: bool = False, seq_order=None,
+            chain_parts: int = 0):
     """KDA multi-token recurrent prefill on the GPU.
 
     q, k, v: bf16 [T, H, 128] (packed, with cu_seqlens int32 [N+1]) or
@@ -226,7 +231,9 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
     and the schedule may use one, a buffer is taken from torch's allocator.
     cu_seqlens may be int32 or int64.  seq_order: optional int32 [N], the
     order in which the recurrence takes packed sequences (a permutation; see
-    kda_problem.seq_order).
+    kda_problem.seq_order).  chain_parts: pieces each (sequence, head)'s
+    recurrence is split into (0 = the library's choice, 1 = none; see
+    kda_problem.chain_parts).
     """
     import torch
 
@@ -298,7 +305,7 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, initial_state=None, scale: Opt
                         ckpt_per_seq=C,
                         state_dtype="bf16" if state_dtype == torch.bfloat16 else "fp32",
                         qk_l2norm=qk_l2norm, beta_logit=beta_logit, cu_seqlens_int64=cu64,
-                        seq_order=_ptr(seq_order))
+                        seq_order=_ptr(seq_order), chain_parts=chain_parts)
     if seq_order is not None and tuple(seq_order.shape) != (N,):
         raise ValueError(f"seq_order must be [{N}]")
     out_given, final_given = out, final_state

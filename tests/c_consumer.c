@@ -48,6 +48,7 @@ int main(void) {
   FIELD(kda_problem, prologue);
   FIELD(kda_problem, cu_seqlens_int64);
   FIELD(kda_problem, seq_order);
+  FIELD(kda_problem, chain_parts);
   printf("sizeof.kda_decode_problem %zu\n", sizeof(kda_decode_problem));
   FIELD(kda_decode_problem, num_seqs);
   FIELD(kda_decode_problem, tokens_per_seq);
@@ -60,11 +61,15 @@ int main(void) {
   FIELD(kda_decode_problem, prologue);
 
   /* workspace sizes: fixed B8 T8192 H12, a packed batch with 3 offsets per
-   * sequence, and the one-launch schedule (no workspace) */
-  const kda_problem ws[3] = {problem(8, 8 * 8192, 12, KDA_VARIANT_AUTO, 0),
-                             problem(5, 1000, 3, KDA_VARIANT_DECOMP, 3),
-                             problem(8, 8 * 8192, 12, KDA_VARIANT_FUSED, 0)};
-  for (int i = 0; i < 3; ++i) {
+   * sequence, the one-launch schedule (no workspace), B1 T8192 H12 (with the
+   * chain area AUTO may use) and the same with 4 chain pieces */
+  kda_problem ws[5] = {problem(8, 8 * 8192, 12, KDA_VARIANT_AUTO, 0),
+                       problem(5, 1000, 3, KDA_VARIANT_DECOMP, 3),
+                       problem(8, 8 * 8192, 12, KDA_VARIANT_FUSED, 0),
+                       problem(1, 8192, 12, KDA_VARIANT_AUTO, 0),
+                       problem(1, 8192, 12, KDA_VARIANT_DECOMP, 0)};
+  ws[4].chain_parts = 4;
+  for (int i = 0; i < 5; ++i) {
     size_t bytes = 0;
     const kda_status s = kda_prefill_workspace_size(&ws[i], &bytes);
     printf("workspace.%d %d %zu\n", i, (int)s, bytes);

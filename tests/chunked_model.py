@@ -291,3 +291,63 @@ def prefill_problem(p, **kw):
     return prefill(f32_from_bf16_bits(p.q), f32_from_bf16_bits(p.k), f32_from_bf16_bits(p.v), p.g,
                    p.beta, scale=p.scale, cu_seqlens=p.cu_seqlens, initial_state=p.initial_state,
                    ckpt_offsets=p.ckpt_offsets, **kw)
+
+
+def prefill_chain(p, pieces, *, emulate=False, recipe=None, chunk=64):
+    """The chain split of the two-launch schedule on a synth.Problem without
+    checkpoints.  Each (sequence, head)'s chunks are cut into `pieces`
+    ranges [floor(i n / P), floor((i + 1) n / P)); piece 0 runs from the
+    initial state; pieces 1..P-2 run from a zero state (V as given: the
+    affine part B_i) and from the identity with V = 0 (the transition T_i,
+    a K x K matrix, as a K x V state with V = K columns); the incoming states
+    follow from S_{i+1} = T_i S_i + B_i in the state's precision; pieces
+    1..P-1 run again from them with outputs.  Every run starts with fresh
+    operand scale exponents, as each workgroup does.  Returns dict(out,
+    final)."""
+    assert p.ckpt_offsets is None
+    dt = np.float32 if emulate else np.float64
+    q, k, v = f32_from_bf16_bits(p.q), f32_from_bf16_bits(p.k), f32_from_bf16_bits(p.v)
+    T, H, K = q.shape
+    V = v.shape[2]
+    cu = p.cu_seqlens
+    out = np.zeros((T, H, V), dt)
+    final = np.zeros((p.N, H, K, V), dt)
+
+    def run(S, h, cuts, zero_v=False):
+        sexp = np.zeros(S.shape[1])
+        outs = []
+        for c0, c1 in zip(cuts[:-1], cuts[1:]):
+            vv = np.zeros((c1 - c0, S.shape[1]), np.float32) if zero_v else v[c0:c1, h]
+            O, S, _ = chunk_step(S, q[c0:c1, h], k[c0:c1, h], vv, p.g[c0:c1, h], p.beta[c0:c1, h],
+                                 p.scale, emulate=emulate, recipe=recipe, sexp=sexp)
+            outs.append((c0, c1, O))
+        return S.astype(dt), outs
+
+    for n in range(p.N):
+        bos, eos = int(cu[n]), int(cu[n + 1])
+        bounds = list(range(bos, eos, chunk)) + [eos] if eos > bos else [bos]
+        nseg = len(bounds) - 1
+        piece_cuts = [bounds[(i * nseg) // pieces:((i + 1) * nseg) // pieces + 1] for i in range(pieces)]
+        for h in range(H):
+            S0 = np.zeros((K, V), dt) if p.initial_state is None else p.initial_state[n, h].astype(dt)
+            S_in, _ = run(S0, h, piece_cuts[0])
+            for i in range(1, pieces - 1):
+                Ti, _ = run(np.eye(K, dtype=dt), h, piece_cuts[i], zero_v=True)
+                Bi, _ = run(np.zeros((K, V), dt), h, piece_cuts[i])
+                start = S_in
+                S_in = (Ti @ start + Bi).astype(dt)
+                # outputs of piece i come from the run from its true state
+                _, outs = run(start, h, piece_cuts[i])
+                for c0, c1, O in outs:
+                    out[c0:c1, h] = O
+            if pieces == 1:
+                _, outs = run(S0, h, piece_cuts[0])
+                S_fin = S_in
+            else:
+                S_fin, outs = run(S_in, h, piece_cuts[-1])
+                _, first = run(S0, h, piece_cuts[0])
+                outs = outs + first
+            for c0, c1, O in outs:
+                out[c0:c1, h] = O
+            final[n, h] = S_fin
+    return {"out": out, "final": final}

@@ -32,7 +32,7 @@ def to_device(p: synth.Problem):
 def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=None,
             sentinel: bool = True, out_alias_v: bool = False, state_in_place: bool = False,
             keep_workspace: bool = False, state_bf16: bool = False, qk_l2norm: bool = False,
-            beta_logit: bool = False, cu64: bool = False, seq_order=None):
+            beta_logit: bool = False, cu64: bool = False, seq_order=None, chain_parts: int = 0):
     """Run kda_prefill through the C ABI on a fresh set of device buffers.
 
     Outputs are pre-filled with NaN so that any element the kernel fails to
@@ -42,7 +42,9 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
     "workspace" when keep_workspace is set.  With state_bf16 the states are
     bf16 tensors (the initial state must hold bf16 values) and come back as
     fp32 arrays of their bf16 values.  cu64 passes the sequence offsets as
-    int64; seq_order (int32 numpy [N]) is the caller's recurrence order."""
+    int64; seq_order (int32 numpy [N]) is the caller's recurrence order;
+    chain_parts the pieces of the two-launch schedule's chain split (0 = the
+    library's choice)."""
     import torch
     import kda_gated_delta_chunked_amd as K
     d = d or to_device(p)
@@ -72,7 +74,8 @@ def run_gpu(p: synth.Problem, *, variant: str = "auto", value_split: int = 0, d=
     prob = K.make_problem(N, T, H, scale=p.scale, variant=variant, value_split=value_split,
                           ckpt_per_seq=C, state_dtype="bf16" if state_bf16 else "fp32",
                           qk_l2norm=qk_l2norm, beta_logit=beta_logit, cu_seqlens_int64=cu64,
-                          seq_order=0 if order is None else order.data_ptr())
+                          seq_order=0 if order is None else order.data_ptr(),
+                          chain_parts=chain_parts)
     need = K.workspace_size(prob)
     ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev) if need else None
     stream = torch.cuda.current_stream(dev)

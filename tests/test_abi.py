@@ -145,11 +145,21 @@ def test_prefill_rejects_on_the_host_without_a_device():
     assert st == OVERLAP
 
 
-def decomp_bytes(N, T, H, C=1):
+def chain_cap(N, T, H):
+    """The documented most chain pieces AUTO may pick: min(16, 1 + 128 // (N H),
+    ceil((T // N) / 64) // 8), or 1 below 3."""
+    cap = min(16, 1 + 128 // (N * H), -(-(T // N) // 64) // 8)
+    return cap if cap >= 3 else 1
+
+
+def decomp_bytes(N, T, H, C=1, pieces=None):
     """The documented workspace formula: 2 N + 1 int32 rounded up to 256
     bytes, then 60,416 bytes per (segment slot, head) for floor(T / 64) + N +
-    N C slots (C checkpoint offsets per sequence, at least 1)."""
-    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + N + N * max(C, 1)) * H * 60416
+    N C slots (C checkpoint offsets per sequence, at least 1), then 3 x 64 KiB
+    per (sequence, head, chain piece) when there are 2 or more pieces."""
+    P = chain_cap(N, T, H) if pieces is None else pieces
+    chain = N * H * P * 3 * 65536 if P >= 2 else 0
+    return ((2 * N + 1) * 4 + 255) // 256 * 256 + (T // 64 + N + N * max(C, 1)) * H * 60416 + chain
 
 
 def test_workspace_grows_with_checkpoints_per_sequence():
@@ -239,10 +249,51 @@ def test_split_stages_rules():
 
 def test_plan_picks_a_schedule_without_a_device():
     # no GPU here: the CU count reads as 0, and the choice is still valid
-    var, vs = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="fused"))
-    assert var == "fused" and vs in (2, 4)
-    var, vs = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="decomp", value_split=4))
-    assert (var, vs) == ("decomp", 4)
+    var, vs, parts = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="fused"))
+    assert var == "fused" and vs in (2, 4) and parts == 1
+    plan = K.plan(K.make_problem(8, 65536, 12, scale=0.088, variant="decomp", value_split=4))
+    assert plan == ("decomp", 4, 1)
+    # with no device known, AUTO splits no chain; a given chain_parts is kept
+    assert K.plan(K.make_problem(1, 8192, 12, scale=0.088))[2] == 1
+    assert K.plan(K.make_problem(1, 8192, 12, scale=0.088, chain_parts=5))[2] == 5
+
+
+def test_chain_split_workspace_and_rules():
+    # the chain area: 3 x 64 KiB per (sequence, head, piece), for the pieces
+    # given, or the most AUTO may pick; none when that is below 3
+    assert chain_cap(1, 8192, 12) == 11 and chain_cap(1, 512, 12) == 1
+    assert chain_cap(1, 8192, 2) == 16 and chain_cap(8, 8 * 8192, 12) == 1
+    assert chain_cap(4, 4 * 2048, 4) == 4
+    for N, T, H in [(1, 8192, 12), (1, 8192, 2), (1, 512, 12), (4, 4 * 2048, 4), (8, 65536, 12),
+                    (2, 40, 1)]:
+        for var in ("auto", "decomp"):
+            assert K.workspace_size(K.make_problem(N, T, H, scale=0.088, variant=var)) == \
+                decomp_bytes(N, T, H), (N, T, H, var)
+        for P in (1, 2, 3, 16):
+            p = K.make_problem(N, T, H, scale=0.088, variant="decomp", chain_parts=P)
+            assert K.workspace_size(p) == decomp_bytes(N, T, H, pieces=P)
+    with pytest.raises(K.KDAError):
+        K.workspace_size(K.make_problem(1, 8192, 12, scale=0.088, chain_parts=17))
+    with pytest.raises(K.KDAError):
+        K.workspace_size(K.make_problem(1, 8192, 12, scale=0.088, chain_parts=-1))
+    b = Bufs()
+    ws = 1 << 44
+
+    def val(p, wsp, wsb):
+        return K.validate_raw(p, *b.args()[:-2], wsp, wsb)
+
+    # FUSED runs no chain split
+    assert val(prob_for(b, variant="fused", chain_parts=1), 0, 0) == OK
+    assert val(prob_for(b, variant="fused", chain_parts=2), 0, 0) == UNSUPPORTED
+    # a given split needs its chain area
+    for P in (2, 5):
+        need = decomp_bytes(b.N, b.T, b.H, pieces=P)
+        for var in ("auto", "decomp"):
+            p = prob_for(b, variant=var, chain_parts=P)
+            assert val(p, ws, need) == OK
+            assert val(p, ws, need - 1) == WS
+    # AUTO runs unsplit in a workspace that holds only the slots
+    assert val(prob_for(b), ws, decomp_bytes(b.N, b.T, b.H, pieces=1)) == OK
 
 
 def test_python_binding_refuses_cpu_tensors():

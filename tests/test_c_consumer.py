@@ -54,7 +54,9 @@ def test_struct_layouts_match_the_binding(consumer_output, struct, name):
 def test_workspace_sizes_match_the_binding(consumer_output):
     probs = [K.make_problem(8, 8 * 8192, 12, scale=0.0884, variant="auto"),
              K.make_problem(5, 1000, 3, scale=0.0884, variant="decomp", ckpt_per_seq=3),
-             K.make_problem(8, 8 * 8192, 12, scale=0.0884, variant="fused")]
+             K.make_problem(8, 8 * 8192, 12, scale=0.0884, variant="fused"),
+             K.make_problem(1, 8192, 12, scale=0.0884, variant="auto"),
+             K.make_problem(1, 8192, 12, scale=0.0884, variant="decomp", chain_parts=4)]
     for i, p in enumerate(probs):
         status, nbytes = (int(x) for x in consumer_output[f"workspace.{i}"].split())
         assert status == 0

@@ -42,15 +42,24 @@ def _full_size_problems():
     return a, b
 
 
+def _few_pair_problems():
+    # two long sequences (H = 2) with one checkpoint each, for the chain split
+    # (its two recurrence launches and the scan between them in one graph)
+    a = synth.make_problem([3000, 1100], 2, seed=43, init_state=True, ckpt="inside", name="graph_few_a")
+    b = synth.make_problem([1700, 2400], 2, seed=44, init_state=True, ckpt="inside", name="graph_few_b")
+    assert a.T_total == b.T_total and a.N == b.N
+    return a, b
+
+
 @pytest.mark.parametrize("variant,size", [("decomp", "small"), ("fused", "small"), ("decomp", "full"),
-                                          ("fused", "full")])
+                                          ("fused", "full"), ("decomp", "split")])
 def test_graph_capture_and_replay_with_new_inputs(variant, size):
     import torch
     import kda_gated_delta_chunked_amd as K
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     dev = torch.device("cuda", 0)
-    pa, pb = _problems() if size == "small" else _full_size_problems()
+    pa, pb = {"small": _problems, "full": _full_size_problems, "split": _few_pair_problems}[size]()
     N, H, T = pa.N, pa.H, pa.T_total
 
     def dev_bf16(bits):
@@ -65,7 +74,8 @@ def test_graph_capture_and_replay_with_new_inputs(variant, size):
     out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
     fin = torch.empty((N, H, 128, 128), device=dev)
     ck = torch.empty((N, H, 128, 128), device=dev)
-    prob = K.make_problem(N, T, H, scale=pa.scale, variant=variant)
+    prob = K.make_problem(N, T, H, scale=pa.scale, variant=variant,
+                          chain_parts=5 if size == "split" else 0)
     need = K.workspace_size(prob)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 

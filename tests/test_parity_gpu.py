@@ -174,6 +174,100 @@ def test_slow_decay_packed_ragged_with_checkpoints(kind, variant):
             assert_parity(gpu, ref, f"slow {kind} packed", p.cu_seqlens))
 
 
+# The chain split of the two-launch schedule (kda_problem.chain_parts): each
+# (sequence, head)'s segments cut into P pieces, run from zero and from the
+# identity, composed by a scan, and run again from the composed states.
+
+@functools.lru_cache(maxsize=None)
+def _b1_t8192_h2(kind):
+    p = synth.make_problem([8192], 2, seed=41, fixed=True, init_state=True)
+    if kind != "random":
+        p = _slow_decay(p, kind, 42)
+    return p, oracle.prefill_problem(p)
+
+
+@pytest.mark.parametrize("pieces,vsplit", [(2, 2), (3, 2), (5, 2), (6, 2), (16, 2), (11, 1), (5, 4),
+                                           (3, 8)])
+def test_chain_split_full_length(pieces, vsplit):
+    # B1 T8192 H2: every (sequence, head) pair's outputs and state against
+    # the oracle, for piece counts from 2 (nothing side by side) to 16
+    p, ref = _b1_t8192_h2("random")
+    gpu = run_gpu(p, variant="decomp", value_split=vsplit, chain_parts=pieces)
+    _report(f"chain P{pieces} vs{vsplit} B1 T8192", assert_parity(gpu, ref, f"chain P{pieces}", p.cu_seqlens))
+
+
+@pytest.mark.parametrize("kind", ["zero", "weak", "skew"])
+def test_chain_split_slow_decay(kind):
+    # at slow decay a piece's transition is far from zero, so the scan carries
+    # the incoming state's rounding through every piece
+    p, ref = _b1_t8192_h2(kind)
+    gpu = run_gpu(p, variant="decomp", chain_parts=11)
+    _report(f"chain P11 slow decay {kind}", assert_parity(gpu, ref, f"chain {kind}", p.cu_seqlens))
+
+
+@pytest.mark.parametrize("pieces", [2, 4, 7])
+def test_chain_split_packed_checkpoints_and_empty(pieces):
+    # a packed batch with empty and one-token sequences (pieces with no
+    # segment: the identity and zero maps), several checkpoints per sequence
+    # landing in every piece, at 0 and at L
+    lens = [3000, 0, 1, 2047, 64, 700, 129]
+    offs = np.array([[0, 700, 1500, 2999, 3000],
+                     [0, -1, -1, -1, -1],
+                     [0, 1, -1, -1, -1],
+                     [1, 512, 1024, 1500, 2047],
+                     [64, 63, 64, -1, 0],
+                     [350, 351, 352, 699, 700],
+                     [65, 128, 129, 0, -1]], np.int32)
+    p = synth.make_problem(lens, 2, seed=43, init_state=True)
+    p.ckpt_offsets = offs
+    p0 = synth.make_problem(lens, 2, seed=43, init_state=True)
+    ref = oracle.prefill_problem(p0)
+    gpu = run_gpu(p, variant="decomp", chain_parts=pieces)
+    _report(f"chain P{pieces} packed", assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref,
+                                                     f"chain P{pieces} packed", p.cu_seqlens))
+    _check_multi_ckpt(p, offs, gpu)
+    # the empty sequence keeps its state bit for bit through the identity and
+    # zero maps; offset 0 exports the initial state and L the final state
+    assert np.array_equal(gpu["final"][1], p.initial_state[1])
+    assert np.array_equal(gpu["ckpt"][1, 0], p.initial_state[1])
+    assert np.array_equal(gpu["ckpt"][0, 0], p.initial_state[0])
+    assert np.array_equal(gpu["ckpt"][0, 4], gpu["final"][0])
+    assert np.array_equal(gpu["ckpt"][3, 4], gpu["final"][3])
+
+
+def test_chain_split_state_variants():
+    # bf16 states, the in-place state update with out over v, int64 offsets
+    # with a caller order: each through the split, against the oracle
+    lens = [2500, 0, 900, 1]
+    p = synth.make_problem(lens, 2, seed=44, init_state=True)
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant="decomp", chain_parts=5, out_alias_v=True, state_in_place=True)
+    _report("chain P5 in place", assert_parity(gpu, ref, "chain in place", p.cu_seqlens))
+    gpu = run_gpu(p, variant="decomp", chain_parts=5, cu64=True,
+                  seq_order=np.array([2, 0, 3, 1], np.int32))
+    _report("chain P5 int64 + order", assert_parity(gpu, ref, "chain int64", p.cu_seqlens))
+    pb = synth.make_problem(lens, 2, seed=44, init_state=True)
+    pb.initial_state = synth.f32_from_bf16_bits(synth.bf16_bits_from_f32(pb.initial_state))
+    refb = oracle.prefill_problem(pb)
+    gpu = run_gpu(pb, variant="decomp", chain_parts=5, state_bf16=True)
+    m = metrics(gpu, refb)
+    _report("chain P5 bf16 states", m)
+    assert m["out_rel_l2"] <= 5e-3 and m["final_rel_l2"] <= BF16_STATE_REL_L2, m
+    assert np.array_equal(gpu["final"][1], pb.initial_state[1])
+
+
+def test_chain_split_against_unsplit_and_deterministic():
+    # the split reorders the arithmetic only: results stay within the
+    # gates of the unsplit run, and repeat bit for bit
+    p = synth.make_problem([4000, 1500], 3, seed=45, init_state=True)
+    d = to_device(p)
+    one = run_gpu(p, variant="decomp", chain_parts=1, d=d)
+    a = run_gpu(p, variant="decomp", chain_parts=6, d=d)
+    b = run_gpu(p, variant="decomp", chain_parts=6, d=d)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["final"], b["final"])
+    assert rel_l2(a["final"], one["final"]) < 1e-3 and rel_l2(a["out"], one["out"]) < 5e-3
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_aliasing_out_v_and_state_in_place(variant):
     p = synth.make_problem([190, 64], 2, seed=13, init_state=True)
@@ -498,8 +592,9 @@ def test_auto_schedule_table():
     # AUTO takes the one-launch schedule for short sequences (mean <= 64
     # tokens) whose workgroups all fit on the device at once, else the
     # two-launch schedule (four workgroups per pair when they fit at once and
-    # the workspace is past 176 MiB); its results are those of the schedule
-    # it names
+    # the workspace is past 176 MiB), with the chain split where its cost
+    # model says it pays (few pairs, long sequences); its results are those
+    # of the schedule it names
     import torch
     import kda_gated_delta_chunked_amd as K
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -508,23 +603,32 @@ def test_auto_schedule_table():
         pairs = N * H
         vs = 4 if pairs * 2 < cus // 2 else 2
         if T // N <= 64 and pairs * vs <= cus:
-            return ("fused", vs)
-        ws = K.workspace_size(K.make_problem(N, T, H, scale=0.088, variant="decomp"))
-        return ("decomp", 4 if pairs * 4 <= cus and ws > (176 << 20) else 2)
+            return ("fused", vs, 1)
+        ws = K.workspace_size(K.make_problem(N, T, H, scale=0.088, variant="decomp", chain_parts=1))
+        return ("decomp", 4 if pairs * 4 <= cus and ws > (176 << 20) else 2, 1)
 
+    # shapes with many pairs or short sequences: no chain split
     for N, T, H, kw in [(1, 64, 12, {}), (8, 8 * 64, 12, {}), (8, 8 * 128, 12, {}),
                         (8, 8 * 192, 12, {}), (16, 16 * 128, 12, {}), (32, 32 * 64, 12, {}),
                         (8, 8 * 8192, 12, {}), (8, 8 * 64, 12, {"qk_l2norm": True}),
-                        (1, 8192, 12, {}), (2, 2 * 8192, 12, {}), (1, 32768, 12, {})]:
+                        (1, 512, 12, {}), (4, 4 * 2048, 12, {}), (6, 6 * 8192, 12, {})]:
         got = K.plan(K.make_problem(N, T, H, scale=0.088, **kw))
         assert got == expect(N, T, H, **kw), (N, T, H, kw, got)
+    # a given chain_parts is kept
+    assert K.plan(K.make_problem(8, 8 * 8192, 12, scale=0.088, chain_parts=3))[2] == 3
     if cus == 256:
-        assert K.plan(K.make_problem(8, 8 * 64, 12, scale=0.088)) == ("fused", 2)
+        assert K.plan(K.make_problem(8, 8 * 64, 12, scale=0.088)) == ("fused", 2, 1)
         assert K.plan(K.make_problem(8, 8 * 128, 12, scale=0.088))[0] == "decomp"
         assert K.plan(K.make_problem(16, 16 * 128, 12, scale=0.088))[0] == "decomp"
-        assert K.plan(K.make_problem(1, 8192, 12, scale=0.088)) == ("decomp", 2)
-        assert K.plan(K.make_problem(2, 2 * 8192, 12, scale=0.088)) == ("decomp", 4)
-        assert K.plan(K.make_problem(8, 8 * 8192, 12, scale=0.088)) == ("decomp", 2)
+        assert K.plan(K.make_problem(8, 8 * 8192, 12, scale=0.088)) == ("decomp", 2, 1)
+        # few pairs: the split (measured on MI355X, us per call unsplit ->
+        # split: B1 T8192 261 -> 141, B2 T8192 309 -> 231, B1 T32768 1026 -> 457)
+        assert K.plan(K.make_problem(1, 8192, 12, scale=0.088)) == ("decomp", 2, 11)
+        assert K.plan(K.make_problem(2, 2 * 8192, 12, scale=0.088)) == ("decomp", 2, 6)
+        assert K.plan(K.make_problem(1, 32768, 12, scale=0.088)) == ("decomp", 2, 11)
+        assert K.plan(K.make_problem(4, 4 * 2048, 12, scale=0.088)) == ("decomp", 2, 1)
+        # value_split given: the split runs with it
+        assert K.plan(K.make_problem(1, 8192, 12, scale=0.088, value_split=1)) == ("decomp", 1, 11)
     p = synth.make_problem([64] * 8, 12, seed=1005, init_state=True, name="packed_64x8")
     ref = oracle.prefill_problem(p)
     auto = run_gpu(p, variant="auto")
@@ -533,19 +637,21 @@ def test_auto_schedule_table():
     _report("packed_64x8 auto", assert_parity(auto, ref, "packed_64x8 auto", p.cu_seqlens))
 
 
-def test_auto_four_workgroups_full_size():
-    # B2 T8192 H12: the workspace (192 MiB) is past the Infinity Cache bound,
-    # so AUTO runs the recurrence with four workgroups per pair
+@pytest.mark.parametrize("N,T,plan256", [(2, 8192, ("decomp", 2, 6)), (1, 8192 * 4, ("decomp", 2, 11)),
+                                          (1, 2048, ("decomp", 2, 4))])
+def test_auto_full_size_few_pairs(N, T, plan256):
+    # few (sequence, head) pairs at full length: AUTO's chain split (and its
+    # workspace from kda_prefill_workspace_size) against the oracle, per pair
     import torch
     import kda_gated_delta_chunked_amd as K
-    p = synth.make_problem([8192] * 2, 12, seed=1006, fixed=True, init_state=True, name="b2_t8192")
+    p = synth.make_problem([T] * N, 12, seed=1006, fixed=True, init_state=True, name=f"b{N}_t{T}")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     plan = K.plan(K.make_problem(p.N, p.T_total, p.H, scale=p.scale))
     if cus == 256:
-        assert plan == ("decomp", 4)
+        assert plan == plan256
     ref = oracle.prefill_problem(p)
     gpu = run_gpu(p, variant="auto")
-    _report(f"b2_t8192 auto {plan}", assert_parity(gpu, ref, "b2_t8192"))
+    _report(f"b{N}_t{T} auto {plan}", assert_parity(gpu, ref, f"b{N}_t{T}", p.cu_seqlens))
 
 
 def _random_case(seed):
@@ -577,17 +683,20 @@ def _random_case(seed):
     if qk:
         p = _raw_inputs(p, 9200 + seed)
     p.beta = rng.normal(0, 1.5, beta.shape).astype(np.float32) if bl else beta
-    return p, offs, variant, vs, qk, bl
+    # the two-launch schedule's chain split (0: the library's choice)
+    pieces = int(rng.choice([0, 0, 2, 3, 5, 9])) if variant == "decomp" else 0
+    return p, offs, variant, vs, qk, bl, pieces
 
 
 @pytest.mark.parametrize("seed", range(32))
 def test_random_problems(seed):
-    p, offs, variant, vs, qk, bl = _random_case(seed)
+    p, offs, variant, vs, qk, bl, pieces = _random_case(seed)
     ref = oracle.prefill_problem(p, qk_l2norm=qk, beta_logit=bl)
     if offs is not None:
         p.ckpt_offsets = offs
-    gpu = run_gpu(p, variant=variant, value_split=vs, qk_l2norm=qk, beta_logit=bl)
-    what = (f"seed {seed}: lens {list(p.seq_lens)} H {p.H} {variant} vs{vs} "
+    gpu = run_gpu(p, variant=variant, value_split=vs, qk_l2norm=qk, beta_logit=bl,
+                  chain_parts=pieces)
+    what = (f"seed {seed}: lens {list(p.seq_lens)} H {p.H} {variant} vs{vs} P{pieces} "
             f"C {0 if offs is None else offs.shape[1]} prologue {int(qk)}{int(bl)}")
     assert_parity({"out": gpu["out"], "final": gpu["final"]}, ref, what, p.cu_seqlens)
     if offs is not None:
