@@ -877,7 +877,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 // a compute wave reads only LDS.  One barrier per segment hands the buffers
 // over.
 
-template <int CW, int KW>
+template <int CW, int KW, bool SPLIT>
 __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(DecompArgs a) {
   constexpr int WAVES = CW;
   // with at most two waves per SIMD (one compute, one copy) a compute wave has
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   // first split launch both ZERO and EYE) on one XCD so they share L2
   const int bx = blockIdx.x, xcd = bx & 7, rest = bx >> 3;
   int pair, cg, piece = 0, role = MAIN;
-  if (a.pass == 0) {
+  if constexpr (!SPLIT) {
     pair = (rest / VG) * 8 + xcd;
     cg = rest % VG;
     if (pair >= a.N * H) return;
@@ -943,10 +943,10 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   const int rank = pair / H, h = pair - rank * H;
   const int n = a.order ? a.order[rank] : rank;
   const int64_t spair = (int64_t)n * H + h;  // the pair's index in the state layouts
-  const bool emit = role == MAIN || role == CONT;
+  const bool emit = !SPLIT || role == MAIN || role == CONT;
   // V's weight: EYE runs with V = 0 (the V block is still copied; finite
   // bf16 values times 0 give 0)
-  const float vmul = role == EYE ? 0.f : 1.f;
+  const float vmul = SPLIT && role == EYE ? 0.f : 1.f;
   // the wave index as a scalar: the role branch below is then uniform, so the
   // compiler keeps the two roles' code paths (and their memory counters) apart
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, q = lane & 15;
@@ -958,7 +958,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   if (base + nseg > a.slot_bound) nseg = base >= a.slot_bound ? 0 : (int)(a.slot_bound - base);
   // the piece's segments [j0, j1) (all of them without the split)
   int j0 = 0;
-  if (a.pass != 0) {
+  if constexpr (SPLIT) {
     j0 = (int)((int64_t)piece * nseg / a.pieces);
     const int j1 = (int)((int64_t)(piece + 1) * nseg / a.pieces);
     base += j0;
@@ -1071,20 +1071,21 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   // S holds 2^sexp times the state (sexp is the wave's operand scale exponent)
   f32x4 S[8];
   int sexp = 0;
-  if (role == MAIN && a.s0 && a.state_bf16) {
+  if ((!SPLIT || role == MAIN) && a.s0 && a.state_bf16) {
     const uint16_t* s0 = reinterpret_cast<const uint16_t*>(a.s0);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[m][e] = bf2f(s0[sbase + (size_t)srow(m, e) * DK]);
-  } else if ((role == MAIN && a.s0) || role == CONT) {
-    const float* src = role == MAIN ? a.s0 + sbase
-                                    : a.chain + chain_matrix(spair, a.pieces, piece, 0) + (sbase - (size_t)spair * DK * DK);
+  } else if (((!SPLIT || role == MAIN) && a.s0) || (SPLIT && role == CONT)) {
+    const float* src = !SPLIT || role == MAIN
+                           ? a.s0 + sbase
+                           : a.chain + chain_matrix(spair, a.pieces, piece, 0) + (sbase - (size_t)spair * DK * DK);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[m][e] = src[(size_t)srow(m, e) * DK];
-  } else if (role == EYE) {
+  } else if (SPLIT && role == EYE) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -1131,7 +1132,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
       *reinterpret_cast<float4*>(colp + srow(m, 0)) =
           make_float4(S[m][0] * unscale, S[m][1] * unscale, S[m][2] * unscale, S[m][3] * unscale);
   };
-  if (role == MAIN)
+  if (!SPLIT || role == MAIN)
     for_each_honoured(si.ck, [&](int c, int p) {
       if (p == 0) store_state(a.ckpt, ckpt_slot(c));
     });
@@ -1403,14 +1404,18 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   }
   // the end state: the result, or what the chain scan takes (as offsets from
   // the pair's own state offset, which store_state adds)
-  const size_t own = (size_t)spair * DK * DK;
-  if (role == EYE) {
-    store_transition(a.chain + chain_matrix(spair, a.pieces, piece, 2));
-  } else if (role == ZERO) {
-    store_state(a.chain, chain_matrix(spair, a.pieces, piece, 1) - own, false);
-  } else if (role == MAIN && a.pass == 1) {
-    store_state(a.chain, chain_matrix(spair, a.pieces, 1, 0) - own, false);
-  } else if (a.final_state && (a.pass == 0 || piece == a.pieces - 1)) {
+  if constexpr (SPLIT) {
+    const size_t own = (size_t)spair * DK * DK;
+    if (role == EYE) {
+      store_transition(a.chain + chain_matrix(spair, a.pieces, piece, 2));
+    } else if (role == ZERO) {
+      store_state(a.chain, chain_matrix(spair, a.pieces, piece, 1) - own, false);
+    } else if (role == MAIN) {
+      store_state(a.chain, chain_matrix(spair, a.pieces, 1, 0) - own, false);
+    } else if (a.final_state && piece == a.pieces - 1) {
+      store_state(a.final_state, 0);
+    }
+  } else if (a.final_state) {
     store_state(a.final_state, 0);
   }
 }
@@ -1534,7 +1539,7 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.N * a.H;
   if (a.pieces < 2) {
     const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * VG));
-    hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), grid, dim3(64 * (CW + KW)), 0, stream, a);
+    hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, false>), grid, dim3(64 * (CW + KW)), 0, stream, a);
     return hipGetLastError();
   }
   // the split: groups of (pair, piece), P - 1 per pair in each launch; a
@@ -1542,7 +1547,7 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
   const int64_t groups = pairs * (a.pieces - 1);
   DecompArgs b = a;
   b.pass = 1;
-  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), dim3((unsigned)(((groups + 7) / 8) * 8 * 2 * VG)),
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, true>), dim3((unsigned)(((groups + 7) / 8) * 8 * 2 * VG)),
                      dim3(64 * (CW + KW)), 0, stream, b);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1552,7 +1557,7 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   b.pass = 2;
-  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW>), dim3((unsigned)(((groups + 7) / 8) * 8 * VG)),
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, true>), dim3((unsigned)(((groups + 7) / 8) * 8 * VG)),
                      dim3(64 * (CW + KW)), 0, stream, b);
   return hipGetLastError();
 }
