@@ -160,8 +160,8 @@ bool fused_is_faster(const kda_problem* p, int cus) {
 // Cost model of the recurrence, in segment times of the unsplit two-
 // workgroup schedule, fitted to MI355X measurements (256 CUs; H = 12 unless
 // stated; recurrence us unsplit -> split, vsplit, pieces):
-//   B1 T8192      223 -> 98   (2, 6) / 98 (2, 11) / 96 (1, 11)
-//   B2 T8192      227 -> 147  (2, 6); 168 (2, 5); 175 (2, 11)
+//   B1 T8192      212 -> 96   (2, 6) / 93 (2, 11) / 92 (1, 11)
+//   B2 T8192      224 -> 145  (2, 6); 167 (2, 5); 172 (2, 11)
 //   B1 T32768     875 -> 305  (2, 11); 343 (2, 6)
 //   B1 T2048       61 -> 51   (2, 5)
 //   B1 T8192 H32  226 -> 178  (2, 3); 188 (2, 5)
@@ -171,7 +171,7 @@ bool fused_is_faster(const kda_problem* p, int cus) {
 // CU, so a launch of G groups of W workgroups takes ceil(ceil(G / 8) W /
 // (CUs / 8)) rounds.  The split adds its scan (P - 2 steps) and two launches.
 double seg_cost(int vsplit) { return vsplit == 1 ? 1.6 : (vsplit == 2 ? 1.0 : 1.05); }
-constexpr double kScanStepCost = 1.2;   // one scan step (2.1 us), in segment times (1.74 us)
+constexpr double kScanStepCost = 0.85;  // one scan step (1.5 us), in segment times (1.74 us)
 constexpr double kSplitCost = 6.0;      // the extra launches and per-run start-up
 
 int64_t rounds(int64_t groups, int per_group, int cus) {

@@ -957,6 +957,7 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   int nseg = si.nseg;
   if (base + nseg > a.slot_bound) nseg = base >= a.slot_bound ? 0 : (int)(a.slot_bound - base);
   // the piece's segments [j0, j1) (all of them without the split)
+  const int nseg_all = nseg;
   int j0 = 0;
   if constexpr (SPLIT) {
     j0 = (int)((int64_t)piece * nseg / a.pieces);
@@ -1071,16 +1072,18 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   // S holds 2^sexp times the state (sexp is the wave's operand scale exponent)
   f32x4 S[8];
   int sexp = 0;
-  if ((!SPLIT || role == MAIN) && a.s0 && a.state_bf16) {
+  // a sequence with no segment keeps its initial state bit for bit, also
+  // through the split (the scan's hi + lo products keep 16 bits)
+  const bool from_s0 = !SPLIT || role == MAIN || (role == CONT && nseg_all == 0);
+  if (from_s0 && a.s0 && a.state_bf16) {
     const uint16_t* s0 = reinterpret_cast<const uint16_t*>(a.s0);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[m][e] = bf2f(s0[sbase + (size_t)srow(m, e) * DK]);
-  } else if (((!SPLIT || role == MAIN) && a.s0) || (SPLIT && role == CONT)) {
-    const float* src = !SPLIT || role == MAIN
-                           ? a.s0 + sbase
-                           : a.chain + chain_matrix(spair, a.pieces, piece, 0) + (sbase - (size_t)spair * DK * DK);
+  } else if ((from_s0 && a.s0) || (SPLIT && role == CONT && !from_s0)) {
+    const float* src = from_s0 ? a.s0 + sbase
+                               : a.chain + chain_matrix(spair, a.pieces, piece, 0) + (sbase - (size_t)spair * DK * DK);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -1120,17 +1123,24 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
   };
   // checkpoint c of this sequence (layout [N, C, H, K, V]): element offset
   auto ckpt_slot = [&](int c) { return ((size_t)n * (a.ckpt_per_seq - 1) + c) * (size_t)H * DK * DK; };
-  // the piece's state transition, transposed (row = the state's column):
-  // each lane's four consecutive rows of a column go out as one 16-byte store
+  // the piece's state transition T (EYE's end state; row = key channel, as
+  // the state), for the scan's matrix products: bf16 hi and lo parts
+  // (T = hi + lo to 16 bits), [K][K] row-major, hi then lo
   auto store_transition = [&](float* mat) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    float* colp = mat + (size_t)(col0 + (ln & 15)) * DK + (ln >> 4) * 8;
+    uint16_t* hi = reinterpret_cast<uint16_t*>(mat) + col0 + (ln & 15) + (size_t)((ln >> 4) * 8) * DK;
+    uint16_t* lo = hi + DK * DK;
     const float unscale = pow2f(-sexp);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      *reinterpret_cast<float4*>(colp + srow(m, 0)) =
-          make_float4(S[m][0] * unscale, S[m][1] * unscale, S[m][2] * unscale, S[m][3] * unscale);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = S[m][e] * unscale;
+        const uint32_t h = pack2(x, 0.f) & 0xffffu;
+        hi[srow(m, e) * DK] = (uint16_t)h;
+        lo[srow(m, e) * DK] = (uint16_t)pack2(x - bf2f(h), 0.f);
+      }
   };
   if (!SPLIT || role == MAIN)
     for_each_honoured(si.ck, [&](int c, int p) {
@@ -1423,107 +1433,140 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
 // ---------------------------------------------------------------------------
 // Chain scan, between the split's two recurrence launches: the state entering
 // piece p + 1 is T_p S_p + B_p for p = 1 .. P-2 (S_1 from the first launch's
-// MAIN run; T_p stored transposed, B_p from ZERO).  Columns of the state are
-// independent, so one workgroup takes 16 columns of one (sequence, head) pair
-// through all the steps, on the fp32 matrix cores (16x16x4 products, fp32
-// accumulation; vector FMAs would be bound by LDS reads of the operands).
-// Wave w owns rows 32 w .. 32 w + 31 as two 16-row tiles, interleaved (tile t
-// row i is state row 32 w + 2 i + t), so one 8-byte LDS read gives a lane its
-// A operands for both tiles.  The steps are latency-bound: T_{p+1}^T streams
-// into one LDS buffer (direct global-to-LDS loads) while step p computes from
-// the other; the buffers are separate arrays and the steps alternate between
-// them by name, so the compiler sees that reads of one do not wait for the
-// copies into the other.
+// MAIN run; T_p from EYE as bf16 hi + lo, B_p from ZERO).  Columns of the
+// state are independent, so one workgroup takes 16 columns of one (sequence,
+// head) pair through all the steps.  T_p S_p runs on the matrix cores as
+// three bf16 products, Th Sh + Th Sl + Tl Sh (16x16x32, fp32 accumulation);
+// the Tl Sl term dropped is about 2^-16 of the result, far below the fp32
+// state's own rounding over a piece.  Wave w owns rows 32 w .. 32 w + 31 (two
+// 16-row tiles).  T_{p+1} streams into one LDS buffer (direct global-to-LDS
+// loads) while step p computes from the other; the buffers are separate
+// arrays and the steps alternate between them by name, so the compiler sees
+// that reads of one do not wait for the copies into the other.  In LDS a row
+// of T (256 bytes per part) keeps its 16-byte pieces XOR-swizzled by the row
+// index, and so does S^T, so that a fragment read, 16 rows at one k, hits 16
+// different bank groups.
 constexpr int kScanCols = 16;
 constexpr int kScanThreads = 256;
 
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
 __global__ __launch_bounds__(kScanThreads) void kda_chain_scan_kernel(DecompArgs a) {
-  __shared__ __attribute__((aligned(16))) uint4 TA[DK * DK / 4];
-  __shared__ __attribute__((aligned(16))) uint4 TB[DK * DK / 4];
-  __shared__ __attribute__((aligned(16))) float Sc[DK * kScanCols];  // [k][16 columns]
+  __shared__ __attribute__((aligned(16))) uint4 TA[DK * DK * 4 / 16];  // hi, then lo: [K][K] bf16
+  __shared__ __attribute__((aligned(16))) uint4 TB[DK * DK * 4 / 16];
+  __shared__ __attribute__((aligned(16))) uint4 St[kScanCols * DK * 4 / 16];  // S^T hi, lo: [16][K] bf16
   // a pair's 8 column groups on one XCD (workgroups are dealt to the 8 XCDs
-  // round-robin), so that T_p^T is fetched into that XCD's L2 once
+  // round-robin), so that T_p is fetched into that XCD's L2 once
   static_assert(DK / kScanCols == 8, "one column group per XCD slot");
   const int bx = blockIdx.x, xcd = bx & 7, slot = bx >> 3;
   const int64_t pair = (int64_t)(slot >> 3) * 8 + xcd;
   const int c0 = (slot & 7) * kScanCols;
   if (pair >= (int64_t)a.N * a.H || a.pieces < 3) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, q = lane & 15, g4 = lane >> 4;
-  // T_p^T (64 KiB): wave w brings 1 KiB units w, w + 4, ... into dst
+  constexpr int PART = DK * DK * 2;  // bytes of one bf16 part of T
+  // T_p (64 KiB: hi then lo), 1 KiB units, wave w taking units w, w + 4, ...;
+  // LDS byte o holds row o / 256 of its part, swizzled piece (o % 256) / 16
   auto fetch = [&](int p, uint4* dst) {
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.chain + chain_matrix(pair, a.pieces, p, 2));
 #pragma unroll
-    for (int i = 0; i < DK * DK * 4 / 1024 / (kScanThreads / 64); ++i) {
+    for (int i = 0; i < 2 * PART / 1024 / (kScanThreads / 64); ++i) {
       const int u = w + (kScanThreads / 64) * i;
-      __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, dst + u * 64, 16, 0, 0);
+      const int o = u * 1024 + lane * 16, part = o / PART, r = (o % PART) >> 8, pc = (o >> 4) & 15;
+      __builtin_amdgcn_global_load_lds(src + part * PART + r * 256 + ((pc ^ (r & 15)) << 4), dst + u * 64, 16, 0,
+                                       0);
     }
   };
-  // the lane's output elements: column c0 + q, rows row(t, e) of tile t
-  auto row = [&](int tile, int e) { return 32 * w + 2 * (4 * g4 + e) + tile; };
+  // the lane's outputs: column c0 + q, rows r0(tile) + 4 g4 + e
+  auto r0 = [&](int tile) { return 32 * w + 16 * tile; };
   auto load_b = [&](int p, f32x4& b0, f32x4& b1) {
     const float* bp = a.chain + chain_matrix(pair, a.pieces, p, 1) + c0 + q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      b0[e] = bp[(size_t)row(0, e) * DK];
-      b1[e] = bp[(size_t)row(1, e) * DK];
+      b0[e] = bp[(size_t)(r0(0) + 4 * g4 + e) * DK];
+      b1[e] = bp[(size_t)(r0(1) + 4 * g4 + e) * DK];
     }
   };
+  // S'^T hi and lo into St: the lane's 4 rows are 4 consecutive k of column q
+  auto put_s = [&](int tile, const f32x4& v) {
+    const int k = r0(tile) + 4 * g4;
+    const uint32_t h0 = pack2(v[0], v[1]), h1 = pack2(v[2], v[3]);
+    const uint32_t l0 = pack2(v[0] - lo_of(h0), v[1] - hi_of(h0)), l1 = pack2(v[2] - lo_of(h1), v[3] - hi_of(h1));
+    unsigned char* sb = reinterpret_cast<unsigned char*>(St) + swz(q, k >> 3) + (k & 4) * 2;
+    *reinterpret_cast<uint2*>(sb) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2*>(sb + kScanCols * DK * 2) = make_uint2(l0, l1);
+  };
   auto step = [&](int p, const uint4* cur, uint4* nxt, f32x4& b0, f32x4& b1) {
-    f32x4 acc0 = b0, acc1 = b1;
+    f32x4 acc[2][3];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      acc[tile][0] = tile ? b1 : b0;
+      acc[tile][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      acc[tile][2] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
     if (p + 2 < a.pieces) {
       fetch(p + 1, nxt);
       load_b(p + 1, b0, b1);
     }
-    const float* Tt = reinterpret_cast<const float*>(cur);
-    // all operands read first (96 registers), then the 64 products back to
-    // back: the reads' latency is paid once, not once per pair of k-steps
-    float2 av[DK / 4];
-    float bv[DK / 4];
+    const unsigned char* tb = reinterpret_cast<const unsigned char*>(cur);
+    const unsigned char* sb = reinterpret_cast<const unsigned char*>(St);
 #pragma unroll
-    for (int ks = 0; ks < DK / 4; ++ks) {
-      const int k = 4 * ks + g4;
-      av[ks] = *reinterpret_cast<const float2*>(Tt + k * DK + 32 * w + 2 * q);
-      bv[ks] = Sc[k * kScanCols + q];
-    }
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const int ch = 4 * kb + g4;  // 16-byte piece: k = 8 ch .. 8 ch + 7
+      const bf16x8 sh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + swz(q, ch)));
+      const bf16x8 sl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + kScanCols * DK * 2 + swz(q, ch)));
 #pragma unroll
-    for (int ks = 0; ks < DK / 4; ++ks) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks].x, bv[ks], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks].y, bv[ks], acc1, 0, 0, 0);
+      for (int tile = 0; tile < 2; ++tile) {
+        const int r = r0(tile) + q;
+        const bf16x8 th = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + swz(r, ch)));
+        const bf16x8 tl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + PART + swz(r, ch)));
+        acc[tile][0] = mfma(th, sh, acc[tile][0]);
+        acc[tile][1] = mfma(th, sl, acc[tile][1]);
+        acc[tile][2] = mfma(tl, sh, acc[tile][2]);
+      }
     }
-    // every wave is done reading Sc and `cur` (its reads have returned: the
+    f32x4 res[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[tile][e] = acc[tile][0][e] + (acc[tile][1][e] + acc[tile][2][e]);
+    // every wave is done reading St and `cur` (its reads have returned: the
     // products used them); the copies into `nxt` stay in flight, so no
     // workgroup-scope fence, whose release would wait for them
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Sc[row(0, e) * kScanCols + q] = acc0[e];
-      Sc[row(1, e) * kScanCols + q] = acc1[e];
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of T_{p+1}^T landed
-    lds_barrier();                       // every wave's part landed; Sc holds S_{p+1}
+    put_s(0, res[0]);
+    put_s(1, res[1]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of T_{p+1} landed
+    lds_barrier();                       // every wave's part landed; St holds S_{p+1}
     // S_{p+1} for the second launch, stored after the wait above so that it
     // covers the copies only; the next step's wait finds these done
     float* dst = a.chain + chain_matrix(pair, a.pieces, p + 1, 0) + c0 + q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dst[(size_t)row(0, e) * DK] = acc0[e];
-      dst[(size_t)row(1, e) * DK] = acc1[e];
+      dst[(size_t)(r0(0) + 4 * g4 + e) * DK] = res[0][e];
+      dst[(size_t)(r0(1) + 4 * g4 + e) * DK] = res[1][e];
     }
   };
   fetch(1, TA);
   f32x4 b0, b1;
   load_b(1, b0, b1);
   {
-    // S_1's 16 columns: thread t takes row t / 2, columns 8 (t & 1) .. + 7
-    const float4* s1 = reinterpret_cast<const float4*>(a.chain + chain_matrix(pair, a.pieces, 1, 0) +
-                                                       (size_t)(t >> 1) * DK + c0 + 8 * (t & 1));
+    // S_1's 16 columns, split: thread t takes row (k) t / 2, columns 8 (t & 1) .. + 7
+    const int k = t >> 1, cb = 8 * (t & 1);
+    const float4* s1 = reinterpret_cast<const float4*>(a.chain + chain_matrix(pair, a.pieces, 1, 0) + (size_t)k * DK +
+                                                       c0 + cb);
     const float4 x = s1[0], y = s1[1];
-    float4* sd = reinterpret_cast<float4*>(Sc + (t >> 1) * kScanCols + 8 * (t & 1));
-    sd[0] = x;
-    sd[1] = y;
+    const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    unsigned char* sb = reinterpret_cast<unsigned char*>(St);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = pack2(v[j], 0.f) & 0xffffu;
+      const int off = swz(cb + j, k >> 3) + (k & 7) * 2;
+      *reinterpret_cast<uint16_t*>(sb + off) = (uint16_t)h;
+      *reinterpret_cast<uint16_t*>(sb + kScanCols * DK * 2 + off) = (uint16_t)pack2(v[j] - bf2f(h), 0.f);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();

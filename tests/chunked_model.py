@@ -293,14 +293,24 @@ def prefill_problem(p, **kw):
                    ckpt_offsets=p.ckpt_offsets, **kw)
 
 
-def prefill_chain(p, pieces, *, emulate=False, recipe=None, chunk=64):
+def _scan_bf16x3(T, S):
+    """T S from bf16 hi + lo parts of both, the lo x lo product dropped
+    (products exact, sums in fp32)."""
+    Th = bf16(T); Tl = bf16(np.asarray(T, np.float32) - Th)
+    Sh = bf16(S); Sl = bf16(np.asarray(S, np.float32) - Sh)
+    f = lambda a, b: (np.asarray(a, np.float64) @ np.asarray(b, np.float64)).astype(np.float32)
+    return f(Th, Sh) + f(Th, Sl) + f(Tl, Sh)
+
+
+def prefill_chain(p, pieces, *, emulate=False, recipe=None, chunk=64, scan="fp32"):
     """The chain split of the two-launch schedule on a synth.Problem without
     checkpoints.  Each (sequence, head)'s chunks are cut into `pieces`
     ranges [floor(i n / P), floor((i + 1) n / P)); piece 0 runs from the
     initial state; pieces 1..P-2 run from a zero state (V as given: the
     affine part B_i) and from the identity with V = 0 (the transition T_i,
     a K x K matrix, as a K x V state with V = K columns); the incoming states
-    follow from S_{i+1} = T_i S_i + B_i in the state's precision; pieces
+    follow from S_{i+1} = T_i S_i + B_i in the state's precision (scan
+    "bf16x3": T_i S_i from bf16 hi + lo parts, the lo x lo term dropped); pieces
     1..P-1 run again from them with outputs.  Every run starts with fresh
     operand scale exponents, as each workgroup does.  Returns dict(out,
     final)."""
@@ -335,7 +345,8 @@ def prefill_chain(p, pieces, *, emulate=False, recipe=None, chunk=64):
                 Ti, _ = run(np.eye(K, dtype=dt), h, piece_cuts[i], zero_v=True)
                 Bi, _ = run(np.zeros((K, V), dt), h, piece_cuts[i])
                 start = S_in
-                S_in = (Ti @ start + Bi).astype(dt)
+                TS = _scan_bf16x3(Ti, start) if scan == "bf16x3" else Ti @ start
+                S_in = (TS + Bi).astype(dt)
                 # outputs of piece i come from the run from its true state
                 _, outs = run(start, h, piece_cuts[i])
                 for c0, c1, O in outs:
