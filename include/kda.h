@@ -152,7 +152,8 @@ typedef struct {
                                 chain P times shorter, for problems with too few pairs to fill
                                 the device (FlashInfer PR #4633, Performance: the B1 T8192 row
                                 is the recurrence's chain alone).  Results equal the unsplit
-                                recurrence's up to rounding.  FUSED takes 0 or 1 only */
+                                recurrence's up to rounding.  FUSED takes 0 or 1 only; with
+                                AUTO, 2 or more selects DECOMP (as value_split 1 and 8 do) */
 } kda_problem;
 
 #define KDA_MAX_CHAIN_PARTS 16

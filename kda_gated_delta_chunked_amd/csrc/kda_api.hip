@@ -151,7 +151,7 @@ int fused_vsplit(const kda_problem* p, int cus) {
 // B8 T128 27.6 / 31.8, packed 8 x 128 32.6 / 32.2, B8 T192 34.0 / 43.8,
 // B16 T128 40.6 / 59.5, B32 T64 45.4 / 55.0.
 bool fused_is_faster(const kda_problem* p, int cus) {
-  if (cus <= 0 || p->value_split == 1 || p->value_split == 8) return false;
+  if (cus <= 0) return false;
   const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
   const int64_t mean_len = p->total_tokens / p->num_seqs;
   return mean_len <= 64 && pairs * fused_vsplit(p, cus) <= cus;
@@ -219,10 +219,11 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
   int32_t var = p->variant;
   *pieces = 1;
   if (var == KDA_VARIANT_AUTO) {
+    // value_split 1 and 8 and a chain split exist only in DECOMP
+    const bool decomp_only = p->value_split == 1 || p->value_split == 8 || p->chain_parts > 1;
     var = ws_bytes >= decomp_bytes(p, 1) ? KDA_VARIANT_DECOMP : KDA_VARIANT_FUSED;
-    if (var == KDA_VARIANT_FUSED && (p->value_split == 1 || p->value_split == 8))
-      var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
-    if (var == KDA_VARIANT_DECOMP && fused_is_faster(p, cus)) var = KDA_VARIANT_FUSED;
+    if (var == KDA_VARIANT_FUSED && decomp_only) var = KDA_VARIANT_DECOMP;  // rejected later by the workspace check
+    if (var == KDA_VARIANT_DECOMP && !decomp_only && fused_is_faster(p, cus)) var = KDA_VARIANT_FUSED;
   }
   *variant = var;
   if (var == KDA_VARIANT_FUSED) {

@@ -294,6 +294,10 @@ def test_chain_split_workspace_and_rules():
             assert val(p, ws, need - 1) == WS
     # AUTO runs unsplit in a workspace that holds only the slots
     assert val(prob_for(b), ws, decomp_bytes(b.N, b.T, b.H, pieces=1)) == OK
+    # a given split pins AUTO to DECOMP: with no workspace it is refused, not
+    # run as FUSED, and the plan says DECOMP
+    assert val(prob_for(b, chain_parts=3), 0, 0) == WS
+    assert K.plan(prob_for(b, chain_parts=3))[::2] == ("decomp", 3)
 
 
 def test_python_binding_refuses_cpu_tensors():
