@@ -279,6 +279,73 @@ kda_status scratch_address(void** addr) {
 
 }  // namespace
 
+namespace {
+
+// kda_decode_validate's checks, and for a verify the state trace as well
+kda_status decode_check(const kda_decode_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* state_pool,
+                        const int32_t* state_indices, const void* out, const float* trace,
+                        bool verify) {
+  if (!p) return KDA_ERR_INVALID_ARG;
+  if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
+  if (p->num_seqs < 0 || p->tokens_per_seq < 1 || p->num_heads < 1 || p->pool_size < 1)
+    return KDA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale)) return KDA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->gate_lower_bound) || p->gate_lower_bound < -5.0f ||
+      p->gate_lower_bound > 0.0f)
+    return KDA_ERR_INVALID_ARG;
+  if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
+  const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
+  if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
+  if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out))
+    return KDA_ERR_INVALID_ARG;
+  if (verify && N > 0 && !trace) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, state_pool, state_indices, out, trace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
+  const uint64_t tok_bf16 = (uint64_t)N * T * H * kHeadDim * 2;
+  const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
+  const Range rg = range_of(g, tok_bf16 * 2), rb = range_of(beta, (uint64_t)N * T * H * 4);
+  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
+  const Range ridx = range_of(state_indices, (uint64_t)N * 4);
+  const Range rout = range_of(out, tok_bf16);
+  for (const Range& r : {rq, rk, rg, rb, rpool, ridx})
+    if (overlaps(rout, r)) return KDA_ERR_OVERLAP;
+  if (overlaps(rout, rv) && !exact(rout, rv)) return KDA_ERR_OVERLAP;
+  for (const Range& r : {rq, rk, rv, rg, rb, ridx})
+    if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
+  if (verify) {
+    // the trace is written: it overlaps nothing else
+    const Range rtr = range_of(trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * 4);
+    for (const Range& r : {rq, rk, rv, rg, rb, rpool, ridx, rout})
+      if (overlaps(rtr, r)) return KDA_ERR_OVERLAP;
+  }
+  return KDA_OK;
+}
+
+kda::DecodeArgs decode_args(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const float* g, const float* beta, float* state_pool,
+                            const int32_t* state_indices, uint16_t* out, float* trace) {
+  kda::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.pool = state_pool;
+  a.state_indices = state_indices;
+  a.out = out;
+  a.N = p->num_seqs;
+  a.T = p->tokens_per_seq;
+  a.H = p->num_heads;
+  a.pool_size = p->pool_size;
+  a.scale = p->scale;
+  a.prologue = p->prologue;
+  a.trace = trace;
+  return a;
+}
+}  // namespace
+
 extern "C" {
 
 const char* kda_status_string(int status) {
@@ -486,35 +553,10 @@ kda_status kda_decode_validate(const kda_decode_problem* p, const void* q, const
                                const void* v, const float* g, const float* beta,
                                const float* state_pool, const int32_t* state_indices,
                                const void* out) {
-  if (!p) return KDA_ERR_INVALID_ARG;
-  if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
-  if (p->num_seqs < 0 || p->tokens_per_seq < 1 || p->num_heads < 1 || p->pool_size < 1)
-    return KDA_ERR_INVALID_ARG;
-  if (!std::isfinite(p->scale)) return KDA_ERR_INVALID_ARG;
-  if (!std::isfinite(p->gate_lower_bound) || p->gate_lower_bound < -5.0f ||
-      p->gate_lower_bound > 0.0f)
-    return KDA_ERR_INVALID_ARG;
-  if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
-  const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
-  if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
-  if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out))
-    return KDA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, g, beta, state_pool, state_indices, out};
-  for (const void* ptr : ptrs)
-    if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
-  const uint64_t tok_bf16 = (uint64_t)N * T * H * kHeadDim * 2;
-  const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
-  const Range rg = range_of(g, tok_bf16 * 2), rb = range_of(beta, (uint64_t)N * T * H * 4);
-  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
-  const Range ridx = range_of(state_indices, (uint64_t)N * 4);
-  const Range rout = range_of(out, tok_bf16);
-  for (const Range& r : {rq, rk, rg, rb, rpool, ridx})
-    if (overlaps(rout, r)) return KDA_ERR_OVERLAP;
-  if (overlaps(rout, rv) && !exact(rout, rv)) return KDA_ERR_OVERLAP;
-  for (const Range& r : {rq, rk, rv, rg, rb, ridx})
-    if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
-  return KDA_OK;
+  return decode_check(p, q, k, v, g, beta, state_pool, state_indices, out, nullptr, false);
 }
+
+
 
 kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
                       const uint16_t* v, const float* g, const float* beta, float* state_pool,
@@ -522,22 +564,54 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
   const kda_status st = kda_decode_validate(p, q, k, v, g, beta, state_pool, state_indices, out);
   if (st != KDA_OK) return st;
   if (p->num_seqs == 0) return KDA_OK;
-  kda::DecodeArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = g;
-  a.beta = beta;
+  const kda::DecodeArgs a = decode_args(p, q, k, v, g, beta, state_pool, state_indices, out, nullptr);
+  return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_verify(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const float* g, const float* beta,
+                             const float* state_pool, const int32_t* state_indices, uint16_t* out,
+                             float* state_trace, void* stream) {
+  const kda_status st =
+      decode_check(p, q, k, v, g, beta, state_pool, state_indices, out, state_trace, true);
+  if (st != KDA_OK) return st;
+  if (p->num_seqs == 0) return KDA_OK;
+  // the pool is only read: the kernel stores no state to it when it has a trace
+  const kda::DecodeArgs a = decode_args(p, q, k, v, g, beta, const_cast<float*>(state_pool), state_indices,
+                                        out, state_trace);
+  return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_commit(const kda_decode_problem* p, float* state_pool,
+                             const int32_t* state_indices, const float* state_trace,
+                             const int32_t* accepted, void* stream) {
+  if (!p) return KDA_ERR_INVALID_ARG;
+  if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
+  if (p->num_seqs < 0 || p->tokens_per_seq < 1 || p->num_heads < 1 || p->pool_size < 1)
+    return KDA_ERR_INVALID_ARG;
+  const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
+  if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
+  if (N > 0 && (!state_pool || !state_indices || !state_trace || !accepted)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {state_pool, state_indices, state_trace, accepted};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
+  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
+  const Range ridx = range_of(state_indices, (uint64_t)N * 4);
+  const Range racc = range_of(accepted, (uint64_t)N * 4);
+  const Range rtr = range_of(state_trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * 4);
+  for (const Range& r : {ridx, racc, rtr})
+    if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
+  if (N == 0) return KDA_OK;
+  kda::DecodeCommitArgs a;
   a.pool = state_pool;
   a.state_indices = state_indices;
-  a.out = out;
+  a.trace = state_trace;
+  a.accepted = accepted;
   a.N = p->num_seqs;
   a.T = p->tokens_per_seq;
   a.H = p->num_heads;
   a.pool_size = p->pool_size;
-  a.scale = p->scale;
-  a.prologue = p->prologue;
-  return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return kda::launch_decode_commit(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

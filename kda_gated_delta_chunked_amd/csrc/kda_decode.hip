@@ -19,6 +19,10 @@
 // read once from the pool, kept across the call's tokens and written back in
 // place.  The path is bound by HBM: 64 KiB of state in and out per (sequence,
 // head).
+//
+// Verify (a state trace given): the same update, with the state after every
+// token stored to the trace and the pool left as it is; a commit launch then
+// copies each request's state at its accepted length into the pool.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -182,11 +186,37 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     }
     if (rr == 0)
       *reinterpret_cast<uint2*>(a.out + vbase + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    if (a.trace) {
+      float* tp = a.trace + (tok * H + h) * DK * DK + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(tp + (rr + 32 * i) * DK) = S[i];
+    }
     lds_barrier();  // the staged vectors and partial sums are rewritten next token
   }
 
+  if (!a.trace) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(sp + (rr + 32 * i) * DK) = S[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(sp + (rr + 32 * i) * DK) = S[i];
+  }
+}
+
+// One workgroup per (request, head, quarter of the columns), the decode
+// kernel's thread layout: each thread copies rows rr + 32 i of its 4 columns.
+__global__ __launch_bounds__(256) void kda_decode_commit_kernel(DecodeCommitArgs a) {
+  const int tid = threadIdx.x, cg = tid & 7, rr = tid >> 3;
+  const int64_t blk = blockIdx.x;
+  const int quarter = (int)(blk & 3);
+  const int64_t pair = blk >> 2;
+  const int H = a.H;
+  const int n = (int)(pair / H), h = (int)(pair - (int64_t)n * H);
+  const int idx = a.state_indices[n], acc = a.accepted[n];
+  if (idx < 0 || (int64_t)idx >= a.pool_size || acc < 1 || acc > a.T) return;
+  const int col = quarter * QCOLS + 4 * cg;
+  const float* src = a.trace + (((int64_t)n * a.T + acc - 1) * H + h) * DK * DK + col;
+  float* dst = a.pool + ((int64_t)idx * H + h) * DK * DK + col;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<float4*>(dst + (rr + 32 * i) * DK) = *reinterpret_cast<const float4*>(src + (rr + 32 * i) * DK);
 }
 
 }  // namespace
@@ -195,6 +225,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.N * a.H * 4;
   if (blocks == 0 || a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(kda_decode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_commit(const DecodeCommitArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.N * a.H * 4;
+  if (blocks == 0 || a.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_decode_commit_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -139,8 +139,25 @@ struct DecodeArgs {
   int64_t pool_size;
   float scale;
   int prologue;               // bit 0: L2-normalise q and k; bit 1: beta is a logit
+  float* trace;               // NULL, or [N, T, H, 128, 128]: the state after each token
+                              // (then the pool is left as it is)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Commit after a verify: pool[idx[n]] <- trace[n, accepted[n] - 1] for the
+// requests with a pool index and 1 <= accepted[n] <= T.
+struct DecodeCommitArgs {
+  float* pool;
+  const int32_t* state_indices;
+  const float* trace;         // [N, T, H, 128, 128]
+  const int32_t* accepted;    // [N]
+  int N;
+  int T;
+  int H;
+  int64_t pool_size;
+};
+
+hipError_t launch_decode_commit(const DecodeCommitArgs& a, hipStream_t stream);
 
 }  // namespace kda

@@ -143,6 +143,10 @@ def load_library(path: Optional[str] = None):
     lib.kda_decode_validate.restype = ctypes.c_int
     lib.kda_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P]
     lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode_verify.argtypes = [DP, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_decode_verify.restype = ctypes.c_int
+    lib.kda_decode_commit.argtypes = [DP, P, P, P, P, P]
+    lib.kda_decode_commit.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -353,6 +357,23 @@ def decode_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indic
                           stream or None)
 
 
+def decode_verify_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indices, out,
+                      state_trace, stream) -> int:
+    """Call ``kda_decode_verify`` with raw integer pointers (0 for NULL); returns the status."""
+    lib = load_library()
+    return lib.kda_decode_verify(ctypes.byref(problem), q or None, k or None, v or None, g or None,
+                                 beta or None, state_pool or None, state_indices or None, out or None,
+                                 state_trace or None, stream or None)
+
+
+def decode_commit_raw(problem: DecodeProblem, state_pool, state_indices, state_trace, accepted,
+                      stream) -> int:
+    """Call ``kda_decode_commit`` with raw integer pointers (0 for NULL); returns the status."""
+    lib = load_library()
+    return lib.kda_decode_commit(ctypes.byref(problem), state_pool or None, state_indices or None,
+                                 state_trace or None, accepted or None, stream or None)
+
+
 def decode_validate_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indices,
                         out) -> int:
     """Call ``kda_decode_validate`` with raw integer pointers; returns the status (host only)."""
@@ -362,16 +383,10 @@ def decode_validate_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, st
                                    state_indices or None, out or None)
 
 
-def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float] = None,
-           out=None, gate_lower_bound: float = -5.0, stream=None, qk_l2norm: bool = False,
-           beta_logit: bool = False):
-    """One state-pool decode step on the GPU.
-
-    q, k, v: bf16 [N, T, H, 128] (T tokens per request; T = 1 for decode).
-    g: fp32 like q; beta: fp32 [N, T, H].  state_pool: fp32 [P, H, 128, 128],
-    updated in place.  state_indices: int32 [N]; entries outside [0, P) mark
-    empty request slots (zero outputs, no state touched).  Returns out, with
-    q's shape (``out=v`` overwrites v)."""
+def _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower_bound, qk_l2norm,
+                  beta_logit):
+    """Shape, dtype and device checks shared by decode and decode_verify;
+    returns the problem struct."""
     import torch
 
     if q.dim() != 4:
@@ -398,13 +413,37 @@ def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float
         raise ValueError(f"state_indices must be [{N}]")
     if scale is None:
         scale = D ** -0.5
-    prob = make_decode_problem(N, T, H, state_pool.shape[0], scale=scale,
+    return make_decode_problem(N, T, H, state_pool.shape[0], scale=scale,
                                gate_lower_bound=gate_lower_bound, head_dim_k=D, head_dim_v=D,
                                qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+
+
+def _decode_out(q, v, out):
+    import torch
+
     if out is None:
-        out = torch.empty_like(v)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16:
+        return torch.empty_like(v)
+    if out.shape != q.shape or out.dtype != torch.bfloat16:
         raise ValueError("out must be bf16 with q's shape")
+    return out
+
+
+def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float] = None,
+           out=None, gate_lower_bound: float = -5.0, stream=None, qk_l2norm: bool = False,
+           beta_logit: bool = False):
+    """One state-pool decode step on the GPU.
+
+    q, k, v: bf16 [N, T, H, 128] (T tokens per request; T = 1 for decode).
+    g: fp32 like q; beta: fp32 [N, T, H].  state_pool: fp32 [P, H, 128, 128],
+    updated in place.  state_indices: int32 [N]; entries outside [0, P) mark
+    empty request slots (zero outputs, no state touched).  Returns out, with
+    q's shape (``out=v`` overwrites v)."""
+    import torch
+
+    prob = _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower_bound,
+                         qk_l2norm, beta_logit)
+    out = _decode_out(q, v, out)
+    dev = q.device
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
@@ -412,3 +451,65 @@ def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float
                         _ptr(state_indices), _ptr(out), int(stream.cuda_stream))
     _check(st, "kda_decode")
     return out
+
+
+def decode_verify(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float] = None,
+                  out=None, state_trace=None, gate_lower_bound: float = -5.0, stream=None,
+                  qk_l2norm: bool = False, beta_logit: bool = False):
+    """Speculative verify: decode's update over the T draft tokens of every
+    request, with state_pool only read and the state after each token stored
+    to state_trace (fp32 [N, T, H, 128, 128], allocated when None).  Returns
+    (out, state_trace); decode_commit then keeps the accepted prefix."""
+    import torch
+
+    prob = _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower_bound,
+                         qk_l2norm, beta_logit)
+    out = _decode_out(q, v, out)
+    N, T, H, D = q.shape
+    dev = q.device
+    if state_trace is None:
+        state_trace = torch.empty((N, T, H, D, D), dtype=torch.float32, device=dev)
+    elif (tuple(state_trace.shape) != (N, T, H, D, D) or state_trace.dtype != torch.float32
+          or state_trace.device != dev or not state_trace.is_contiguous()):
+        raise ValueError(f"state_trace must be contiguous fp32 [{N}, {T}, {H}, {D}, {D}] on {dev}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = decode_verify_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(state_pool), _ptr(state_indices), _ptr(out), _ptr(state_trace),
+                               int(stream.cuda_stream))
+    _check(st, "kda_decode_verify")
+    return out, state_trace
+
+
+def decode_commit(state_pool, state_indices, state_trace, accepted, *, stream=None):
+    """After decode_verify: pool[state_indices[n]] <- state_trace[n, accepted[n] - 1]
+    for the requests with a pool index and 1 <= accepted[n] <= T (int32 [N] on
+    the device); the others keep their pool state."""
+    import torch
+
+    if state_trace.dim() != 5:
+        raise ValueError("state_trace must be [N, T, H, 128, 128]")
+    N, T, H, D, _ = state_trace.shape
+    dev = state_trace.device
+    for name, t, dt in (("state_pool", state_pool, torch.float32),
+                        ("state_indices", state_indices, torch.int32),
+                        ("state_trace", state_trace, torch.float32),
+                        ("accepted", accepted, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if dev.type != "cuda":
+        raise ValueError("libkda runs on the GPU: tensors must be on a cuda (HIP) device")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError(f"state_pool must be [P, {H}, {D}, {D}]")
+    if tuple(state_indices.shape) != (N,) or tuple(accepted.shape) != (N,):
+        raise ValueError(f"state_indices and accepted must be [{N}]")
+    prob = make_decode_problem(N, T, H, state_pool.shape[0], scale=1.0, head_dim_k=D, head_dim_v=D)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = decode_commit_raw(prob, _ptr(state_pool), _ptr(state_indices), _ptr(state_trace),
+                               _ptr(accepted), int(stream.cuda_stream))
+    _check(st, "kda_decode_commit")

@@ -315,7 +315,8 @@ class DecodeBufs:
         rows = N * T * H
         base = 1 << 41
         sizes = {"q": rows * 256, "k": rows * 256, "v": rows * 256, "g": rows * 512,
-                 "beta": rows * 4, "pool": P * H * 65536, "idx": N * 4, "out": rows * 256}
+                 "beta": rows * 4, "pool": P * H * 65536, "idx": N * 4, "out": rows * 256,
+                 "trace": rows * 65536, "acc": N * 4}
         self.addr = {}
         for k_, sz in sizes.items():
             self.addr[k_] = base
@@ -369,6 +370,51 @@ def test_decode_rejects_on_the_host():
     assert lib.kda_decode(ctypes.byref(prob), *P, None) == INVALID
     prob = _dprob(b)
     assert lib.kda_decode(ctypes.byref(prob), *b.args(out=b.addr["pool"]), None) == OVERLAP
+
+
+def test_decode_verify_and_commit_rules():
+    # argument errors of the speculative pair come back on the host, before
+    # anything is enqueued (the fake addresses are never dereferenced)
+    b = DecodeBufs()
+    a = b.addr
+
+    def verify(prob=None, trace=a["trace"], **over):
+        return ops.decode_verify_raw(prob or _dprob(b), *b.args(**over), trace, 0)
+
+    def commit(prob=None, **over):
+        d = dict(pool=a["pool"], idx=a["idx"], trace=a["trace"], acc=a["acc"])
+        d.update(over)
+        return ops.decode_commit_raw(prob or _dprob(b), d["pool"], d["idx"], d["trace"], d["acc"], 0)
+
+    # the decode rules hold for a verify as well
+    assert verify(_dprob(b, T=0)) == INVALID
+    assert verify(_dprob(b, head_dim_k=64)) == UNSUPPORTED
+    assert verify(out=a["pool"]) == OVERLAP
+    assert verify(pool=a["pool"] + 4) == ALIGN
+    # and the trace: required, aligned, overlapping nothing (not even out = v)
+    assert verify(trace=0) == INVALID
+    assert verify(trace=a["trace"] + 8) == ALIGN
+    for name in ("q", "k", "v", "g", "beta", "pool", "idx", "out"):
+        assert verify(trace=a[name]) == OVERLAP, name
+    # the trace's extent is N T H 128 128 fp32: one that ends 16 bytes into
+    # the pool overlaps it (a call that passes every check would launch, so no
+    # accepted case is made here with these fake addresses)
+    extent = b.N * b.T * b.H * 65536
+    far = 1 << 48
+    assert verify(trace=far + 16, pool=far + extent) == OVERLAP
+    # an empty batch needs no buffers at all
+    assert ops.decode_verify_raw(_dprob(b, N=0), *[0] * 9, 0) == OK
+
+    assert commit(_dprob(b, T=0)) == INVALID
+    assert commit(_dprob(b, P=0)) == INVALID
+    assert commit(_dprob(b, head_dim_v=64)) == UNSUPPORTED
+    for name in ("pool", "idx", "trace", "acc"):
+        assert commit(**{name: 0}) == INVALID, name
+        assert commit(**{name: a[name] + 4}) == ALIGN, name
+    for name in ("idx", "trace", "acc"):
+        assert commit(pool=a[name]) == OVERLAP, name
+    assert ops.decode_commit_raw(_dprob(b, N=0), 0, 0, 0, 0, 0) == OK
+    assert commit(_dprob(b, N=1 << 20, T=16, H=2)) == TOO_LARGE
 
 
 def test_state_dtype_rules():

@@ -130,3 +130,80 @@ def test_decode_input_prologue():
     p.beta = rng.normal(0, 1.5, p.beta.shape).astype(np.float32)
     gout, gpool = _run(p, pool, idx, 3, qk_l2norm=True, beta_logit=True)
     _check(p, pool, idx, 3, gout, gpool, "decode prologue", qk_l2norm=True, beta_logit=True)
+
+
+def _prefix(bits, N, T, t):
+    """The first t tokens of each of N requests of T tokens (token-major rows)."""
+    return np.ascontiguousarray(bits.reshape(N, T, *bits.shape[1:])[:, :t]).reshape(N * t, *bits.shape[1:])
+
+
+# speculative verify: T draft tokens per request, pool only read, the state
+# after every token in the trace; then a commit of each request's accepted
+# prefix.  The last shape is the decode bench size with 4 drafts per request.
+@pytest.mark.parametrize("N,T,H,P,empty", [(1, 1, 1, 1, 0), (6, 4, 3, 9, 1), (37, 3, 2, 40, 4),
+                                           (256, 4, 12, 300, 8)])
+def test_decode_verify_trace_and_commit(N, T, H, P, empty):
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    dev = torch.device("cuda", 0)
+    p, pool, idx = _case(N, T, H, P, seed=170 + N + T, empty=empty)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    shp = (N, T, H, 128)
+    q, k, v = bf16(p.q).view(shp), bf16(p.k).view(shp), bf16(p.v).view(shp)
+    g = torch.from_numpy(p.g).to(dev).view(shp)
+    beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
+    didx = torch.from_numpy(idx).to(dev)
+    vpool = torch.from_numpy(pool).to(dev)
+    trace = torch.full((N, T, H, 128, 128), 7.0, dtype=torch.float32, device=dev)
+    vout, _ = K.decode_verify(q, k, v, g, beta, vpool, didx, scale=p.scale, state_trace=trace)
+    # the same tokens through kda_decode on a copy of the pool
+    dpool = torch.from_numpy(pool).to(dev)
+    dout = K.decode(q, k, v, g, beta, dpool, didx, scale=p.scale)
+    torch.cuda.synchronize()
+    what = f"N{N} T{T} H{H} P{P}"
+    gtrace = trace.cpu().numpy()
+    # the pool is only read; outputs and the last traced state are kda_decode's, bit for bit
+    assert np.array_equal(vpool.cpu().numpy(), pool), what
+    assert torch.equal(vout.view(torch.int16), dout.view(torch.int16)), what
+    gdpool = dpool.cpu().numpy()
+    named = [n for n in range(N) if 0 <= idx[n] < P]
+    for n in range(N):
+        if n in named:
+            assert np.array_equal(gtrace[n, T - 1], gdpool[idx[n]]), (what, n)
+        else:
+            assert np.all(gtrace[n] == 7.0), (what, n)   # no state: trace rows untouched
+    # outputs against the oracle (as kda_decode's), each traced state against
+    # the oracle's decode of the first t + 1 tokens
+    gout = vout.float().cpu().numpy().reshape(N * T, H, 128)
+    _check(p, pool, idx, T, gout, gdpool, what)
+    for t in range(T):
+        ref = oracle.decode(_prefix(p.q, N, T, t + 1), _prefix(p.k, N, T, t + 1),
+                            _prefix(p.v, N, T, t + 1), _prefix(p.g, N, T, t + 1),
+                            _prefix(p.beta, N, T, t + 1), scale=p.scale, num_seqs=N,
+                            tokens_per_seq=t + 1, state_pool=pool, state_indices=idx)
+        if named:
+            assert rel_l2(gtrace[named, t], ref["pool"][idx[named]]) <= POOL_REL_L2, (what, t)
+
+    # commit: every accepted length from 0 (all drafts rejected) to T, and
+    # values outside [0, T] that change nothing
+    rng = np.random.default_rng(180 + N)
+    acc = rng.integers(0, T + 1, N).astype(np.int32)
+    acc[: min(N, 2)] = T
+    if N > 3:
+        acc[2], acc[3] = -1, T + 1
+    vpool.copy_(torch.from_numpy(pool))
+    K.decode_commit(vpool, didx, trace, torch.from_numpy(acc).to(dev))
+    torch.cuda.synchronize()
+    want = pool.copy()
+    for n in named:
+        if 1 <= acc[n] <= T:
+            want[idx[n]] = gtrace[n, acc[n] - 1]
+    assert np.array_equal(vpool.cpu().numpy(), want), what
+    # accepting every draft leaves the pool as kda_decode does
+    vpool.copy_(torch.from_numpy(pool))
+    K.decode_commit(vpool, didx, trace, torch.full((N,), T, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(vpool.cpu().numpy(), gdpool), what
