@@ -1160,10 +1160,18 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     // lane offset formed here (opaque), not kept live across the segment loop
     int ro = q * H * DK + 4 * g4;
     asm volatile("" : "+v"(ro));
+    if (poff == 0) {
+      // a whole segment (all but a sequence's last and those cut at a
+      // checkpoint): no per-lane condition, so no branches around the stores
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (16 * t + q >= poff)
+      for (int t = 0; t < 4; ++t)
         *reinterpret_cast<uint2*>(ob + ro + t * 16 * H * DK) = make_uint2(opk[2 * t], opk[2 * t + 1]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (16 * t + q >= poff)
+          *reinterpret_cast<uint2*>(ob + ro + t * 16 * H * DK) = make_uint2(opk[2 * t], opk[2 * t + 1]);
+    }
   };
 
   auto step = [&](int jseg, const uint4* cur) {
@@ -1217,6 +1225,13 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     f16x8 Sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) Sb[b] = acc_pair_h(S[2 * b], S[2 * b + 1]);
+    // max |2^s S| for the operand scale check below, formed beside the first
+    // products (it needs only the state)
+    float smx = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) smx = fmaxf(smx, fabsf(S[m][e]));
     float4 gm[8];
     if constexpr (BATCHED) {
 #pragma unroll
@@ -1283,17 +1298,13 @@ __global__ __launch_bounds__(64 * (CW + KW), 1) void kda_recurrence_kernel(Decom
     for (int b = 1; b < 4; ++b)
 #pragma unroll
       for (int t = 0; t < 4; ++t) O[t] = mfma(Sb[b], fq[t * 4 + b], O[t]);
-    KDA_FENCE();
-    // Operand scale check, while the products above run: the largest of
+    // Operand scale check, while the products above run (no fence: its VALU
+    // work fills the issue slots between them): the largest of
     // |2^s S| and |2^s V| over the wave must lie in [4, 64] (or be 0).  When
     // it does not, s is reset so that it lands in [16, 32) -- the state is
     // multiplied by the change of 2^s (exact) and X, O are formed again.
     {
-      float mx = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(S[m][e]));
+      const float mx = smx;
       // |V| as bf16 bits: for non-negative values their order is the values' order
       uint32_t vmax = 0u;
 #pragma unroll
