@@ -291,7 +291,8 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
 /* Speculative verify, then commit.  FlashInfer PR #4262 (upstream recurrent-
  * KDA comparison) says speculative decode has different checkpoint / state
  * semantics from decode, and its dispatch contract names accepted-token
- * features, without defining either.  Reading taken: verifying T draft tokens
+ * features; lmdeploy PR #5050 (Modification) keeps a ring of states for its
+ * MTP decode kernels; none of them defines the semantics.  Reading taken: verifying T draft tokens
  * per request runs the decode recurrence over all T (outputs for every
  * position, as kda_decode) but leaves the pool as it is and stores the state
  * after every token, so that the caller can keep the state of the accepted
