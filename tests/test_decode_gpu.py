@@ -207,3 +207,122 @@ def test_decode_verify_trace_and_commit(N, T, H, P, empty):
     K.decode_commit(vpool, didx, trace, torch.full((N,), T, dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     assert np.array_equal(vpool.cpu().numpy(), gdpool), what
+
+
+def test_decode_verify_input_prologue():
+    # raw q / k and beta logits through the verify: outputs and the last traced
+    # state are kda_decode's with the same flags, bit for bit, and every traced
+    # state meets the oracle's decode of that prefix with the prologue
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32
+    dev = torch.device("cuda", 0)
+    N, T, H, P = 9, 3, 4, 12
+    p, pool, idx = _case(N, T, H, P, seed=190, empty=2)
+    rng = np.random.default_rng(191)
+    p.q = bf16_bits_from_f32(rng.normal(0, 2.0, p.q.shape).astype(np.float32))
+    p.k = bf16_bits_from_f32(rng.normal(0, 2.0, p.k.shape).astype(np.float32))
+    p.beta = rng.normal(0, 1.5, p.beta.shape).astype(np.float32)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    shp = (N, T, H, 128)
+    q, k, v = bf16(p.q).view(shp), bf16(p.k).view(shp), bf16(p.v).view(shp)
+    g = torch.from_numpy(p.g).to(dev).view(shp)
+    beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
+    didx = torch.from_numpy(idx).to(dev)
+    flags = dict(qk_l2norm=True, beta_logit=True)
+    vpool = torch.from_numpy(pool).to(dev)
+    vout, trace = K.decode_verify(q, k, v, g, beta, vpool, didx, scale=p.scale, **flags)
+    dpool = torch.from_numpy(pool).to(dev)
+    dout = K.decode(q, k, v, g, beta, dpool, didx, scale=p.scale, **flags)
+    torch.cuda.synchronize()
+    assert torch.equal(vout.view(torch.int16), dout.view(torch.int16))
+    gtrace, gdpool = trace.cpu().numpy(), dpool.cpu().numpy()
+    named = [n for n in range(N) if 0 <= idx[n] < P]
+    for n in named:
+        assert np.array_equal(gtrace[n, T - 1], gdpool[idx[n]]), n
+    for t in range(T):
+        ref = oracle.decode(_prefix(p.q, N, T, t + 1), _prefix(p.k, N, T, t + 1), _prefix(p.v, N, T, t + 1),
+                            _prefix(p.g, N, T, t + 1), _prefix(p.beta, N, T, t + 1), scale=p.scale,
+                            num_seqs=N, tokens_per_seq=t + 1, state_pool=pool, state_indices=idx, **flags)
+        assert rel_l2(gtrace[named, t], ref["pool"][idx[named]]) <= POOL_REL_L2, t
+
+
+def test_decode_verify_commit_graph_steps():
+    # one speculative step (verify, then commit of the accepted prefixes)
+    # captured in a HIP graph and replayed for three steps in a row on one pool,
+    # with new drafts and new accepted lengths written into the captured
+    # buffers each time and eager work between replays: every replay equals the
+    # same two calls made eagerly, bit for bit, and the pool follows the oracle
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    dev = torch.device("cuda", 0)
+    N, T, H, P = 16, 4, 3, 20
+    rng = np.random.default_rng(200)
+    pool0 = rng.normal(0, 0.05, (P, H, 128, 128)).astype(np.float32)
+    idx = rng.permutation(P)[:N].astype(np.int32)
+    idx[[3, 11]] = -1
+    shp = (N, T, H, 128)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    steps = []
+    for s in range(3):
+        p = synth.make_problem([T] * N, H, seed=210 + s, fixed=True)
+        acc = rng.integers(0, T + 1, N).astype(np.int32)
+        acc[s] = T
+        steps.append((p, acc))
+    p0 = steps[0][0]
+    q, k, v = bf16(p0.q).view(shp), bf16(p0.k).view(shp), bf16(p0.v).view(shp)
+    g = torch.from_numpy(p0.g).to(dev).view(shp)
+    beta = torch.from_numpy(p0.beta).to(dev).view(N, T, H)
+    pool = torch.from_numpy(pool0).to(dev)
+    didx = torch.from_numpy(idx).to(dev)
+    acc_d = torch.from_numpy(steps[0][1]).to(dev)
+    out = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    trace = torch.empty((N, T, H, 128, 128), device=dev)
+
+    def spec_step(stream):
+        K.decode_verify(q, k, v, g, beta, pool, didx, scale=p0.scale, out=out, state_trace=trace, stream=stream)
+        K.decode_commit(pool, didx, trace, acc_d, stream=stream)
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            spec_step(side)
+    torch.cuda.synchronize()
+
+    # the eager twin on its own buffers
+    epool = torch.from_numpy(pool0).to(dev)
+    cpu_pool = pool0.copy()
+    for s, (p, acc) in enumerate(steps):
+        q.copy_(bf16(p.q).view(shp)); k.copy_(bf16(p.k).view(shp)); v.copy_(bf16(p.v).view(shp))
+        g.copy_(torch.from_numpy(p.g).view(shp)); beta.copy_(torch.from_numpy(p.beta).view(N, T, H))
+        acc_d.copy_(torch.from_numpy(acc))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eout, etrace = K.decode_verify(q, k, v, g, beta, epool, didx, scale=p.scale)
+        K.decode_commit(epool, didx, etrace, acc_d)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eout.view(torch.int16)), s
+        gpool = pool.cpu().numpy()
+        assert np.array_equal(gpool, epool.cpu().numpy()), s
+        # the oracle: each accepted prefix from the previous pool
+        for n in range(N):
+            if not (0 <= idx[n] < P) or acc[n] == 0:
+                continue
+            a = int(acc[n])
+            sl = slice(n * T, n * T + a)
+            ref = oracle.decode(p.q[sl], p.k[sl], p.v[sl], p.g[sl], p.beta[sl], scale=p.scale, num_seqs=1,
+                                tokens_per_seq=a, state_pool=cpu_pool, state_indices=idx[n:n + 1])
+            cpu_pool_n = ref["pool"][idx[n]]
+            assert rel_l2(gpool[idx[n]], cpu_pool_n) <= POOL_REL_L2, (s, n)
+        untouched = [i for i in range(P) if i not in {int(idx[n]) for n in range(N) if 0 <= idx[n] < P and acc[n] > 0}]
+        assert np.array_equal(gpool[untouched], cpu_pool[untouched]), s
+        cpu_pool = gpool.copy()
+        _ = (q.float() * 2).sum().item()   # eager work between replays
