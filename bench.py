@@ -242,6 +242,79 @@ def bench_decode(args, torch, K, synth) -> int:
     return 0
 
 
+def bench_verify(args, torch, K, synth) -> int:
+    """One speculative step for N requests x T draft tokens, H = 12: the verify
+    (outputs for every draft, the pool only read), then the pool keeps each
+    request's accepted prefix (seeded accepted counts in [0, T]), two ways:
+    the verify stores every intermediate state and a commit copies the
+    accepted one (trace), or the verify stores none and an advance recomputes
+    the accepted prefix (recompute).  Inputs resident; `value` is the
+    recompute path's draft tokens per second."""
+    N, T = (int(x) for x in args.verify.split(","))
+    H = 12
+    dev = torch.device("cuda", 0)
+    p = synth.make_problem([T] * N, H, seed=3000 + N + T, fixed=True)
+    shp = (N, T, H, 128)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16).view(shp)
+
+    q, k, v = bf16(p.q), bf16(p.k), bf16(p.v)
+    g = torch.from_numpy(p.g).to(dev).view(shp)
+    beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
+    rng = np.random.default_rng(3001)
+    pool = torch.from_numpy(rng.normal(0, 0.02, (N, H, 128, 128)).astype(np.float32)).to(dev)
+    idx = torch.from_numpy(rng.permutation(N).astype(np.int32)).to(dev)
+    acc_h = rng.integers(0, T + 1, N).astype(np.int32)
+    acc = torch.from_numpy(acc_h).to(dev)
+    out = torch.empty_like(v)
+    trace = torch.empty((N, T, H, 128, 128), device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step_trace():
+        K.decode_verify(q, k, v, g, beta, pool, idx, scale=p.scale, out=out, state_trace=trace, stream=stream)
+        K.decode_commit(pool, idx, trace, acc, stream=stream)
+
+    def step_recompute():
+        K.decode_verify(q, k, v, g, beta, pool, idx, scale=p.scale, out=out, state_trace=False, stream=stream)
+        K.decode_advance(q, k, v, g, beta, pool, idx, acc, scale=p.scale, stream=stream)
+
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_trace = timed(step_trace)
+    ms_re = timed(step_recompute)
+    state = 128 * 128 * 4
+    taken = int(acc_h.sum())
+    tok_in = 128 * 2 * 3 + 128 * 4 + 4          # q, k, v, g, beta per token-head
+    # recompute: the verify reads every state, the inputs and writes the
+    # outputs; the advance reads and writes the states of requests that took a
+    # draft, with the inputs of the drafts taken
+    alg = N * H * state + N * T * H * (tok_in + 256) + int((acc_h > 0).sum()) * H * 2 * state + taken * H * tok_in
+    res = {"metric": "speculative verify step draft tokens/s (H=12, K=V=128, fp32 state)",
+           "value": round(N * T / (ms_re * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_re, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+           "data": "synthetic",
+           "config": {"workload": f"verify_n{N}_t{T}", "requests": N, "drafts_per_request": T, "H": H,
+                      "pool_size": N, "accepted_mean": round(float(acc_h.mean()), 3)},
+           "paths": {"recompute_ms_per_step": round(ms_re, 4), "trace_ms_per_step": round(ms_trace, 4),
+                     "trace_bytes": N * T * H * state},
+           "roofline": {"bound": "hbm", "achieved": round(alg / (ms_re * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(alg / (ms_re * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "kda_decode_kernel (verify + advance)", "algorithmic_bytes": alg}}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +332,10 @@ def main() -> int:
     ap.add_argument("--decode", default="", metavar="N,T",
                     help="instead of the prefill, time the state-pool decode of N requests "
                          "advancing T tokens each (H = 12, pool of N states)")
+    ap.add_argument("--verify", default="", metavar="N,T",
+                    help="instead of the prefill, time a speculative step of N requests with T draft "
+                         "tokens each (verify, then commit of the traced states or advance by "
+                         "recompute; H = 12, pool of N states)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, --steps times "
                          "(reference for the HBM byte counters)")
@@ -284,6 +361,8 @@ def main() -> int:
 
     if args.decode:
         return bench_decode(args, torch, K, synth)
+    if args.verify:
+        return bench_verify(args, torch, K, synth)
 
     p = synth.workload(args.workload)
     dev = torch.device("cuda", 0)

@@ -288,29 +288,41 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
                       const uint16_t* v, const float* g, const float* beta, float* state_pool,
                       const int32_t* state_indices, uint16_t* out, void* stream);
 
-/* Speculative verify, then commit.  FlashInfer PR #4262 (upstream recurrent-
- * KDA comparison) says speculative decode has different checkpoint / state
- * semantics from decode, and its dispatch contract names accepted-token
+/* Speculative verify, then commit or advance.  FlashInfer PR #4262 (upstream
+ * recurrent-KDA comparison) says speculative decode has different checkpoint /
+ * state semantics from decode, and its dispatch contract names accepted-token
  * features; lmdeploy PR #5050 (Modification) keeps a ring of states for its
- * MTP decode kernels; none of them defines the semantics.  Reading taken: verifying T draft tokens
- * per request runs the decode recurrence over all T (outputs for every
- * position, as kda_decode) but leaves the pool as it is and stores the state
- * after every token, so that the caller can keep the state of the accepted
- * prefix once it knows its length.
- *   kda_decode_verify: as kda_decode, plus state_trace fp32
- *     [N, T, H, 128, 128] (device, caller-owned): state_trace[n, t] = the
- *     state of request n after its first t + 1 tokens.  The pool is only read.
- *     A request with no pool index gives zero outputs and leaves its trace rows
- *     untouched.  state_trace must not overlap any other buffer.
+ * MTP decode kernels; none of them defines the semantics.  Reading taken:
+ * verifying T draft tokens per request runs the decode recurrence over all T
+ * (outputs for every position, as kda_decode) but leaves the pool as it is;
+ * once the caller knows how many drafts each request accepted, the pool takes
+ * the state after that accepted prefix.  Two ways to get there:
+ *   - a trace: the verify stores the state after every token and a commit
+ *     copies the accepted one (N T H x 64 KiB of trace; the intermediate
+ *     states stay available to the caller);
+ *   - a recompute: the verify stores no state and an advance runs the accepted
+ *     prefix again from the pool, with no outputs (no trace; the pool's state
+ *     is read twice and written once).
+ *   kda_decode_verify: as kda_decode with the pool only read, plus
+ *     state_trace fp32 [N, T, H, 128, 128] (device, caller-owned) or NULL (no
+ *     trace): state_trace[n, t] = the state of request n after its first t + 1
+ *     tokens.  A request with no pool index gives zero outputs and leaves its
+ *     trace rows untouched.  state_trace must not overlap any other buffer.
  *   kda_decode_commit: for every request n with a pool index and
  *     1 <= accepted[n] <= T (accepted: device int32 [N], e.g. written by the
  *     sampler, so nothing synchronises), copies state_trace[n, accepted[n] - 1]
  *     into pool[state_indices[n]]; other requests (accepted[n] = 0: every draft
  *     rejected) keep their pool state.  Values in accepted are the caller's
  *     contract, as offsets are; out-of-range ones change nothing.
- * After a verify, commit with accepted[n] = T leaves the pool bit for bit as
- * kda_decode would have.  Both check their arguments on the host first, as
- * kda_decode. */
+ *   kda_decode_advance: the same inputs as the verify (all T tokens' q, k, v,
+ *     g, beta), no outputs: request n's pool state advances by its first
+ *     accepted[n] tokens (accepted as for the commit; 0 or out of range leaves
+ *     it as it is).  The pool is written in place and must not overlap the
+ *     inputs, the indices or accepted.
+ * After a verify, commit or advance with accepted[n] = T leaves the pool bit
+ * for bit as kda_decode would have, and advance with any accepted[n] leaves it
+ * bit for bit as the commit of the traced state does.  All three check their
+ * arguments on the host first, as kda_decode. */
 kda_status kda_decode_verify(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const float* g, const float* beta,
                              const float* state_pool, const int32_t* state_indices, uint16_t* out,
@@ -318,6 +330,9 @@ kda_status kda_decode_verify(const kda_decode_problem* p, const uint16_t* q, con
 kda_status kda_decode_commit(const kda_decode_problem* p, float* state_pool,
                              const int32_t* state_indices, const float* state_trace,
                              const int32_t* accepted, void* stream);
+kda_status kda_decode_advance(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const float* g, const float* beta, float* state_pool,
+                              const int32_t* state_indices, const int32_t* accepted, void* stream);
 
 /* Static string for a status code (a kda_status value; any other int gives
  * "unknown status").  Errors are reported, never retried or rerouted through

@@ -281,11 +281,16 @@ kda_status scratch_address(void** addr) {
 
 namespace {
 
-// kda_decode_validate's checks, and for a verify the state trace as well
+// What a decode-family call passes besides the inputs: kda_decode and the
+// verify write `out`; the verify may also write a state trace; the advance
+// writes no output and reads the accepted counts.
+enum DecodeMode { DECODE, VERIFY, ADVANCE };
+
+// kda_decode_validate's checks, and those of the verify and the advance
 kda_status decode_check(const kda_decode_problem* p, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const float* state_pool,
                         const int32_t* state_indices, const void* out, const float* trace,
-                        bool verify) {
+                        const int32_t* accepted, DecodeMode mode) {
   if (!p) return KDA_ERR_INVALID_ARG;
   if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
   if (p->num_seqs < 0 || p->tokens_per_seq < 1 || p->num_heads < 1 || p->pool_size < 1)
@@ -297,10 +302,14 @@ kda_status decode_check(const kda_decode_problem* p, const void* q, const void* 
   if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
   const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
   if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
-  if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out))
+  if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices))
     return KDA_ERR_INVALID_ARG;
-  if (verify && N > 0 && !trace) return KDA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, g, beta, state_pool, state_indices, out, trace};
+  if (N > 0 && mode != ADVANCE && !out) return KDA_ERR_INVALID_ARG;
+  if (N > 0 && mode == ADVANCE && !accepted) return KDA_ERR_INVALID_ARG;
+  if (mode == ADVANCE) out = nullptr;
+  if (mode != VERIFY) trace = nullptr;
+  if (mode != ADVANCE) accepted = nullptr;
+  const void* ptrs[] = {q, k, v, g, beta, state_pool, state_indices, out, trace, accepted};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
   const uint64_t tok_bf16 = (uint64_t)N * T * H * kHeadDim * 2;
@@ -308,13 +317,15 @@ kda_status decode_check(const kda_decode_problem* p, const void* q, const void* 
   const Range rg = range_of(g, tok_bf16 * 2), rb = range_of(beta, (uint64_t)N * T * H * 4);
   const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
   const Range ridx = range_of(state_indices, (uint64_t)N * 4);
+  const Range racc = range_of(accepted, (uint64_t)N * 4);
   const Range rout = range_of(out, tok_bf16);
   for (const Range& r : {rq, rk, rg, rb, rpool, ridx})
     if (overlaps(rout, r)) return KDA_ERR_OVERLAP;
   if (overlaps(rout, rv) && !exact(rout, rv)) return KDA_ERR_OVERLAP;
-  for (const Range& r : {rq, rk, rv, rg, rb, ridx})
+  // the pool is written (read only by a verify, checked the same way)
+  for (const Range& r : {rq, rk, rv, rg, rb, ridx, racc})
     if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
-  if (verify) {
+  if (trace) {
     // the trace is written: it overlaps nothing else
     const Range rtr = range_of(trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * 4);
     for (const Range& r : {rq, rk, rv, rg, rb, rpool, ridx, rout})
@@ -325,7 +336,8 @@ kda_status decode_check(const kda_decode_problem* p, const void* q, const void* 
 
 kda::DecodeArgs decode_args(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const float* g, const float* beta, float* state_pool,
-                            const int32_t* state_indices, uint16_t* out, float* trace) {
+                            const int32_t* state_indices, uint16_t* out, float* trace,
+                            const int32_t* accepted, bool writeback) {
   kda::DecodeArgs a;
   a.q = q;
   a.k = k;
@@ -342,6 +354,8 @@ kda::DecodeArgs decode_args(const kda_decode_problem* p, const uint16_t* q, cons
   a.scale = p->scale;
   a.prologue = p->prologue;
   a.trace = trace;
+  a.accepted = accepted;
+  a.writeback = writeback ? 1 : 0;
   return a;
 }
 }  // namespace
@@ -553,7 +567,7 @@ kda_status kda_decode_validate(const kda_decode_problem* p, const void* q, const
                                const void* v, const float* g, const float* beta,
                                const float* state_pool, const int32_t* state_indices,
                                const void* out) {
-  return decode_check(p, q, k, v, g, beta, state_pool, state_indices, out, nullptr, false);
+  return decode_check(p, q, k, v, g, beta, state_pool, state_indices, out, nullptr, nullptr, DECODE);
 }
 
 
@@ -564,7 +578,8 @@ kda_status kda_decode(const kda_decode_problem* p, const uint16_t* q, const uint
   const kda_status st = kda_decode_validate(p, q, k, v, g, beta, state_pool, state_indices, out);
   if (st != KDA_OK) return st;
   if (p->num_seqs == 0) return KDA_OK;
-  const kda::DecodeArgs a = decode_args(p, q, k, v, g, beta, state_pool, state_indices, out, nullptr);
+  const kda::DecodeArgs a =
+      decode_args(p, q, k, v, g, beta, state_pool, state_indices, out, nullptr, nullptr, true);
   return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -573,12 +588,24 @@ kda_status kda_decode_verify(const kda_decode_problem* p, const uint16_t* q, con
                              const float* state_pool, const int32_t* state_indices, uint16_t* out,
                              float* state_trace, void* stream) {
   const kda_status st =
-      decode_check(p, q, k, v, g, beta, state_pool, state_indices, out, state_trace, true);
+      decode_check(p, q, k, v, g, beta, state_pool, state_indices, out, state_trace, nullptr, VERIFY);
   if (st != KDA_OK) return st;
   if (p->num_seqs == 0) return KDA_OK;
-  // the pool is only read: the kernel stores no state to it when it has a trace
+  // the pool is only read: the kernel runs with its write-back off
   const kda::DecodeArgs a = decode_args(p, q, k, v, g, beta, const_cast<float*>(state_pool), state_indices,
-                                        out, state_trace);
+                                        out, state_trace, nullptr, false);
+  return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_advance(const kda_decode_problem* p, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const float* g, const float* beta, float* state_pool,
+                              const int32_t* state_indices, const int32_t* accepted, void* stream) {
+  const kda_status st =
+      decode_check(p, q, k, v, g, beta, state_pool, state_indices, nullptr, nullptr, accepted, ADVANCE);
+  if (st != KDA_OK) return st;
+  if (p->num_seqs == 0) return KDA_OK;
+  const kda::DecodeArgs a =
+      decode_args(p, q, k, v, g, beta, state_pool, state_indices, nullptr, nullptr, accepted, true);
   return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

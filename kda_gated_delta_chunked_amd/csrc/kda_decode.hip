@@ -20,9 +20,12 @@
 // place.  The path is bound by HBM: 64 KiB of state in and out per (sequence,
 // head).
 //
-// Verify (a state trace given): the same update, with the state after every
-// token stored to the trace and the pool left as it is; a commit launch then
-// copies each request's state at its accepted length into the pool.
+// Speculative steps use the same kernel: a verify runs the T draft tokens
+// with the pool only read (write-back off), optionally storing the state after
+// every token to a trace; a commit launch then copies each request's traced
+// state at its accepted length into the pool, or, with no trace, an advance
+// runs the kernel again over each request's first accepted[n] tokens only,
+// with no outputs, and writes that state back.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -61,14 +64,22 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
   const int col = quarter * QCOLS + 4 * cg;
   const int T = a.T;
   const int idx = a.state_indices[n];
+  // tokens this request takes: all T, or its accepted prefix (none when the
+  // count is out of range)
+  int Tn = T;
+  if (a.accepted) {
+    const int acc = a.accepted[n];
+    Tn = acc >= 0 && acc <= T ? acc : 0;
+  }
 
   if (idx < 0 || (int64_t)idx >= a.pool_size) {
     // a request slot with no state: its outputs are zero, no state is touched
-    if (rr == 0)
+    if (rr == 0 && a.out)
       for (int t = 0; t < T; ++t)
         *reinterpret_cast<uint2*>(a.out + (((int64_t)n * T + t) * H + h) * DK + col) = make_uint2(0u, 0u);
     return;
   }
+  if (Tn == 0) return;  // nothing accepted: the pool keeps its state
 
   float* sp = a.pool + ((int64_t)idx * H + h) * DK * DK + col;
   float4 S[4];
@@ -95,7 +106,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
   };
   fetch(0);
 
-  for (int t = 0; t < T; ++t) {
+  for (int t = 0; t < Tn; ++t) {
     const int64_t tok = (int64_t)n * T + t;
     const int64_t vbase = (tok * H + h) * DK;
     if (tid < DK) {
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       sbeta = (a.prologue & 2) ? 1.f / (1.f + __expf(-nx)) : nx;  // beta given as a logit
     }
     lds_barrier();
-    if (t + 1 < T) fetch(t + 1);
+    if (t + 1 < Tn) fetch(t + 1);
     // k . q, and with the prologue the norms of k and q: every wave sums the
     // 128 staged values itself (no further barrier)
     float kq = sk[lane] * sq[lane] + sk[lane + 64] * sq[lane + 64];
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       S[i].z += kr * u[2];
       S[i].w += kr * u[3];
     }
-    if (rr == 0)
+    if (rr == 0 && a.out)
       *reinterpret_cast<uint2*>(a.out + vbase + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     if (a.trace) {
       float* tp = a.trace + (tok * H + h) * DK * DK + col;
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     lds_barrier();  // the staged vectors and partial sums are rewritten next token
   }
 
-  if (!a.trace) {
+  if (a.writeback) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(sp + (rr + 32 * i) * DK) = S[i];
   }

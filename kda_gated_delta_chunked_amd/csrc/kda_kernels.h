@@ -132,7 +132,7 @@ struct DecodeArgs {
   const float* beta;          // [N * T, H]
   float* pool;                // [pool_size, H, 128, 128], updated in place
   const int32_t* state_indices;  // [N]; outside [0, pool_size): no state
-  uint16_t* out;              // [N * T, H, 128] bf16
+  uint16_t* out;              // [N * T, H, 128] bf16, or NULL (no outputs)
   int N;
   int T;
   int H;
@@ -140,7 +140,9 @@ struct DecodeArgs {
   float scale;
   int prologue;               // bit 0: L2-normalise q and k; bit 1: beta is a logit
   float* trace;               // NULL, or [N, T, H, 128, 128]: the state after each token
-                              // (then the pool is left as it is)
+  const int32_t* accepted;    // NULL (every request takes its T tokens), or [N]: request n
+                              // takes its first accepted[n] (outside [0, T]: none)
+  int writeback;              // store the advanced state back into the pool
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

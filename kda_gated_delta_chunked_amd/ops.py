@@ -147,6 +147,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_decode_verify.restype = ctypes.c_int
     lib.kda_decode_commit.argtypes = [DP, P, P, P, P, P]
     lib.kda_decode_commit.restype = ctypes.c_int
+    lib.kda_decode_advance.argtypes = [DP, P, P, P, P, P, P, P, P, P]
+    lib.kda_decode_advance.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -374,6 +376,15 @@ def decode_commit_raw(problem: DecodeProblem, state_pool, state_indices, state_t
                                  state_trace or None, accepted or None, stream or None)
 
 
+def decode_advance_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indices, accepted,
+                       stream) -> int:
+    """Call ``kda_decode_advance`` with raw integer pointers (0 for NULL); returns the status."""
+    lib = load_library()
+    return lib.kda_decode_advance(ctypes.byref(problem), q or None, k or None, v or None, g or None,
+                                  beta or None, state_pool or None, state_indices or None,
+                                  accepted or None, stream or None)
+
+
 def decode_validate_raw(problem: DecodeProblem, q, k, v, g, beta, state_pool, state_indices,
                         out) -> int:
     """Call ``kda_decode_validate`` with raw integer pointers; returns the status (host only)."""
@@ -457,9 +468,11 @@ def decode_verify(q, k, v, g, beta, state_pool, state_indices, *, scale: Optiona
                   out=None, state_trace=None, gate_lower_bound: float = -5.0, stream=None,
                   qk_l2norm: bool = False, beta_logit: bool = False):
     """Speculative verify: decode's update over the T draft tokens of every
-    request, with state_pool only read and the state after each token stored
-    to state_trace (fp32 [N, T, H, 128, 128], allocated when None).  Returns
-    (out, state_trace); decode_commit then keeps the accepted prefix."""
+    request, with state_pool only read.  state_trace: None allocates the trace
+    of the state after each token (fp32 [N, T, H, 128, 128]), False stores no
+    trace, or a tensor of that shape.  Returns (out, state_trace or None);
+    decode_commit (with a trace) or decode_advance (without) then keeps the
+    accepted prefix."""
     import torch
 
     prob = _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower_bound,
@@ -469,6 +482,8 @@ def decode_verify(q, k, v, g, beta, state_pool, state_indices, *, scale: Optiona
     dev = q.device
     if state_trace is None:
         state_trace = torch.empty((N, T, H, D, D), dtype=torch.float32, device=dev)
+    elif state_trace is False:
+        state_trace = None
     elif (tuple(state_trace.shape) != (N, T, H, D, D) or state_trace.dtype != torch.float32
           or state_trace.device != dev or not state_trace.is_contiguous()):
         raise ValueError(f"state_trace must be contiguous fp32 [{N}, {T}, {H}, {D}, {D}] on {dev}")
@@ -476,10 +491,33 @@ def decode_verify(q, k, v, g, beta, state_pool, state_indices, *, scale: Optiona
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         st = decode_verify_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                               _ptr(state_pool), _ptr(state_indices), _ptr(out), _ptr(state_trace),
-                               int(stream.cuda_stream))
+                               _ptr(state_pool), _ptr(state_indices), _ptr(out),
+                               0 if state_trace is None else _ptr(state_trace), int(stream.cuda_stream))
     _check(st, "kda_decode_verify")
     return out, state_trace
+
+
+def decode_advance(q, k, v, g, beta, state_pool, state_indices, accepted, *,
+                   scale: Optional[float] = None, gate_lower_bound: float = -5.0, stream=None,
+                   qk_l2norm: bool = False, beta_logit: bool = False):
+    """After a verify without a trace: each request's pool state advances by
+    its first accepted[n] tokens of the same drafts (int32 [N] on the device;
+    0 or out of range leaves it as it is), recomputed, with no outputs."""
+    import torch
+
+    prob = _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower_bound,
+                         qk_l2norm, beta_logit)
+    N = q.shape[0]
+    dev = q.device
+    if accepted.dtype != torch.int32 or tuple(accepted.shape) != (N,) or accepted.device != dev \
+            or not accepted.is_contiguous():
+        raise ValueError(f"accepted must be contiguous int32 [{N}] on {dev}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = decode_advance_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                _ptr(state_indices), _ptr(accepted), int(stream.cuda_stream))
+    _check(st, "kda_decode_advance")
 
 
 def decode_commit(state_pool, state_indices, state_trace, accepted, *, stream=None):

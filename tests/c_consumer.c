@@ -120,15 +120,18 @@ int main(void) {
    * every check would launch) */
   float* pool = (float*)addr(5);
   const int32_t* idx = (const int32_t*)addr(8);
-  printf("verify.no_trace %d\n", (int)kda_decode_verify(&d, (const uint16_t*)q, (const uint16_t*)k,
-                                                         (const uint16_t*)v, g, beta, pool, idx,
-                                                         (uint16_t*)out, NULL, NULL));
+  printf("verify.no_out %d\n", (int)kda_decode_verify(&d, (const uint16_t*)q, (const uint16_t*)k,
+                                                       (const uint16_t*)v, g, beta, pool, idx, NULL,
+                                                       (float*)addr(9), NULL));
   printf("verify.trace_on_pool %d\n", (int)kda_decode_verify(&d, (const uint16_t*)q, (const uint16_t*)k,
                                                               (const uint16_t*)v, g, beta, pool, idx,
                                                               (uint16_t*)out, pool + 4, NULL));
   printf("commit.no_accepted %d\n", (int)kda_decode_commit(&d, pool, idx, (const float*)addr(9), NULL, NULL));
   printf("commit.trace_on_pool %d\n",
          (int)kda_decode_commit(&d, pool, idx, pool + 4, (const int32_t*)addr(10), NULL));
+  printf("advance.no_accepted %d\n", (int)kda_decode_advance(&d, (const uint16_t*)q, (const uint16_t*)k,
+                                                               (const uint16_t*)v, g, beta, pool, idx, NULL,
+                                                               NULL));
 
   for (int s = -8; s <= 0; ++s) printf("status.%d %s\n", s, kda_status_string(s));
   return 0;

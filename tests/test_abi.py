@@ -391,8 +391,7 @@ def test_decode_verify_and_commit_rules():
     assert verify(_dprob(b, head_dim_k=64)) == UNSUPPORTED
     assert verify(out=a["pool"]) == OVERLAP
     assert verify(pool=a["pool"] + 4) == ALIGN
-    # and the trace: required, aligned, overlapping nothing (not even out = v)
-    assert verify(trace=0) == INVALID
+    # and the trace (optional): aligned, overlapping nothing (not even out = v)
     assert verify(trace=a["trace"] + 8) == ALIGN
     for name in ("q", "k", "v", "g", "beta", "pool", "idx", "out"):
         assert verify(trace=a[name]) == OVERLAP, name
@@ -415,6 +414,21 @@ def test_decode_verify_and_commit_rules():
         assert commit(pool=a[name]) == OVERLAP, name
     assert ops.decode_commit_raw(_dprob(b, N=0), 0, 0, 0, 0, 0) == OK
     assert commit(_dprob(b, N=1 << 20, T=16, H=2)) == TOO_LARGE
+
+    # the advance: the decode's inputs and pool, accepted instead of out
+    def advance(prob=None, **over):
+        d = dict(a)
+        d.update(over)
+        return ops.decode_advance_raw(prob or _dprob(b), d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                      d["pool"], d["idx"], d["acc"], 0)
+
+    assert advance(_dprob(b, T=0)) == INVALID
+    assert advance(_dprob(b, head_dim_k=64)) == UNSUPPORTED
+    assert advance(acc=0) == INVALID
+    assert advance(acc=a["acc"] + 4) == ALIGN
+    for name in ("q", "k", "v", "g", "beta", "idx", "acc"):
+        assert advance(pool=a[name]) == OVERLAP, name
+    assert ops.decode_advance_raw(_dprob(b, N=0), *[0] * 8, 0) == OK
 
 
 def test_state_dtype_rules():

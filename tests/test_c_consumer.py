@@ -70,8 +70,9 @@ def test_validation_results_from_c(consumer_output):
             "validate.overlap_out_q": OVERLAP, "validate.head_dim": UNSUPPORTED,
             "validate.bound": INVALID, "validate.no_workspace": WS,
             "decode.good": OK, "decode.empty_pool": INVALID,
-            "verify.no_trace": INVALID, "verify.trace_on_pool": OVERLAP,
-            "commit.no_accepted": INVALID, "commit.trace_on_pool": OVERLAP}
+            "verify.no_out": INVALID, "verify.trace_on_pool": OVERLAP,
+            "commit.no_accepted": INVALID, "commit.trace_on_pool": OVERLAP,
+            "advance.no_accepted": INVALID}
     for key, status in want.items():
         assert int(consumer_output[key]) == status, key
 

@@ -207,6 +207,18 @@ def test_decode_verify_trace_and_commit(N, T, H, P, empty):
     K.decode_commit(vpool, didx, trace, torch.full((N,), T, dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     assert np.array_equal(vpool.cpu().numpy(), gdpool), what
+    # the recompute path: a verify with no trace gives the same outputs and
+    # leaves the pool alone; an advance by the accepted counts then leaves the
+    # pool as the commit of the traced states did, bit for bit
+    npool = torch.from_numpy(pool).to(dev)
+    nout, ntrace = K.decode_verify(q, k, v, g, beta, npool, didx, scale=p.scale, state_trace=False)
+    torch.cuda.synchronize()
+    assert ntrace is None
+    assert torch.equal(nout.view(torch.int16), dout.view(torch.int16)), what
+    assert np.array_equal(npool.cpu().numpy(), pool), what
+    K.decode_advance(q, k, v, g, beta, npool, didx, torch.from_numpy(acc).to(dev), scale=p.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(npool.cpu().numpy(), want), what
 
 
 def test_decode_verify_input_prologue():
@@ -250,9 +262,10 @@ def test_decode_verify_input_prologue():
         assert rel_l2(gtrace[named, t], ref["pool"][idx[named]]) <= POOL_REL_L2, t
 
 
-def test_decode_verify_commit_graph_steps():
-    # one speculative step (verify, then commit of the accepted prefixes)
-    # captured in a HIP graph and replayed for three steps in a row on one pool,
+@pytest.mark.parametrize("mode", ["trace", "recompute"])
+def test_decode_verify_commit_graph_steps(mode):
+    # one speculative step (verify, then commit of the traced states or advance
+    # by recompute, of the accepted prefixes) captured in a HIP graph and replayed for three steps in a row on one pool,
     # with new drafts and new accepted lengths written into the captured
     # buffers each time and eager work between replays: every replay equals the
     # same two calls made eagerly, bit for bit, and the pool follows the oracle
@@ -286,8 +299,14 @@ def test_decode_verify_commit_graph_steps():
     trace = torch.empty((N, T, H, 128, 128), device=dev)
 
     def spec_step(stream):
-        K.decode_verify(q, k, v, g, beta, pool, didx, scale=p0.scale, out=out, state_trace=trace, stream=stream)
-        K.decode_commit(pool, didx, trace, acc_d, stream=stream)
+        if mode == "trace":
+            K.decode_verify(q, k, v, g, beta, pool, didx, scale=p0.scale, out=out, state_trace=trace,
+                            stream=stream)
+            K.decode_commit(pool, didx, trace, acc_d, stream=stream)
+        else:
+            K.decode_verify(q, k, v, g, beta, pool, didx, scale=p0.scale, out=out, state_trace=False,
+                            stream=stream)
+            K.decode_advance(q, k, v, g, beta, pool, didx, acc_d, scale=p0.scale, stream=stream)
 
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(dev)
@@ -306,8 +325,12 @@ def test_decode_verify_commit_graph_steps():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        eout, etrace = K.decode_verify(q, k, v, g, beta, epool, didx, scale=p.scale)
-        K.decode_commit(epool, didx, etrace, acc_d)
+        if mode == "trace":
+            eout, etrace = K.decode_verify(q, k, v, g, beta, epool, didx, scale=p.scale)
+            K.decode_commit(epool, didx, etrace, acc_d)
+        else:
+            eout, _ = K.decode_verify(q, k, v, g, beta, epool, didx, scale=p.scale, state_trace=False)
+            K.decode_advance(q, k, v, g, beta, epool, didx, acc_d, scale=p.scale)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eout.view(torch.int16)), s
         gpool = pool.cpu().numpy()
