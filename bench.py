@@ -197,11 +197,14 @@ def bench_decode(args, torch, K, synth) -> int:
     g = torch.from_numpy(p.g).to(dev).view(shp)
     beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
     rng = np.random.default_rng(2001)
+    sdt = args.decode_state
     pool = torch.from_numpy(rng.normal(0, 0.02, (N, H, 128, 128)).astype(np.float32)).to(dev)
+    if sdt == "bf16":
+        pool = pool.to(torch.bfloat16)
     idx = torch.from_numpy(rng.permutation(N).astype(np.int32)).to(dev)
     out = torch.empty_like(v)
     stream = torch.cuda.current_stream(dev)
-    prob = K.make_decode_problem(N, T, H, N, scale=p.scale)
+    prob = K.make_decode_problem(N, T, H, N, scale=p.scale, state_dtype=sdt)
 
     def step():
         st = K.decode_raw(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
@@ -224,18 +227,20 @@ def bench_decode(args, torch, K, synth) -> int:
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     ms_kernel = float(np.median(ms))
-    alg = N * H * (2 * 128 * 128 * 4) + N * T * H * (128 * 2 * 4 + 128 * 4 + 4)
+    es = 2 if sdt == "bf16" else 4
+    alg = N * H * (2 * 128 * 128 * es) + N * T * H * (128 * 2 * 4 + 128 * 4 + 4)
     achieved = alg / (ms_kernel * 1e-3) / 1e9
-    res = {"metric": "state-pool decode tokens/s (H=12, K=V=128, fp32 state)",
+    workload = f"decode_n{N}_t{T}" + ("_bf16" if sdt == "bf16" else "")
+    res = {"metric": f"state-pool decode tokens/s (H=12, K=V=128, {sdt} state)",
            "value": round(N * T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
            "data": "synthetic",
-           "config": {"workload": f"decode_n{N}_t{T}", "requests": N, "tokens_per_request": T,
-                      "H": H, "pool_size": N},
+           "config": {"workload": workload, "requests": N, "tokens_per_request": T,
+                      "H": H, "pool_size": N, "state_dtype": sdt},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic(f"decode_n{N}_t{T}", "decode", "kda_decode_kernel"),
+                        "traffic": measured_traffic(workload, "decode", "kda_decode_kernel"),
                         "kernel": "kda_decode_kernel", "kernel_ms": round(ms_kernel, 4),
                         "algorithmic_bytes": alg}}
     print(json.dumps(res), flush=True)
@@ -263,12 +268,15 @@ def bench_verify(args, torch, K, synth) -> int:
     g = torch.from_numpy(p.g).to(dev).view(shp)
     beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
     rng = np.random.default_rng(3001)
+    sdt = args.decode_state
     pool = torch.from_numpy(rng.normal(0, 0.02, (N, H, 128, 128)).astype(np.float32)).to(dev)
+    if sdt == "bf16":
+        pool = pool.to(torch.bfloat16)
     idx = torch.from_numpy(rng.permutation(N).astype(np.int32)).to(dev)
     acc_h = rng.integers(0, T + 1, N).astype(np.int32)
     acc = torch.from_numpy(acc_h).to(dev)
     out = torch.empty_like(v)
-    trace = torch.empty((N, T, H, 128, 128), device=dev)
+    trace = torch.empty((N, T, H, 128, 128), dtype=pool.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step_trace():
@@ -291,20 +299,21 @@ def bench_verify(args, torch, K, synth) -> int:
 
     ms_trace = timed(step_trace)
     ms_re = timed(step_recompute)
-    state = 128 * 128 * 4
+    state = 128 * 128 * (2 if sdt == "bf16" else 4)
     taken = int(acc_h.sum())
     tok_in = 128 * 2 * 3 + 128 * 4 + 4          # q, k, v, g, beta per token-head
     # recompute: the verify reads every state, the inputs and writes the
     # outputs; the advance reads and writes the states of requests that took a
     # draft, with the inputs of the drafts taken
     alg = N * H * state + N * T * H * (tok_in + 256) + int((acc_h > 0).sum()) * H * 2 * state + taken * H * tok_in
-    res = {"metric": "speculative verify step draft tokens/s (H=12, K=V=128, fp32 state)",
+    res = {"metric": f"speculative verify step draft tokens/s (H=12, K=V=128, {sdt} state)",
            "value": round(N * T / (ms_re * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_re, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
            "data": "synthetic",
-           "config": {"workload": f"verify_n{N}_t{T}", "requests": N, "drafts_per_request": T, "H": H,
-                      "pool_size": N, "accepted_mean": round(float(acc_h.mean()), 3)},
+           "config": {"workload": f"verify_n{N}_t{T}" + ("_bf16" if sdt == "bf16" else ""), "requests": N,
+                      "drafts_per_request": T, "H": H, "pool_size": N, "state_dtype": sdt,
+                      "accepted_mean": round(float(acc_h.mean()), 3)},
            "paths": {"recompute_ms_per_step": round(ms_re, 4), "trace_ms_per_step": round(ms_trace, 4),
                      "trace_bytes": N * T * H * state},
            "roofline": {"bound": "hbm", "achieved": round(alg / (ms_re * 1e-3) / 1e9, 1),
@@ -336,6 +345,8 @@ def main() -> int:
                     help="instead of the prefill, time a speculative step of N requests with T draft "
                          "tokens each (verify, then commit of the traced states or advance by "
                          "recompute; H = 12, pool of N states)")
+    ap.add_argument("--decode-state", default="fp32", choices=("fp32", "bf16"),
+                    help="state pool element type of --decode and --verify")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, --steps times "
                          "(reference for the HBM byte counters)")

@@ -272,6 +272,12 @@ typedef struct {
   float gate_lower_bound;    /* caller's promise g >= bound; must lie in [-5, 0] */
   int64_t pool_size;         /* states in the pool, >= 1 */
   int32_t prologue;          /* kda_prologue flags, as for kda_prefill */
+  int32_t state_dtype;       /* kda_state_dtype of the pool and of a verify's state
+                                trace: fp32, or bf16 (same layouts, 2-byte elements,
+                                passed through the same pointer types).  The tokens
+                                run in fp32 from the widened state; a bf16 state is
+                                rounded to nearest even once, when it is stored (the
+                                BF16 state of FlashInfer PR #4262's benchmark) */
 } kda_decode_problem;
 
 /* Host-side checks of kda_decode without launching: sizes, NULL rules,

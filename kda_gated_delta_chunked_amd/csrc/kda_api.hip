@@ -300,6 +300,8 @@ kda_status decode_check(const kda_decode_problem* p, const void* q, const void* 
       p->gate_lower_bound > 0.0f)
     return KDA_ERR_INVALID_ARG;
   if (p->prologue & ~(KDA_PROLOGUE_QK_L2NORM | KDA_PROLOGUE_BETA_LOGIT)) return KDA_ERR_INVALID_ARG;
+  if (p->state_dtype != KDA_STATE_F32 && p->state_dtype != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;
+  const uint64_t es = p->state_dtype == KDA_STATE_BF16 ? 2 : 4;  // bytes per state element
   const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
   if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if (N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices))
@@ -315,7 +317,7 @@ kda_status decode_check(const kda_decode_problem* p, const void* q, const void* 
   const uint64_t tok_bf16 = (uint64_t)N * T * H * kHeadDim * 2;
   const Range rq = range_of(q, tok_bf16), rk = range_of(k, tok_bf16), rv = range_of(v, tok_bf16);
   const Range rg = range_of(g, tok_bf16 * 2), rb = range_of(beta, (uint64_t)N * T * H * 4);
-  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
+  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * es);
   const Range ridx = range_of(state_indices, (uint64_t)N * 4);
   const Range racc = range_of(accepted, (uint64_t)N * 4);
   const Range rout = range_of(out, tok_bf16);
@@ -327,7 +329,7 @@ kda_status decode_check(const kda_decode_problem* p, const void* q, const void* 
     if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
   if (trace) {
     // the trace is written: it overlaps nothing else
-    const Range rtr = range_of(trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * 4);
+    const Range rtr = range_of(trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * es);
     for (const Range& r : {rq, rk, rv, rg, rb, rpool, ridx, rout})
       if (overlaps(rtr, r)) return KDA_ERR_OVERLAP;
   }
@@ -356,6 +358,7 @@ kda::DecodeArgs decode_args(const kda_decode_problem* p, const uint16_t* q, cons
   a.trace = trace;
   a.accepted = accepted;
   a.writeback = writeback ? 1 : 0;
+  a.state_bf16 = p->state_dtype == KDA_STATE_BF16 ? 1 : 0;
   return a;
 }
 }  // namespace
@@ -616,16 +619,18 @@ kda_status kda_decode_commit(const kda_decode_problem* p, float* state_pool,
   if (p->head_dim_k != kHeadDim || p->head_dim_v != kHeadDim) return KDA_ERR_UNSUPPORTED;
   if (p->num_seqs < 0 || p->tokens_per_seq < 1 || p->num_heads < 1 || p->pool_size < 1)
     return KDA_ERR_INVALID_ARG;
+  if (p->state_dtype != KDA_STATE_F32 && p->state_dtype != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;
+  const uint64_t es = p->state_dtype == KDA_STATE_BF16 ? 2 : 4;
   const int64_t N = p->num_seqs, T = p->tokens_per_seq, H = p->num_heads;
   if (N * T * H * kHeadDim > kInt32Max) return KDA_ERR_TOO_LARGE;
   if (N > 0 && (!state_pool || !state_indices || !state_trace || !accepted)) return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {state_pool, state_indices, state_trace, accepted};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGNMENT;
-  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * 4);
+  const Range rpool = range_of(state_pool, (uint64_t)p->pool_size * H * kHeadDim * kHeadDim * es);
   const Range ridx = range_of(state_indices, (uint64_t)N * 4);
   const Range racc = range_of(accepted, (uint64_t)N * 4);
-  const Range rtr = range_of(state_trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * 4);
+  const Range rtr = range_of(state_trace, (uint64_t)N * T * H * kHeadDim * kHeadDim * es);
   for (const Range& r : {ridx, racc, rtr})
     if (overlaps(rpool, r)) return KDA_ERR_OVERLAP;
   if (N == 0) return KDA_OK;
@@ -638,6 +643,7 @@ kda_status kda_decode_commit(const kda_decode_problem* p, float* state_pool,
   a.T = p->tokens_per_seq;
   a.H = p->num_heads;
   a.pool_size = p->pool_size;
+  a.state_bf16 = p->state_dtype == KDA_STATE_BF16 ? 1 : 0;
   return kda::launch_decode_commit(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -17,8 +17,9 @@
 // run in four workgroups.  Thread (rr = tid / 8, cg = tid % 8) holds rows
 // rr + 32 i (i = 0..3) of columns 4 cg .. 4 cg + 3 as four float4 registers,
 // read once from the pool, kept across the call's tokens and written back in
-// place.  The path is bound by HBM: 64 KiB of state in and out per (sequence,
-// head).
+// place.  The path is bound by HBM: 64 KiB of fp32 state in and out per
+// (sequence, head), 32 KiB with a bf16 pool (widened on load, the tokens in
+// fp32, rounded to nearest even once on store).
 //
 // Speculative steps use the same kernel: a verify runs the T draft tokens
 // with the pool only read (write-back off), optionally storing the state after
@@ -46,6 +47,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   const b2 r = __builtin_convertvector((f2){x, y}, b2);
   return __builtin_bit_cast(uint32_t, r);
+}
+
+// four bf16 (two packed pairs, low half first) to four floats (exact)
+__device__ __forceinline__ float4 bf16x4_to_f32(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
 }
 
 __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
@@ -81,10 +88,33 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
   }
   if (Tn == 0) return;  // nothing accepted: the pool keeps its state
 
-  float* sp = a.pool + ((int64_t)idx * H + h) * DK * DK + col;
+  // element offset of this thread's first state element in the pool (fp32 or
+  // bf16 elements)
+  const int64_t se = ((int64_t)idx * H + h) * DK * DK + col;
   float4 S[4];
+  if (a.state_bf16) {
+    const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.pool) + se;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const float4*>(sp + (rr + 32 * i) * DK);
+    for (int i = 0; i < 4; ++i) S[i] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(sp + (rr + 32 * i) * DK));
+  } else {
+    const float* sp = a.pool + se;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const float4*>(sp + (rr + 32 * i) * DK);
+  }
+  // the state's four rows to `dst` at element offset e0: fp32, or bf16
+  // rounded to nearest even
+  auto store_state = [&](float* dst, int64_t e0) {
+    if (a.state_bf16) {
+      uint16_t* p16 = reinterpret_cast<uint16_t*>(dst) + e0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint2*>(p16 + (rr + 32 * i) * DK) =
+            make_uint2(pack_bf16x2(S[i].x, S[i].y), pack_bf16x2(S[i].z, S[i].w));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(dst + e0 + (rr + 32 * i) * DK) = S[i];
+    }
+  };
 
   // The per-token vectors are fetched one token ahead into registers (threads
   // 0..127: k, q, g of row tid; 128..159: v of this workgroup's columns; 160:
@@ -197,18 +227,11 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     }
     if (rr == 0 && a.out)
       *reinterpret_cast<uint2*>(a.out + vbase + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    if (a.trace) {
-      float* tp = a.trace + (tok * H + h) * DK * DK + col;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(tp + (rr + 32 * i) * DK) = S[i];
-    }
+    if (a.trace) store_state(a.trace, (tok * H + h) * DK * DK + col);
     lds_barrier();  // the staged vectors and partial sums are rewritten next token
   }
 
-  if (a.writeback) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(sp + (rr + 32 * i) * DK) = S[i];
-  }
+  if (a.writeback) store_state(a.pool, se);
 }
 
 // One workgroup per (request, head, quarter of the columns), the decode
@@ -223,11 +246,21 @@ __global__ __launch_bounds__(256) void kda_decode_commit_kernel(DecodeCommitArgs
   const int idx = a.state_indices[n], acc = a.accepted[n];
   if (idx < 0 || (int64_t)idx >= a.pool_size || acc < 1 || acc > a.T) return;
   const int col = quarter * QCOLS + 4 * cg;
-  const float* src = a.trace + (((int64_t)n * a.T + acc - 1) * H + h) * DK * DK + col;
-  float* dst = a.pool + ((int64_t)idx * H + h) * DK * DK + col;
+  const int64_t se = (((int64_t)n * a.T + acc - 1) * H + h) * DK * DK + col;
+  const int64_t de = ((int64_t)idx * H + h) * DK * DK + col;
+  if (a.state_bf16) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.trace) + se;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.pool) + de;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<float4*>(dst + (rr + 32 * i) * DK) = *reinterpret_cast<const float4*>(src + (rr + 32 * i) * DK);
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint2*>(dst + (rr + 32 * i) * DK) = *reinterpret_cast<const uint2*>(src + (rr + 32 * i) * DK);
+  } else {
+    const float* src = a.trace + se;
+    float* dst = a.pool + de;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(dst + (rr + 32 * i) * DK) = *reinterpret_cast<const float4*>(src + (rr + 32 * i) * DK);
+  }
 }
 
 }  // namespace

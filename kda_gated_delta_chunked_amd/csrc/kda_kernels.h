@@ -130,7 +130,7 @@ struct DecodeArgs {
   const uint16_t* v;
   const float* g;             // [N * T, H, 128]
   const float* beta;          // [N * T, H]
-  float* pool;                // [pool_size, H, 128, 128], updated in place
+  float* pool;                // [pool_size, H, 128, 128] fp32 or bf16, updated in place
   const int32_t* state_indices;  // [N]; outside [0, pool_size): no state
   uint16_t* out;              // [N * T, H, 128] bf16, or NULL (no outputs)
   int N;
@@ -143,6 +143,7 @@ struct DecodeArgs {
   const int32_t* accepted;    // NULL (every request takes its T tokens), or [N]: request n
                               // takes its first accepted[n] (outside [0, T]: none)
   int writeback;              // store the advanced state back into the pool
+  int state_bf16;             // pool and trace hold bf16 states (else fp32)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
@@ -158,6 +159,7 @@ struct DecodeCommitArgs {
   int T;
   int H;
   int64_t pool_size;
+  int state_bf16;             // pool and trace hold bf16 states (else fp32)
 };
 
 hipError_t launch_decode_commit(const DecodeCommitArgs& a, hipStream_t stream);

@@ -61,16 +61,17 @@ class DecodeProblem(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
                 ("head_dim_v", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("gate_lower_bound", ctypes.c_float), ("pool_size", ctypes.c_int64),
-                ("prologue", ctypes.c_int32)]
+                ("prologue", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 def make_decode_problem(num_seqs: int, tokens_per_seq: int, num_heads: int, pool_size: int, *,
                         scale: float, gate_lower_bound: float = -5.0,
                         head_dim_k: int = HEAD_DIM, head_dim_v: int = HEAD_DIM,
-                        qk_l2norm: bool = False, beta_logit: bool = False) -> DecodeProblem:
+                        qk_l2norm: bool = False, beta_logit: bool = False,
+                        state_dtype: str = "fp32") -> DecodeProblem:
     return DecodeProblem(int(num_seqs), int(tokens_per_seq), int(num_heads), int(head_dim_k),
                          int(head_dim_v), float(scale), float(gate_lower_bound), int(pool_size),
-                         (1 if qk_l2norm else 0) | (2 if beta_logit else 0))
+                         (1 if qk_l2norm else 0) | (2 if beta_logit else 0), STATE_DTYPES[state_dtype])
 
 
 def make_problem(num_seqs: int, total_tokens: int, num_heads: int, *, scale: float,
@@ -406,9 +407,11 @@ def _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("libkda runs on the GPU: tensors must be on a cuda (HIP) device")
+    if state_pool.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"state_pool must be float32 or bfloat16, got {state_pool.dtype}")
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
                         ("g", g, torch.float32), ("beta", beta, torch.float32),
-                        ("state_pool", state_pool, torch.float32),
+                        ("state_pool", state_pool, state_pool.dtype),
                         ("state_indices", state_indices, torch.int32)):
         if t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
@@ -426,7 +429,8 @@ def _decode_setup(q, k, v, g, beta, state_pool, state_indices, scale, gate_lower
         scale = D ** -0.5
     return make_decode_problem(N, T, H, state_pool.shape[0], scale=scale,
                                gate_lower_bound=gate_lower_bound, head_dim_k=D, head_dim_v=D,
-                               qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+                               qk_l2norm=qk_l2norm, beta_logit=beta_logit,
+                               state_dtype="bf16" if state_pool.dtype == torch.bfloat16 else "fp32")
 
 
 def _decode_out(q, v, out):
@@ -445,8 +449,8 @@ def decode(q, k, v, g, beta, state_pool, state_indices, *, scale: Optional[float
     """One state-pool decode step on the GPU.
 
     q, k, v: bf16 [N, T, H, 128] (T tokens per request; T = 1 for decode).
-    g: fp32 like q; beta: fp32 [N, T, H].  state_pool: fp32 [P, H, 128, 128],
-    updated in place.  state_indices: int32 [N]; entries outside [0, P) mark
+    g: fp32 like q; beta: fp32 [N, T, H].  state_pool: fp32 or bf16 [P, H, 128, 128],
+    updated in place (bf16: widened on load, rounded to nearest even on store).  state_indices: int32 [N]; entries outside [0, P) mark
     empty request slots (zero outputs, no state touched).  Returns out, with
     q's shape (``out=v`` overwrites v)."""
     import torch
@@ -480,13 +484,14 @@ def decode_verify(q, k, v, g, beta, state_pool, state_indices, *, scale: Optiona
     out = _decode_out(q, v, out)
     N, T, H, D = q.shape
     dev = q.device
+    sdt = state_pool.dtype
     if state_trace is None:
-        state_trace = torch.empty((N, T, H, D, D), dtype=torch.float32, device=dev)
+        state_trace = torch.empty((N, T, H, D, D), dtype=sdt, device=dev)
     elif state_trace is False:
         state_trace = None
-    elif (tuple(state_trace.shape) != (N, T, H, D, D) or state_trace.dtype != torch.float32
+    elif (tuple(state_trace.shape) != (N, T, H, D, D) or state_trace.dtype != sdt
           or state_trace.device != dev or not state_trace.is_contiguous()):
-        raise ValueError(f"state_trace must be contiguous fp32 [{N}, {T}, {H}, {D}, {D}] on {dev}")
+        raise ValueError(f"state_trace must be contiguous {sdt} [{N}, {T}, {H}, {D}, {D}] on {dev}")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
@@ -530,9 +535,11 @@ def decode_commit(state_pool, state_indices, state_trace, accepted, *, stream=No
         raise ValueError("state_trace must be [N, T, H, 128, 128]")
     N, T, H, D, _ = state_trace.shape
     dev = state_trace.device
-    for name, t, dt in (("state_pool", state_pool, torch.float32),
+    if state_pool.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"state_pool must be float32 or bfloat16, got {state_pool.dtype}")
+    for name, t, dt in (("state_pool", state_pool, state_pool.dtype),
                         ("state_indices", state_indices, torch.int32),
-                        ("state_trace", state_trace, torch.float32),
+                        ("state_trace", state_trace, state_pool.dtype),
                         ("accepted", accepted, torch.int32)):
         if t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
@@ -544,7 +551,8 @@ def decode_commit(state_pool, state_indices, state_trace, accepted, *, stream=No
         raise ValueError(f"state_pool must be [P, {H}, {D}, {D}]")
     if tuple(state_indices.shape) != (N,) or tuple(accepted.shape) != (N,):
         raise ValueError(f"state_indices and accepted must be [{N}]")
-    prob = make_decode_problem(N, T, H, state_pool.shape[0], scale=1.0, head_dim_k=D, head_dim_v=D)
+    prob = make_decode_problem(N, T, H, state_pool.shape[0], scale=1.0, head_dim_k=D, head_dim_v=D,
+                               state_dtype="bf16" if state_pool.dtype == torch.bfloat16 else "fp32")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):

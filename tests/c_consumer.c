@@ -59,6 +59,7 @@ int main(void) {
   FIELD(kda_decode_problem, gate_lower_bound);
   FIELD(kda_decode_problem, pool_size);
   FIELD(kda_decode_problem, prologue);
+  FIELD(kda_decode_problem, state_dtype);
 
   /* workspace sizes: fixed B8 T8192 H12, a packed batch with 3 offsets per
    * sequence, the one-launch schedule (no workspace), B1 T8192 H12 (with the

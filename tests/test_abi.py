@@ -361,6 +361,26 @@ def test_decode_validation_rules():
     assert dv(_dprob(b, N=1 << 20, T=16, H=2), *b.args()) == TOO_LARGE
 
 
+def test_decode_state_dtype_rules():
+    # a bf16 pool holds 2-byte elements: a buffer right after its extent does
+    # not overlap it, while the same placement would overlap an fp32 pool
+    b = DecodeBufs()
+    dv = ops.decode_validate_raw
+    bad = _dprob(b)
+    bad.state_dtype = 2
+    assert dv(bad, *b.args()) == INVALID
+    far = 1 << 47
+    half = b.P * b.H * 128 * 128 * 2
+    for dt, want in (("bf16", OK), ("fp32", OVERLAP)):
+        prob = ops.make_decode_problem(b.N, b.T, b.H, b.P, scale=0.088, state_dtype=dt)
+        assert dv(prob, *b.args(pool=far, idx=far + half)) == want, dt
+    # the commit checks it too
+    bad_c = _dprob(b)
+    bad_c.state_dtype = 3
+    assert ops.decode_commit_raw(bad_c, b.addr["pool"], b.addr["idx"], b.addr["trace"], b.addr["acc"], 0) \
+        == INVALID
+
+
 def test_decode_rejects_on_the_host():
     # argument errors come back before anything touches a device
     b = DecodeBufs()

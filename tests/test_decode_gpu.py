@@ -349,3 +349,112 @@ def test_decode_verify_commit_graph_steps(mode):
         assert np.array_equal(gpool[untouched], cpu_pool[untouched]), s
         cpu_pool = gpool.copy()
         _ = (q.float() * 2).sum().item()   # eager work between replays
+
+
+# a bf16 pool: the stored state is rounded to bf16 once per call (7 fraction
+# bits, nearest even: a relative RMS error of at most 2^-7 / sqrt(12) = 2.3e-3)
+# on top of the fp32 token loop, so the pool is held to 3.5e-3, the bound the
+# prefill's bf16 states use
+BF16_POOL_REL_L2 = 3.5e-3
+
+
+def _bf16_tensor(x, dev):
+    import torch
+    from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32
+    return torch.from_numpy(bf16_bits_from_f32(np.ascontiguousarray(x, np.float32)).view(np.int16)).to(dev) \
+        .view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("N,T,H,P,empty", [(37, 1, 3, 50, 5), (8, 4, 12, 9, 1), (1024, 1, 12, 1100, 32)])
+def test_decode_bf16_pool(N, T, H, P, empty):
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32, f32_from_bf16_bits
+    dev = torch.device("cuda", 0)
+    p, pool, idx = _case(N, T, H, P, seed=220 + N + T, empty=empty)
+    pool_b = f32_from_bf16_bits(bf16_bits_from_f32(pool))     # the values a bf16 pool holds
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    shp = (N, T, H, 128)
+    q, k, v = bf16(p.q).view(shp), bf16(p.k).view(shp), bf16(p.v).view(shp)
+    g = torch.from_numpy(p.g).to(dev).view(shp)
+    beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
+    dpool = _bf16_tensor(pool_b, dev)
+    didx = torch.from_numpy(idx).to(dev)
+    out = K.decode(q, k, v, g, beta, dpool, didx, scale=p.scale)
+    torch.cuda.synchronize()
+    gout = out.float().cpu().numpy().reshape(N * T, H, 128)
+    gpool = dpool.float().cpu().numpy()
+    ref = oracle.decode(p.q, p.k, p.v, p.g, p.beta, scale=p.scale, num_seqs=N, tokens_per_seq=T,
+                        state_pool=pool_b, state_indices=idx)
+    what = f"bf16 pool N{N} T{T} H{H} P{P}"
+    assert np.all(np.isfinite(gout)), what
+    assert float(np.max(np.abs(gout - ref["out"]))) <= OUT_MAX_ABS, what
+    assert rel_l2(gout, ref["out"]) <= OUT_REL_L2, what
+    named = sorted(set(int(i) for i in idx if 0 <= i < P))
+    assert rel_l2(gpool[named], ref["pool"][named]) <= BF16_POOL_REL_L2, what
+    others = [i for i in range(P) if i not in named]
+    assert np.array_equal(gpool[others], pool_b[others]), what
+    for n, i in enumerate(idx):
+        if not (0 <= i < P):
+            assert not np.any(gout[n * T:(n + 1) * T]), what
+
+
+def test_decode_bf16_pool_speculative():
+    # the speculative paths on a bf16 pool (a bf16 trace): outputs and the
+    # last traced state are kda_decode's bit for bit, a commit of every draft
+    # leaves the pool as kda_decode does, and the advance equals the commit
+    import torch
+    import kda_gated_delta_chunked_amd as K
+    from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32, f32_from_bf16_bits
+    dev = torch.device("cuda", 0)
+    N, T, H, P = 37, 3, 2, 40
+    p, pool, idx = _case(N, T, H, P, seed=230, empty=4)
+    pool_b = f32_from_bf16_bits(bf16_bits_from_f32(pool))
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+    shp = (N, T, H, 128)
+    q, k, v = bf16(p.q).view(shp), bf16(p.k).view(shp), bf16(p.v).view(shp)
+    g = torch.from_numpy(p.g).to(dev).view(shp)
+    beta = torch.from_numpy(p.beta).to(dev).view(N, T, H)
+    didx = torch.from_numpy(idx).to(dev)
+    acc_h = np.random.default_rng(231).integers(0, T + 1, N).astype(np.int32)
+    acc_h[0] = T
+    acc = torch.from_numpy(acc_h).to(dev)
+    vpool = _bf16_tensor(pool_b, dev)
+    vout, trace = K.decode_verify(q, k, v, g, beta, vpool, didx, scale=p.scale)
+    assert trace.dtype == torch.bfloat16
+    dpool = _bf16_tensor(pool_b, dev)
+    dout = K.decode(q, k, v, g, beta, dpool, didx, scale=p.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(vout.view(torch.int16), dout.view(torch.int16))
+    assert torch.equal(vpool.view(torch.int16), _bf16_tensor(pool_b, dev).view(torch.int16))
+    named = [n for n in range(N) if 0 <= idx[n] < P]
+    for n in named:
+        assert torch.equal(trace[n, T - 1].view(torch.int16), dpool[int(idx[n])].view(torch.int16)), n
+    # commit of every draft == kda_decode; commit of the accepted counts == advance
+    cpool = _bf16_tensor(pool_b, dev)
+    K.decode_commit(cpool, didx, trace, torch.full((N,), T, dtype=torch.int32, device=dev))
+    apool, bpool = _bf16_tensor(pool_b, dev), _bf16_tensor(pool_b, dev)
+    K.decode_commit(apool, didx, trace, acc)
+    _, none = K.decode_verify(q, k, v, g, beta, bpool, didx, scale=p.scale, state_trace=False)
+    K.decode_advance(q, k, v, g, beta, bpool, didx, acc, scale=p.scale)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(cpool.view(torch.int16), dpool.view(torch.int16))
+    assert torch.equal(apool.view(torch.int16), bpool.view(torch.int16))
+    # and the advanced pool against the oracle's decode of each accepted prefix
+    gpool = bpool.float().cpu().numpy()
+    for n in named:
+        a = int(acc_h[n])
+        if a == 0:
+            assert np.array_equal(gpool[idx[n]], pool_b[idx[n]]), n
+            continue
+        sl = slice(n * T, n * T + a)
+        ref = oracle.decode(p.q[sl], p.k[sl], p.v[sl], p.g[sl], p.beta[sl], scale=p.scale, num_seqs=1,
+                            tokens_per_seq=a, state_pool=pool_b, state_indices=idx[n:n + 1])
+        assert rel_l2(gpool[idx[n]], ref["pool"][idx[n]]) <= BF16_POOL_REL_L2, n
