@@ -139,9 +139,10 @@ def _prefix(bits, N, T, t):
 
 # speculative verify: T draft tokens per request, pool only read, the state
 # after every token in the trace; then a commit of each request's accepted
-# prefix.  The last shape is the decode bench size with 4 drafts per request.
+# prefix.  The last shape is the verify bench size (1024 requests x 4 drafts,
+# a 3.2 GB trace).
 @pytest.mark.parametrize("N,T,H,P,empty", [(1, 1, 1, 1, 0), (6, 4, 3, 9, 1), (37, 3, 2, 40, 4),
-                                           (256, 4, 12, 300, 8)])
+                                           (256, 4, 12, 300, 8), (1024, 4, 12, 1100, 16)])
 def test_decode_verify_trace_and_commit(N, T, H, P, empty):
     import torch
     import kda_gated_delta_chunked_amd as K
