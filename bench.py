@@ -9,6 +9,13 @@ With the two-launch schedule, each launch is also timed on its own (the
 library's split-stage calls) for the roofline of the dominant kernel.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The default warm-up is 100 steps (about 60 ms of work at B8 T8192): after an
+idle spell the GPU runs the first 30 ms or so about 4.5% slower (measured in
+blocks of 50 calls: 0.578-0.582 ms per call in the block after a 50 ms pause,
+0.553 ms in the blocks that follow it), so a shorter warm-up times part of
+that ramp.  The per-call timing blocks each start with 20 untimed calls for
+the same reason.
 """
 from __future__ import annotations
 
@@ -327,8 +334,8 @@ def bench_verify(args, torch, K, synth) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="b8_t8192")
     ap.add_argument("--value-split", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--chain-parts", type=int, default=0,
@@ -421,11 +428,14 @@ def main() -> int:
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])), wall
 
-    def per_call(fn, calls, before=None):
+    def per_call(fn, calls, before=None, lead=20):
         """Event-timed milliseconds of each of `calls` calls of fn (optionally
-        preceded, outside the events, by `before`)."""
+        preceded, outside the events, by `before`), after `lead` untimed
+        calls."""
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(calls)]
+        for _ in range(lead):
+            fn()
         for a, b in ev:
             if before is not None:
                 before()

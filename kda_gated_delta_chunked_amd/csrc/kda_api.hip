@@ -510,11 +510,19 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     a.pass = 0;
     a.chain = pieces >= 2 ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bytes) : nullptr;
     const int64_t prepare_slots = cu_seqlens ? slots : (int64_t)p->num_seqs * a.slots_per_seq;
-    const int stages = p->stages ? p->stages : (KDA_STAGE_PREPARE | KDA_STAGE_RECURRENCE);
     // measured on MI355X, ms per call, normal / non-temporal workspace
     // stores: B8 T8192 0.643 / 0.630, B1 T8192 0.252 / 0.272, packed 8 x 1024
     // 0.091 / 0.093 (the last two keep their workspace in the cache)
     const bool stream_ws = bytes > kDecompCacheBytes;
+    // a slot's heads on one XCD, also only for a workspace past the cache.
+    // Measured on MI355X, outputs bit for bit the same, ms per call with
+    // slot-major order / heads on one XCD: B8 T8192 0.560 / 0.552 (prepare
+    // 0.289 / 0.282), 16 ragged + checkpoints 0.689 / 0.678, 32 ragged 0.579
+    // / 0.570, B6 T8192 0.471 / 0.468; with the workspace in the cache no
+    // gain (B8 T1024 0.075 both ways, B1 T8192 0.133 both ways) or a loss
+    // (B1 T512 0.034 / 0.035: the prepare alike, the recurrence slower)
+    a.prep_xcd = stream_ws;
+    const int stages = p->stages ? p->stages : (KDA_STAGE_PREPARE | KDA_STAGE_RECURRENCE);
     err = kda::launch_decomp(a, vsplit, prepare_slots, stages, stream_ws, st_);
   } else {
     kda::FusedArgs a;

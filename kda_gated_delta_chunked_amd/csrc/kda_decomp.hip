@@ -453,9 +453,18 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
 
   const int H = a.H;
   const int64_t bid = blockIdx.x;
-  const int64_t s = bid / H;
-  const int h = (int)(bid - s * H);
+  int64_t s;
+  int h;
+  if (a.prep_xcd) {
+    const int64_t r = bid >> 3;
+    s = (r / H) * 8 + (bid & 7);
+    h = (int)(r - (r / H) * H);
+  } else {
+    s = bid / H;
+    h = (int)(bid - s * H);
+  }
   if (s >= a.slot_bound) return;
+  if (!a.cu_seqlens && s >= (int64_t)a.N * a.slots_per_seq) return;
 
   // slot -> (sequence, segment)
   int n, j;
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   seg_range(si, j, lo_t, hi_t);
   const int off = CH - (hi_t - lo_t);
   const int64_t tok0 = si.bos + lo_t - off;        // token of tile row 0
-  unsigned char* slot = a.slots + (size_t)bid * kDecompSlotBytes;
+  unsigned char* slot = a.slots + (size_t)(s * H + h) * kDecompSlotBytes;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q = lane & 15;
   const int i = w;
@@ -1626,7 +1635,7 @@ hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots,
       hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    const int64_t blocks = prepare_slots * a.H;
+    const int64_t blocks = (a.prep_xcd ? (prepare_slots + 7) / 8 * 8 : prepare_slots) * a.H;
     if (blocks > 0) {
       if (stream_ws)
         hipLaunchKernelGGL(kda_prepare_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);

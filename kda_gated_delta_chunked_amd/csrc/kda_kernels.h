@@ -78,6 +78,12 @@ struct DecompArgs {
   int64_t slots_per_seq;      // fixed layout: slots owned by each sequence
   int64_t slot_bound;         // slots the workspace holds
   float scale;
+  // prepare launch order.  0: block b prepares slot b / H, head b % H.  1:
+  // block b prepares slot 8 (b / 8 / H) + b % 8, head (b / 8) % H.  Blocks go
+  // to the 8 XCDs in turn, so with 1 the H workgroups of a slot share one XCD
+  // and its L2 fetches the slot's beta rows (all heads of a token in one
+  // row) once instead of on up to 8 XCDs.
+  int prep_xcd;
   // chain split (pieces >= 2): each (sequence, head)'s segments are cut into
   // `pieces` consecutive ranges; `chain` holds per pair and piece three fp32
   // 128 x 128 matrices (chain_matrix).  pass 0: no split; 1 and 2: the two
@@ -113,7 +119,7 @@ inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64
 
 // vsplit = workgroups per (sequence, head): 1, 2, 4 or 8.  prepare_slots =
 // slots the prepare launch covers (fixed layout: N * slots_per_seq; packed:
-// slot_bound).
+// slot_bound), rounded up to a multiple of 8 when a.prep_xcd is set.
 // stages: bit 0 = the prepare launch (and the slot plan), bit 1 = the recurrence.
 // stream_ws: the prepare writes the workspace with non-temporal stores (for a
 // workspace that does not stay in the Infinity Cache until the recurrence).

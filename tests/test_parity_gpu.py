@@ -300,6 +300,21 @@ def test_full_size_workloads(name, variant):
     _report(f"{name} {variant}", assert_parity(gpu, ref, name, p.cu_seqlens))
 
 
+def test_fixed_layout_streamed_workspace_odd_slot_count():
+    # a fixed layout whose workspace is past the Infinity Cache bound, so the
+    # prepare streams it and runs the H workgroups of a slot on one XCD, its
+    # grid rounded up to whole groups of 8 slots; here 3 x 258 = 774 slots
+    # (16,400 tokens and one checkpoint per sequence), not a multiple of 8
+    import kda_gated_delta_chunked_amd as K
+    p = synth.make_problem([16400] * 3, 6, seed=41, fixed=True, init_state=True, ckpt="inside")
+    prob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, variant="decomp", ckpt_per_seq=1)
+    assert K.workspace_size(prob) > 176 << 20
+    ref = oracle.prefill_problem(p)
+    gpu = run_gpu(p, variant="decomp")
+    _report("fixed 3 x 16400 H6, streamed workspace",
+            assert_parity(gpu, ref, "odd slots", p.cu_seqlens))
+
+
 def test_decomp_matches_fused_on_packed_layout_as_separate_runs():
     # packed sequences are independent: the packed call equals per-sequence
     # fixed calls bit for bit (chunks align to each sequence start)
