@@ -12,14 +12,17 @@
 // so each token needs two reductions over the 128 key rows of the state,
 // and no chunking.
 //
-// One workgroup of 256 threads owns one (sequence, head) and 32 of the 128
-// state columns; columns are independent, so the four quarters of a state
-// run in four workgroups.  Thread (rr = tid / 8, cg = tid % 8) holds rows
-// rr + 32 i (i = 0..3) of columns 4 cg .. 4 cg + 3 as four float4 registers,
-// read once from the pool, kept across the call's tokens and written back in
-// place.  The path is bound by HBM: 64 KiB of fp32 state in and out per
-// (sequence, head), 32 KiB with a bf16 pool (widened on load, the tokens in
-// fp32, rounded to nearest even once on store).
+// One workgroup of 256 threads owns one (sequence, head) and 8 CPT of the 128
+// state columns, CPT = 4 with an fp32 pool and 8 with a bf16 one; columns are
+// independent, so a state runs in P = 128 / (8 CPT) workgroups.  Thread
+// (rr = tid / 8, cg = tid % 8) holds rows rr + 32 i (i = 0..3) of CPT
+// consecutive columns in registers, read once from the pool, kept across the
+// call's tokens and written back in place.  Workgroups are handed to the 8
+// XCDs in turn, so block b takes part (b / 8) % P of pair 8 (b / (8 P)) + b %
+// 8: the workgroups of a pair share one XCD and its L2, which serves the token
+// vectors they all read.  The path is bound by HBM: 64 KiB of fp32 state in
+// and out per (sequence, head), 32 KiB with a bf16 pool (widened on load, the
+// tokens in fp32, rounded to nearest even once on store).
 //
 // Speculative steps use the same kernel: a verify runs the T draft tokens
 // with the pool only read (write-back off), optionally storing the state after
@@ -37,7 +40,7 @@ namespace kda {
 namespace {
 
 constexpr int DK = 128;
-constexpr int QCOLS = 32;  // state columns per workgroup
+constexpr int QCOLS = 32;  // state columns per workgroup of the commit
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -55,20 +58,28 @@ __device__ __forceinline__ float4 bf16x4_to_f32(uint2 u) {
                      __uint_as_float(u.y & 0xffff0000u));
 }
 
+// CPT state columns per thread: 4 for an fp32 pool, 8 for a bf16 one (one
+// 16-byte load per row piece, half as many workgroups).  Measured on MI355X,
+// 1024 requests x 1 token x 12 heads, us per call, CPT 4 / 8: fp32 298 / 312,
+// bf16 200 / 161; 4 tokens bf16 445 / 410.
+template <int CPT>
 __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
+  constexpr int WC = 8 * CPT;      // state columns per workgroup
+  constexpr int PARTS = DK / WC;   // workgroups per (sequence, head)
   __shared__ float sk[DK], sq[DK], sd[DK];  // k, q and exp(g) of the token
-  __shared__ float sv[QCOLS];               // v of the token, this workgroup's columns
-  __shared__ float red[2][4][QCOLS];        // per-wave partial S^T k and S^T q
+  __shared__ float sv[WC];                  // v of the token, this workgroup's columns
+  __shared__ float red[2][4][WC];           // per-wave partial S^T k and S^T q
   __shared__ float sbeta;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cg = tid & 7, rr = tid >> 3;
   const int64_t blk = blockIdx.x;
-  const int quarter = (int)(blk & 3);
-  const int64_t pair = blk >> 2;
+  const int part = (int)((blk >> 3) % PARTS);
+  const int64_t pair = (blk / (8 * PARTS)) * 8 + (blk & 7);
   const int H = a.H;
+  if (pair >= (int64_t)a.N * H) return;
   const int n = (int)(pair / H), h = (int)(pair - (int64_t)n * H);
-  const int col = quarter * QCOLS + 4 * cg;
+  const int col = part * WC + CPT * cg;
   const int T = a.T;
   const int idx = a.state_indices[n];
   // tokens this request takes: all T, or its accepted prefix (none when the
@@ -83,7 +94,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
     // a request slot with no state: its outputs are zero, no state is touched
     if (rr == 0 && a.out)
       for (int t = 0; t < T; ++t)
-        *reinterpret_cast<uint2*>(a.out + (((int64_t)n * T + t) * H + h) * DK + col) = make_uint2(0u, 0u);
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4)
+          *reinterpret_cast<uint2*>(a.out + (((int64_t)n * T + t) * H + h) * DK + col + c) = make_uint2(0u, 0u);
     return;
   }
   if (Tn == 0) return;  // nothing accepted: the pool keeps its state
@@ -91,15 +104,25 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
   // element offset of this thread's first state element in the pool (fp32 or
   // bf16 elements)
   const int64_t se = ((int64_t)idx * H + h) * DK * DK + col;
-  float4 S[4];
+  float S[4][CPT];
   if (a.state_bf16) {
     const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.pool) + se;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[i] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(sp + (rr + 32 * i) * DK));
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        const float4 f = bf16x4_to_f32(*reinterpret_cast<const uint2*>(sp + (rr + 32 * i) * DK + c));
+        S[i][c] = f.x; S[i][c + 1] = f.y; S[i][c + 2] = f.z; S[i][c + 3] = f.w;
+      }
   } else {
     const float* sp = a.pool + se;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const float4*>(sp + (rr + 32 * i) * DK);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(sp + (rr + 32 * i) * DK + c);
+        S[i][c] = f.x; S[i][c + 1] = f.y; S[i][c + 2] = f.z; S[i][c + 3] = f.w;
+      }
   }
   // the state's four rows to `dst` at element offset e0: fp32, or bf16
   // rounded to nearest even
@@ -108,17 +131,24 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       uint16_t* p16 = reinterpret_cast<uint16_t*>(dst) + e0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint2*>(p16 + (rr + 32 * i) * DK) =
-            make_uint2(pack_bf16x2(S[i].x, S[i].y), pack_bf16x2(S[i].z, S[i].w));
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4)
+          *reinterpret_cast<uint2*>(p16 + (rr + 32 * i) * DK + c) =
+              make_uint2(pack_bf16x2(S[i][c], S[i][c + 1]), pack_bf16x2(S[i][c + 2], S[i][c + 3]));
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(dst + e0 + (rr + 32 * i) * DK) = S[i];
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4)
+          *reinterpret_cast<float4*>(dst + e0 + (rr + 32 * i) * DK + c) =
+              make_float4(S[i][c], S[i][c + 1], S[i][c + 2], S[i][c + 3]);
     }
   };
 
   // The per-token vectors are fetched one token ahead into registers (threads
-  // 0..127: k, q, g of row tid; 128..159: v of this workgroup's columns; 160:
-  // beta), so their latency overlaps the previous token's arithmetic.
+  // 0..127: k, q, g of row tid; the next WC: v of this workgroup's columns;
+  // then one for beta), so their latency overlaps the previous token's
+  // arithmetic.
   uint16_t nk = 0, nq = 0;
   float nx = 0.f;
   auto fetch = [&](int t) {
@@ -128,9 +158,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       nk = a.k[vbase + tid];
       nq = a.q[vbase + tid];
       nx = a.g[vbase + tid];
-    } else if (tid < DK + QCOLS) {
-      nk = a.v[vbase + quarter * QCOLS + tid - DK];
-    } else if (tid == DK + QCOLS) {
+    } else if (tid < DK + WC) {
+      nk = a.v[vbase + part * WC + tid - DK];
+    } else if (tid == DK + WC) {
       nx = a.beta[tok * H + h];
     }
   };
@@ -143,9 +173,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       sk[tid] = bf16_to_f32(nk);
       sq[tid] = bf16_to_f32(nq);
       sd[tid] = __expf(nx);
-    } else if (tid < DK + QCOLS) {
+    } else if (tid < DK + WC) {
       sv[tid - DK] = bf16_to_f32(nk);
-    } else if (tid == DK + QCOLS) {
+    } else if (tid == DK + WC) {
       sbeta = (a.prologue & 2) ? 1.f / (1.f + __expf(-nx)) : nx;  // beta given as a logit
     }
     lds_barrier();
@@ -172,27 +202,23 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       inv_q = qq > 0.f ? 1.f / __builtin_sqrtf(qq) : 0.f;
     }
     // decay the rows, then partial S^T k and S^T q over this thread's rows
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+    float pk[CPT], pq[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) pk[j] = pq[j] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rr + 32 * i;
       const float d = sd[r], kr = sk[r] * inv_k, qr = sq[r] * inv_q;
-      S[i].x *= d;
-      S[i].y *= d;
-      S[i].z *= d;
-      S[i].w *= d;
-      pk[0] += kr * S[i].x;
-      pk[1] += kr * S[i].y;
-      pk[2] += kr * S[i].z;
-      pk[3] += kr * S[i].w;
-      pq[0] += qr * S[i].x;
-      pq[1] += qr * S[i].y;
-      pq[2] += qr * S[i].z;
-      pq[3] += qr * S[i].w;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        S[i][j] *= d;
+        pk[j] += kr * S[i][j];
+        pq[j] += qr * S[i][j];
+      }
     }
     // sum over the 8 row positions of the wave (lanes cg, cg + 8, ..., cg + 56)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < CPT; ++j)
 #pragma unroll
       for (int o = 8; o < 64; o <<= 1) {
         pk[j] += __shfl_xor(pk[j], o, 64);
@@ -200,18 +226,18 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
       }
     if (lane < 8) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        red[0][w][4 * cg + j] = pk[j];
-        red[1][w][4 * cg + j] = pq[j];
+      for (int j = 0; j < CPT; ++j) {
+        red[0][w][CPT * cg + j] = pk[j];
+        red[1][w][CPT * cg + j] = pq[j];
       }
     }
     lds_barrier();
-    float u[4], o[4];
+    float u[CPT], o[CPT];
     const float beta = sbeta;
     kq *= inv_k * inv_q;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = 4 * cg + j;
+    for (int j = 0; j < CPT; ++j) {
+      const int c = CPT * cg + j;
       const float p = (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]);
       const float sqc = (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]);
       u[j] = beta * (sv[c] - p);
@@ -220,13 +246,14 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float kr = sk[rr + 32 * i] * inv_k;
-      S[i].x += kr * u[0];
-      S[i].y += kr * u[1];
-      S[i].z += kr * u[2];
-      S[i].w += kr * u[3];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) S[i][j] += kr * u[j];
     }
     if (rr == 0 && a.out)
-      *reinterpret_cast<uint2*>(a.out + vbase + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4)
+        *reinterpret_cast<uint2*>(a.out + vbase + col + c) =
+            make_uint2(pack_bf16x2(o[c], o[c + 1]), pack_bf16x2(o[c + 2], o[c + 3]));
     if (a.trace) store_state(a.trace, (tok * H + h) * DK * DK + col);
     lds_barrier();  // the staged vectors and partial sums are rewritten next token
   }
@@ -234,14 +261,16 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeArgs a) {
   if (a.writeback) store_state(a.pool, se);
 }
 
-// One workgroup per (request, head, quarter of the columns), the decode
-// kernel's thread layout: each thread copies rows rr + 32 i of its 4 columns.
+// One workgroup per (request, head, quarter of the columns), in the decode
+// kernel's block order with 4 parts per pair and its CPT = 4 thread layout:
+// each thread copies rows rr + 32 i of its 4 columns.
 __global__ __launch_bounds__(256) void kda_decode_commit_kernel(DecodeCommitArgs a) {
   const int tid = threadIdx.x, cg = tid & 7, rr = tid >> 3;
   const int64_t blk = blockIdx.x;
-  const int quarter = (int)(blk & 3);
-  const int64_t pair = blk >> 2;
+  const int quarter = (int)((blk >> 3) & 3);
+  const int64_t pair = (blk >> 5) * 8 + (blk & 7);
   const int H = a.H;
+  if (pair >= (int64_t)a.N * H) return;
   const int n = (int)(pair / H), h = (int)(pair - (int64_t)n * H);
   const int idx = a.state_indices[n], acc = a.accepted[n];
   if (idx < 0 || (int64_t)idx >= a.pool_size || acc < 1 || acc > a.T) return;
@@ -265,15 +294,21 @@ __global__ __launch_bounds__(256) void kda_decode_commit_kernel(DecodeCommitArgs
 
 }  // namespace
 
+// blocks for N x H pairs: whole groups of 8 pairs, `parts` workgroups each
+static int64_t decode_blocks(int64_t pairs, int parts) { return (pairs + 7) / 8 * 8 * parts; }
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.N * a.H * 4;
-  if (blocks == 0 || a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(kda_decode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  const int64_t pairs = (int64_t)a.N * a.H;
+  if (pairs == 0 || a.T == 0) return hipSuccess;
+  if (a.state_bf16)
+    hipLaunchKernelGGL(kda_decode_kernel<8>, dim3((unsigned)decode_blocks(pairs, 2)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(kda_decode_kernel<4>, dim3((unsigned)decode_blocks(pairs, 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_commit(const DecodeCommitArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.N * a.H * 4;
+  const int64_t blocks = decode_blocks((int64_t)a.N * a.H, 4);
   if (blocks == 0 || a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(kda_decode_commit_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
