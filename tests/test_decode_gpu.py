@@ -403,7 +403,9 @@ def test_decode_bf16_pool(N, T, H, P, empty):
             assert not np.any(gout[n * T:(n + 1) * T]), what
 
 
-def test_decode_bf16_pool_speculative():
+# the second shape is the bf16 verify bench size (1024 requests x 4 drafts)
+@pytest.mark.parametrize("N,T,H,P,empty", [(37, 3, 2, 40, 4), (1024, 4, 12, 1100, 16)])
+def test_decode_bf16_pool_speculative(N, T, H, P, empty):
     # the speculative paths on a bf16 pool (a bf16 trace): outputs and the
     # last traced state are kda_decode's bit for bit, a commit of every draft
     # leaves the pool as kda_decode does, and the advance equals the commit
@@ -411,8 +413,7 @@ def test_decode_bf16_pool_speculative():
     import kda_gated_delta_chunked_amd as K
     from kda_gated_delta_chunked_amd.synth import bf16_bits_from_f32, f32_from_bf16_bits
     dev = torch.device("cuda", 0)
-    N, T, H, P = 37, 3, 2, 40
-    p, pool, idx = _case(N, T, H, P, seed=230, empty=4)
+    p, pool, idx = _case(N, T, H, P, seed=230, empty=empty)
     pool_b = f32_from_bf16_bits(bf16_bits_from_f32(pool))
 
     def bf16(bits):
@@ -449,13 +450,16 @@ def test_decode_bf16_pool_speculative():
     assert torch.equal(cpool.view(torch.int16), dpool.view(torch.int16))
     assert torch.equal(apool.view(torch.int16), bpool.view(torch.int16))
     # and the advanced pool against the oracle's decode of each accepted prefix
+    # (every 16th request at the large size)
     gpool = bpool.float().cpu().numpy()
-    for n in named:
+    for n in (named if N <= 64 else named[::16]):
         a = int(acc_h[n])
         if a == 0:
             assert np.array_equal(gpool[idx[n]], pool_b[idx[n]]), n
             continue
         sl = slice(n * T, n * T + a)
+        # a one-entry pool holding this request's state
         ref = oracle.decode(p.q[sl], p.k[sl], p.v[sl], p.g[sl], p.beta[sl], scale=p.scale, num_seqs=1,
-                            tokens_per_seq=a, state_pool=pool_b, state_indices=idx[n:n + 1])
-        assert rel_l2(gpool[idx[n]], ref["pool"][idx[n]]) <= BF16_POOL_REL_L2, n
+                            tokens_per_seq=a, state_pool=pool_b[idx[n]:idx[n] + 1],
+                            state_indices=np.zeros(1, np.int32))
+        assert rel_l2(gpool[idx[n]], ref["pool"][0]) <= BF16_POOL_REL_L2, n
