@@ -372,7 +372,7 @@ constexpr int F_W31 = 15;       // exp(bt_2)
 constexpr int F_W30 = 16;       // exp(bt_1 + bt_2)
 constexpr int F_ROWS = 17;
 // k exp(bt_j - Gl_s) of row blocks 0..2 (fp32 [block][row][channel]); after
-// the gated products the same space holds T (pitch P_LP) and solve scratch
+// the gated products the same space holds T (pitch P_LP)
 constexpr int P_E_FLOATS = CH * P_LP + 4 * 512;
 // during steps 2-3 the same space holds k exp(bt_j - Gl_s) as bf16 (12 KiB)
 // and, after it, the K^^T half fragments that waves hand to their partner
@@ -380,12 +380,6 @@ constexpr int P_E_FLOATS = CH * P_LP + 4 * 512;
 constexpr int P_EP = DK + 8;    // bf16 pitch of those rows (16-byte shift per row: fewer bank conflicts)
 constexpr int P_X_BYTES = 3 * 16 * P_EP * 2;
 static_assert(P_E_FLOATS * 4 >= P_X_BYTES + 4 * 4 * 512, "prepare LDS layout");
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // the 8 channels of key block b of this lane: 8 consecutive at p + off
 __device__ __forceinline__ void load8_f32(const float* p, float (&x)[8], int off) {
@@ -810,49 +804,53 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   // quarter of the block inverse, -T_hh L_hl T_ll with hh = rows 32..63 and
   // ll = columns 0..31: wave w writes block (2 + w / 2, w % 2) as
   //   T_ij = -sum_{p=2}^{i} T_ip Z_pj,   Z_pj = sum_{m=j}^{1} L_pm T_mj.
-  const int rr = lane >> 2, c4 = 4 * (lane & 3);
-  float* sZ = sE + CH * P_LP + 512 * w;
-  // Z = sum_{m=m0}^{m1-1} L[pb, m] T[m, jb] for this lane's row rr and columns c4..c4+3
-  auto lt_prod = [&](int pb, int m0, int m1, int jb) {
-    float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int m = m0; m < m1; ++m) {
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const float lv = sL[(16 * pb + rr) * P_LP + 16 * m + kk];
-        const float4 tv = *reinterpret_cast<const float4*>(&sT[(16 * m + kk) * P_LP + 16 * jb + c4]);
-        z.x += lv * tv.x; z.y += lv * tv.y; z.z += lv * tv.z; z.w += lv * tv.w;
-      }
-    }
-    return z;
+  // Each 16 x 16 x 16 block product is four fp32 matrix-core steps
+  // (v_mfma_f32_16x16x4_f32, fp32 products and sums).  Step e takes the
+  // contraction index 4 g + e from lane group g, which is the row an fp32
+  // accumulator holds in its element e (lane 16 g + q: rows 4 g .. 4 g + 3 of
+  // column q): a product's accumulator is then the right operand of the next
+  // as it stands, and Z never goes through LDS.
+  auto mf4 = [](float x, float y, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0); };
+  // acc += A[block ab, kb] B[block kb, jb], both 16 x 16 blocks of pitch P_LP in LDS
+  auto mm_lds = [&](const float* A, int ab, int kb, const float* B, int jb, f32x4 acc) {
+    const float4 av = *reinterpret_cast<const float4*>(&A[(16 * ab + q) * P_LP + 16 * kb + 4 * g4]);
+    const float* bp = &B[(16 * kb + 4 * g4) * P_LP + 16 * jb + q];
+    acc = mf4(av.x, bp[0], acc);
+    acc = mf4(av.y, bp[P_LP], acc);
+    acc = mf4(av.z, bp[2 * P_LP], acc);
+    acc = mf4(av.w, bp[3 * P_LP], acc);
+    return acc;
   };
-  // sum_{p=p0}^{p1} T[ib, p] Zs[p - p0], Zs in this wave's scratch
-  auto tz_prod = [&](int ib, int p0, int p1) {
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int pb = p0; pb <= p1; ++pb) {
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const float tv = sT[(16 * ib + rr) * P_LP + 16 * pb + kk];
-        const float4 zv = *reinterpret_cast<const float4*>(&sZ[(pb - p0) * 256 + kk * 16 + c4]);
-        o.x += tv * zv.x; o.y += tv * zv.y; o.z += tv * zv.z; o.w += tv * zv.w;
-      }
-    }
-    return o;
+  // acc += A[block ab, kb] Z, Z an accumulator
+  auto mm_acc = [&](const float* A, int ab, int kb, const f32x4& Z, f32x4 acc) {
+    const float4 av = *reinterpret_cast<const float4*>(&A[(16 * ab + q) * P_LP + 16 * kb + 4 * g4]);
+    acc = mf4(av.x, Z[0], acc);
+    acc = mf4(av.y, Z[1], acc);
+    acc = mf4(av.z, Z[2], acc);
+    acc = mf4(av.w, Z[3], acc);
+    return acc;
   };
+  // -O into block (ib, jb) of T
+  auto store_neg = [&](int ib, int jb, const f32x4& o) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(16 * ib + 4 * g4 + e) * P_LP + 16 * jb + q] = -o[e];
+  };
+  const f32x4 z4t = {0.f, 0.f, 0.f, 0.f};
   if (w < 2) {
     const int ib = 2 * w + 1, jb = 2 * w;
-    *reinterpret_cast<float4*>(&sZ[rr * 16 + c4]) = lt_prod(ib, jb, ib, jb);
-    wave_sync();
-    const float4 o = tz_prod(ib, ib, ib);
-    *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o.x, -o.y, -o.z, -o.w);
+    const f32x4 z = mm_lds(sL, ib, jb, sT, jb, z4t);
+    store_neg(ib, jb, mm_acc(sT, ib, ib, z, z4t));
   }
   lds_barrier();
   {
     const int ib = 2 + (w >> 1), jb = w & 1;
-    for (int pb = 2; pb <= ib; ++pb)
-      *reinterpret_cast<float4*>(&sZ[(pb - 2) * 256 + rr * 16 + c4]) = lt_prod(pb, jb, 2, jb);
-    wave_sync();
-    const float4 o = tz_prod(ib, 2, ib);
-    *reinterpret_cast<float4*>(&sT[(16 * ib + rr) * P_LP + 16 * jb + c4]) = make_float4(-o.x, -o.y, -o.z, -o.w);
+    f32x4 o = z4t;
+    for (int pb = 2; pb <= ib; ++pb) {
+      f32x4 z = z4t;
+      for (int m = jb; m < 2; ++m) z = mm_lds(sL, pb, m, sT, jb, z);
+      o = mm_acc(sT, ib, pb, z, o);
+    }
+    store_neg(ib, jb, o);
   }
   lds_barrier();
 
