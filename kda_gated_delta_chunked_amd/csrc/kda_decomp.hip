@@ -554,7 +554,10 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     inv_k = ssk > 0.f ? 1.f / __builtin_sqrtf(ssk) : 0.f;
     inv_q = ssq > 0.f ? 1.f / __builtin_sqrtf(ssq) : 0.f;
   }
-  const float qmul = inv_q;   // the read-out scale is applied by the recurrence
+  // per-row factors of k and q: the prologue's norms, and 0 on rows before
+  // the segment (one factor per row instead of a select per channel); the
+  // read-out scale is applied by the recurrence
+  const float kmul = rv ? inv_k : 0.f, qmul = rv ? inv_q : 0.f;
   lds_barrier();
 
   // (1) per-channel block factors; Gam and beta go straight to the slot
@@ -626,8 +629,8 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     unpack8(qA[b], qf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kf[e] = rv ? kf[e] * inv_k : 0.f;
-      qf[e] = rv ? qf[e] * qmul : 0.f;  // Q~ and M carry the read-out scale
+      kf[e] *= kmul;
+      qf[e] *= qmul;
     }
     load8_f32(sF, bt, (F_BT + i) * DK + ch0);
     float Kf[8], Qf[8], kb[8];
@@ -779,23 +782,29 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     else
       ws_store<NT>(slot + SL_M + tri_off(f) + lane * 16, mv);
   }
-  lds_barrier();
-
-  // (4) T_bb = (I + L_bb)^-1 by forward substitution, lane = (block, column)
+  // (4) T_bb = (I + L_bb)^-1 by forward substitution, lane = (block, column).
+  // Wave 0, which has no block in step (3), solves them while the other waves
+  // run it: the solve reads only the diagonal blocks of L, which step (3)
+  // does not write.  The result waits in registers until the barrier, since
+  // T's space still holds the operands step (3) reads.
   float* sT = sE;
+  float tdg[16];
   if (w == 0) {
     const int bb = lane >> 4, col = lane & 15;
-    float x[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       float acc = rr == col ? 1.f : 0.f;
       const float* lrow = &sL[(16 * bb + rr) * P_LP + 16 * bb];
 #pragma unroll
-      for (int ss = 0; ss < rr; ++ss) acc -= lrow[ss] * x[ss];
-      x[rr] = acc;
+      for (int ss = 0; ss < rr; ++ss) acc -= lrow[ss] * tdg[ss];
+      tdg[rr] = acc;
     }
+  }
+  lds_barrier();
+  if (w == 0) {
+    const int bb = lane >> 4, col = lane & 15;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sT[(16 * bb + rr) * P_LP + 16 * bb + col] = x[rr];
+    for (int rr = 0; rr < 16; ++rr) sT[(16 * bb + rr) * P_LP + 16 * bb + col] = tdg[rr];
   }
   lds_barrier();
 
