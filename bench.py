@@ -44,6 +44,7 @@ KERNEL_SOURCES = {"fused": os.path.join(CSRC, "kda_fused.hip"), "decomp": os.pat
                   "decode": os.path.join(CSRC, "kda_decode.hip")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 MFMA_FLOPS = 16 * 16 * 32 * 2    # one v_mfma_f32_16x16x32_f16 or _bf16
+MFMA_F32_FLOPS = 16 * 16 * 4 * 2  # one v_mfma_f32_16x16x4_f32
 
 
 def stage_bytes(p):
@@ -94,7 +95,7 @@ def segments(p) -> int:
 
 
 def modelled_mfma_flops(p, variant: str, vsplit: int) -> float:
-    """Flops of the 16x16x32 MFMA instructions the kernels issue (hi/lo passes
+    """Flops of the MFMA instructions the kernels issue (hi/lo passes
     included), counted from their schedules (a model: the committed rocprofv3
     SQ counters give the measured figure).  Per segment and head:
     * FUSED, per workgroup: 156 for the gate products (4 diagonal blocks x 4
@@ -103,11 +104,13 @@ def modelled_mfma_flops(p, variant: str, vsplit: int) -> float:
     * DECOMP: the prepare's 176 (4 diagonal blocks x 4 x 6, 6 off-diagonal
       x 4 x 2, 32 transposes of K^) and the recurrence's 76 per 16 columns,
       8 column tiles per (sequence, head).  The recurrence's 76: K~ S 16,
-      Q~ S 16, N Y 6, M U 6, K^^T U with U hi + lo 32."""
+      Q~ S 16, N Y 6, M U 6, K^^T U with U hi + lo 32.  The prepare also
+      issues 76 fp32 16x16x4 products (2,048 flops each) for the block
+      inverse of T: 16 for its 32 x 32 halves, 60 for the lower-left quarter."""
     segs = segments(p)
     if variant == "fused":
         return float((156 + 76 * (128 // vsplit // 16)) * MFMA_FLOPS) * segs * p.H * vsplit
-    return float((176 + 8 * 76) * MFMA_FLOPS) * segs * p.H
+    return (float((176 + 8 * 76) * MFMA_FLOPS) + 76.0 * MFMA_F32_FLOPS) * segs * p.H
 
 
 # headers every kernel source includes: a change there changes the kernel too
