@@ -367,10 +367,10 @@ constexpr int F_BT = 0;         // bt_0..3 (block sums of g)
 constexpr int F_P = 4;          // P_1..3 = exp(bt_0 + ... + bt_{i-1})  (row F_P + i - 1)
 constexpr int F_R = 7;          // R_0..2 = exp(bt_{i+1} + ... + bt_3)  (row F_R + i)
 constexpr int F_IBD = 10;       // exp(-bt_i)
-constexpr int F_W20 = 14;       // exp(bt_1)
-constexpr int F_W31 = 15;       // exp(bt_2)
-constexpr int F_W30 = 16;       // exp(bt_1 + bt_2)
-constexpr int F_ROWS = 17;
+constexpr int F_ROWS = 14;
+// the off-diagonal blocks' factors W, as fp16 rows (sW): exp(bt_1) for
+// block (2, 0), exp(bt_2) for (3, 1), exp(bt_1 + bt_2) for (3, 0)
+constexpr int W_ROWS = 3;
 // k exp(bt_j - Gl_s) of row blocks 0..2 (fp32 [block][row][channel]); after
 // the gated products the same space holds T (pitch P_LP)
 constexpr int P_E_FLOATS = CH * P_LP + 4 * 512;
@@ -395,11 +395,6 @@ __device__ __forceinline__ void store8_f32(float* p, const float (&x)[8], int of
 __device__ __forceinline__ void unpack8(const uint2 (&u)[2], float (&x)[8]) {
   x[0] = lo_of(u[0].x); x[1] = hi_of(u[0].x); x[2] = lo_of(u[0].y); x[3] = hi_of(u[0].y);
   x[4] = lo_of(u[1].x); x[5] = hi_of(u[1].x); x[6] = lo_of(u[1].y); x[7] = hi_of(u[1].y);
-}
-// eight fp16 (two uint2) -> floats
-__device__ __forceinline__ void unpack8h(const uint2 (&u)[2], float (&x)[8]) {
-  x[0] = h_lo(u[0].x); x[1] = h_hi(u[0].x); x[2] = h_lo(u[0].y); x[3] = h_hi(u[0].y);
-  x[4] = h_lo(u[1].x); x[5] = h_hi(u[1].x); x[6] = h_lo(u[1].y); x[7] = h_hi(u[1].y);
 }
 // value of lane q - n of this 16-lane row (0 for q < n)
 template <int N>
@@ -441,6 +436,7 @@ __device__ __forceinline__ int rescale_exponent(float big, int s) {
 template <bool NT>
 __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   __shared__ __attribute__((aligned(16))) float sF[F_ROWS * DK];
+  __shared__ __attribute__((aligned(16))) _Float16 sW[W_ROWS * DK];
   __shared__ __attribute__((aligned(16))) float sE[P_E_FLOATS];
   __shared__ __attribute__((aligned(16))) float sL[CH * P_LP];        // beta_r A[r,s]
   __shared__ __attribute__((aligned(16))) float sB[CH];
@@ -575,9 +571,9 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     sF[(F_IBD + 1) * DK + d] = __expf(-b1);
     sF[(F_IBD + 2) * DK + d] = __expf(-b2);
     sF[(F_IBD + 3) * DK + d] = __expf(-b3);
-    sF[F_W20 * DK + d] = __expf(b1);
-    sF[F_W31 * DK + d] = __expf(b2);
-    sF[F_W30 * DK + d] = __expf(b1 + b2);
+    sW[0 * DK + d] = (_Float16)__expf(b1);
+    sW[1 * DK + d] = (_Float16)__expf(b2);
+    sW[2 * DK + d] = (_Float16)__expf(b1 + b2);
     // Gam in the state's row order
     const int sd = state_row_channel(d);
     ws_store<NT>(slot + SL_GAM + 4 * d,
@@ -747,21 +743,14 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     if (jb >= i) continue;
     f32x4 aacc = {0.f, 0.f, 0.f, 0.f};
     f32x4 m1 = {0.f, 0.f, 0.f, 0.f};
-    const int wrow = (jb == i - 1) ? -1 : (i == 2 ? F_W20 : (jb == 1 ? F_W31 : F_W30));
+    // W's fp16 row (none for the block next to the diagonal); the scaled
+    // operand is rounded once more, by the packed fp16 products
+    const int wsel = (jb == i - 1) ? -1 : (i == 2 ? 0 : (jb == 1 ? 1 : 2));
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int ch0 = 32 * b + 8 * g4;
       f16x8 bb = *reinterpret_cast<const f16x8*>(sEb + (jb * 16 + q) * P_EP + ch0);
-      if (wrow >= 0) {
-        const uint4 kv = __builtin_bit_cast(uint4, bb);
-        const uint2 kv2[2] = {make_uint2(kv.x, kv.y), make_uint2(kv.z, kv.w)};
-        float ks[8], wf[8];
-        unpack8h(kv2, ks);
-        load8_f32(sF, wf, wrow * DK + ch0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ks[e] *= wf[e];
-        bb = to_f16x8(ks);
-      }
+      if (wsel >= 0) bb = bb * *reinterpret_cast<const f16x8*>(&sW[wsel * DK + ch0]);
       aacc = mfma(bb, aK[b], aacc);
       m1 = mfma(bb, aQ[b], m1);
     }
