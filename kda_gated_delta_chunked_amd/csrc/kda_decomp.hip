@@ -488,8 +488,18 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
   // load under a per-lane condition makes the compiler wait before the join).
   const bool rv = r >= off;
   const size_t erow = ((size_t)(tok0 + max(r, off)) * H + h) * DK;
+  // g and beta first: the gate cumsum and the block factors need only them,
+  // and run while k and q are still arriving (loads complete in order)
   uint2 kA[4][2], qA[4][2];
   float4 gA[4][2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int ch = 32 * b + 8 * g4;
+    gA[b][0] = *reinterpret_cast<const float4*>(a.g + erow + ch);
+    gA[b][1] = *reinterpret_cast<const float4*>(a.g + erow + ch + 4);
+  }
+  const float beta_ld = a.beta[(size_t)(tok0 + max(tid & (CH - 1), off)) * H + h];
+  __builtin_amdgcn_sched_barrier(0);  // keep the k and q loads behind these
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int ch = 32 * b + 8 * g4;
@@ -499,10 +509,7 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     kA[b][1] = make_uint2(kv.z, kv.w);
     qA[b][0] = make_uint2(qv.x, qv.y);
     qA[b][1] = make_uint2(qv.z, qv.w);
-    gA[b][0] = *reinterpret_cast<const float4*>(a.g + erow + ch);
-    gA[b][1] = *reinterpret_cast<const float4*>(a.g + erow + ch + 4);
   }
-  const float beta_ld = a.beta[(size_t)(tok0 + max(tid & (CH - 1), off)) * H + h];
 
   // Gl: cumulative sum of g over the rows of the block, for this lane's 32
   // channels -- an inclusive scan over the 16 lanes of a DPP row (lane q = row q)
@@ -534,9 +541,14 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+      // opaque copies: this unpacking stays inside the branch rather than
+      // being shared with step (2)'s, which would make every wave wait for
+      // its k and q before the first barrier, prologue or not
+      uint2 kk[2] = {kA[b][0], kA[b][1]}, qq[2] = {qA[b][0], qA[b][1]};
+      asm volatile("" : "+v"(kk[0]), "+v"(kk[1]), "+v"(qq[0]), "+v"(qq[1]));
       float kf[8], qf[8];
-      unpack8(kA[b], kf);
-      unpack8(qA[b], qf);
+      unpack8(kk, kf);
+      unpack8(qq, qf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ssk += kf[e] * kf[e];
@@ -593,6 +605,9 @@ __global__ __launch_bounds__(256, 3) void kda_prepare_kernel(DecompArgs a) {
     *reinterpret_cast<unsigned long long*>(slot + SL_HDR + 16) = mask;
   }
   lds_barrier();
+  // nothing of step (2) (the unpacking of k and q) moves above the barrier:
+  // there it would wait for k and q
+  __builtin_amdgcn_sched_barrier(0);
 
   // (2) wave i: operands of row block i and the diagonal block (i, i).
   // Identity slices that transpose a K^ tile with one exact matrix product:
