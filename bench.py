@@ -492,8 +492,11 @@ def main() -> int:
     kernels = {}
     if variant == "decomp":
         for st, kname in (("prepare", "kda_prepare_kernel"), ("recurrence", "kda_recurrence_kernel")):
+            # the call's own value split when none is given: with a chain
+            # split the library may run its first launch with fewer
+            # workgroups per pair than the plan reports
             sprob = K.make_problem(p.N, p.T_total, p.H, scale=p.scale, variant="decomp",
-                                   value_split=vsplit, stages=st, chain_parts=pieces)
+                                   value_split=args.value_split, stages=st, chain_parts=pieces)
 
             def one(sprob=sprob):
                 rc = K.prefill_raw(sprob, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), ptr(s0),

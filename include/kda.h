@@ -354,7 +354,10 @@ const char* kda_status_string(int status);
  * table of measured rows keyed on the compute-unit count, not on the device's
  * name (FlashInfer PR #4633, Description: neither the two-launch nor the
  * one-launch kernel is faster everywhere, so a table keyed on SM count picks
- * per call, and a query reports the choice). */
+ * per call, and a query reports the choice).  value_split is the count of the
+ * unsplit recurrence and of the chain split's second launch; with value_split
+ * 0 in the problem, the split's first launch (twice the workgroups) may run
+ * with fewer per (sequence, head), from the same cost table. */
 kda_status kda_plan(const kda_problem* p, int32_t* variant, int32_t* value_split,
                     int32_t* chain_parts);
 

@@ -179,44 +179,71 @@ int64_t rounds(int64_t groups, int per_group, int cus) {
   return (per_xcd + slots - 1) / slots;
 }
 
-double split_cost(int64_t pairs, int64_t chunks, int vsplit, int P, int cus) {
+double split_cost(int64_t pairs, int64_t chunks, int vsplit_first, int vsplit, int P, int cus) {
   const int64_t groups = pairs * (P - 1), L = (chunks + P - 1) / P;
-  return seg_cost(vsplit) * (double)L * (double)(rounds(groups, 2 * vsplit, cus) + rounds(groups, vsplit, cus)) +
+  return (double)L * (seg_cost(vsplit_first) * (double)rounds(groups, 2 * vsplit_first, cus) +
+                      seg_cost(vsplit) * (double)rounds(groups, vsplit, cus)) +
          kScanStepCost * (P - 2) + kSplitCost;
 }
 
 // Chain pieces (and the workgroups per pair they run with) for the two-launch
-// schedule: chain_parts when given; else (AUTO) the split, up to chain_cap
-// pieces, whose modelled cost is below 0.9 of the unsplit run's -- over
+// schedule: chain_parts when given, else the cheapest P by the model above --
 // vsplit 1, 2 and 4 when value_split is automatic -- and whose chain area the
-// workspace holds.  Fewer than 3 pieces run nothing side by side.
-int chain_pieces(const kda_problem* p, int cus, size_t ws_bytes, int32_t* vsplit) {
-  if (p->chain_parts) return p->chain_parts;
-  const int cap = chain_cap(p);
-  if (cap < 3 || cus < 8) return 1;
+// workspace holds (none when no device is known).  The first split launch
+// holds twice the workgroups of the second, so with value_split automatic it
+// takes its own count (vsplit_first): at B1 T8192 H12, 11 pieces, one
+// workgroup per pair and role fits the first launch in one round where two
+// need two.
+struct FirstPass {
+  int vsplit;
+  double cost;
+};
+
+int chain_pieces(const kda_problem* p, int cus, size_t ws_bytes, int32_t* vsplit, int32_t* vsplit_first) {
+  *vsplit_first = *vsplit;
+  if (cus < 8) return p->chain_parts ? p->chain_parts : 1;
   const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
   const int64_t chunks = (p->total_tokens / p->num_seqs + 63) / 64;
+  auto first_pass = [&](int P, int vs) {
+    FirstPass f{vs, split_cost(pairs, chunks, vs, vs, P, cus)};
+    if (!p->value_split)
+      for (int v1 : {1, 2, 4}) {
+        const double c = split_cost(pairs, chunks, v1, vs, P, cus);
+        if (c < f.cost) f = FirstPass{v1, c};
+      }
+    return f;
+  };
+  if (p->chain_parts) {
+    if (p->chain_parts >= 2) *vsplit_first = first_pass(p->chain_parts, *vsplit).vsplit;
+    return p->chain_parts;
+  }
+  const int cap = chain_cap(p);
+  if (cap < 3) return 1;
   const double unsplit = seg_cost(*vsplit) * (double)chunks * (double)rounds(pairs, *vsplit, cus);
   double best = 0.9 * unsplit;
-  int best_p = 1, best_vs = *vsplit;
+  int best_p = 1, best_vs = *vsplit, best_first = *vsplit;
   for (int vs : {2, 1, 4}) {
     if (p->value_split && vs != p->value_split) continue;
     for (int P = 3; P <= cap; ++P) {
-      const double c = split_cost(pairs, chunks, vs, P, cus);
-      if (c < best && ws_bytes >= decomp_bytes(p, P)) {
-        best = c;
+      if (ws_bytes < decomp_bytes(p, P)) continue;
+      const FirstPass f = first_pass(P, vs);
+      if (f.cost < best) {
+        best = f.cost;
         best_p = P;
         best_vs = vs;
+        best_first = f.vsplit;
       }
     }
   }
   *vsplit = best_vs;
+  *vsplit_first = best_first;
   return best_p;
 }
 
 void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, int32_t* vsplit,
-            int32_t* pieces) {
+            int32_t* pieces, int32_t* vsplit_first = nullptr) {
   int32_t var = p->variant;
+  int32_t first = 0;
   *pieces = 1;
   if (var == KDA_VARIANT_AUTO) {
     // value_split 1 and 8 and a chain split exist only in DECOMP
@@ -242,7 +269,9 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
     const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
     *vsplit = (cus > 0 && pairs * 4 <= cus && decomp_bytes(p, 1) > kDecompCacheBytes) ? 4 : 2;
   }
-  if (var == KDA_VARIANT_DECOMP) *pieces = chain_pieces(p, cus, ws_bytes, vsplit);
+  first = *vsplit;
+  if (var == KDA_VARIANT_DECOMP) *pieces = chain_pieces(p, cus, ws_bytes, vsplit, &first);
+  if (vsplit_first) *vsplit_first = first;
 }
 
 // ---------------------------------------------------------------------------
@@ -469,8 +498,8 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
                                      final_state, ckpt_offsets, ckpt_state, workspace,
                                      workspace_bytes);
   if (st != KDA_OK) return st;
-  int32_t variant = 0, vsplit = 0, pieces = 1;
-  choose(p, device_cu_count(), workspace ? workspace_bytes : 0, &variant, &vsplit, &pieces);
+  int32_t variant = 0, vsplit = 0, pieces = 1, vsplit_first = 0;
+  choose(p, device_cu_count(), workspace ? workspace_bytes : 0, &variant, &vsplit, &pieces, &vsplit_first);
   const hipStream_t st_ = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (variant == KDA_VARIANT_DECOMP) {
@@ -523,7 +552,7 @@ kda_status kda_prefill(const kda_problem* p, const uint16_t* q, const uint16_t* 
     // (B1 T512 0.034 / 0.035: the prepare alike, the recurrence slower)
     a.prep_xcd = stream_ws;
     const int stages = p->stages ? p->stages : (KDA_STAGE_PREPARE | KDA_STAGE_RECURRENCE);
-    err = kda::launch_decomp(a, vsplit, prepare_slots, stages, stream_ws, st_);
+    err = kda::launch_decomp(a, vsplit, vsplit_first, prepare_slots, stages, stream_ws, st_);
   } else {
     kda::FusedArgs a;
     a.q = q;

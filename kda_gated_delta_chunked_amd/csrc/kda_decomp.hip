@@ -1611,19 +1611,41 @@ template <int CW, int KW>
 hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
   constexpr int VG = 8 / CW;
   const int64_t pairs = (int64_t)a.N * a.H;
-  if (a.pieces < 2) {
-    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * VG));
-    hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, false>), grid, dim3(64 * (CW + KW)), 0, stream, a);
-    return hipGetLastError();
+  const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * VG));
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, false>), grid, dim3(64 * (CW + KW)), 0, stream, a);
+  return hipGetLastError();
+}
+
+// one launch of the chain split: groups of (pair, piece), `roles` runs of VG
+// workgroups each per group (the first launch: ZERO's and EYE's)
+template <int CW, int KW>
+hipError_t launch_split_pass(const DecompArgs& b, int64_t groups, int roles, hipStream_t stream) {
+  constexpr int VG = 8 / CW;
+  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, true>), dim3((unsigned)(((groups + 7) / 8) * 8 * roles * VG)),
+                     dim3(64 * (CW + KW)), 0, stream, b);
+  return hipGetLastError();
+}
+
+hipError_t split_pass(int vsplit, const DecompArgs& b, int64_t groups, int roles, hipStream_t stream) {
+  switch (vsplit) {
+    case 1: return launch_split_pass<8, 4>(b, groups, roles, stream);
+    case 2: return launch_split_pass<4, 4>(b, groups, roles, stream);
+    case 4: return launch_split_pass<2, 2>(b, groups, roles, stream);
+    case 8: return launch_split_pass<1, 1>(b, groups, roles, stream);
+    default: return hipErrorInvalidValue;
   }
-  // the split: groups of (pair, piece), P - 1 per pair in each launch; a
-  // group of the first launch holds ZERO's and EYE's workgroups
+}
+
+// the chain split: P - 1 groups of (pair, piece) per pair in each launch; a
+// group of the first launch holds ZERO's and EYE's workgroups (piece 0's
+// MAIN takes ZERO's place).  The two launches may run with different
+// workgroups per pair: the first holds twice the workgroups of the second.
+hipError_t launch_split(const DecompArgs& a, int vsplit_first, int vsplit, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.N * a.H;
   const int64_t groups = pairs * (a.pieces - 1);
   DecompArgs b = a;
   b.pass = 1;
-  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, true>), dim3((unsigned)(((groups + 7) / 8) * 8 * 2 * VG)),
-                     dim3(64 * (CW + KW)), 0, stream, b);
-  hipError_t err = hipGetLastError();
+  hipError_t err = split_pass(vsplit_first, b, groups, 2, stream);
   if (err != hipSuccess) return err;
   if (a.pieces > 2) {
     hipLaunchKernelGGL(kda_chain_scan_kernel, dim3((unsigned)(((pairs + 7) / 8) * 8 * (DK / kScanCols))),
@@ -1631,14 +1653,12 @@ hipError_t launch_recurrence(const DecompArgs& a, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   b.pass = 2;
-  hipLaunchKernelGGL((kda_recurrence_kernel<CW, KW, true>), dim3((unsigned)(((groups + 7) / 8) * 8 * VG)),
-                     dim3(64 * (CW + KW)), 0, stream, b);
-  return hipGetLastError();
+  return split_pass(vsplit, b, groups, 1, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
+hipError_t launch_decomp(const DecompArgs& a, int vsplit, int vsplit_first, int64_t prepare_slots, int stages,
                          bool stream_ws, hipStream_t stream) {
   hipError_t err;
   if (stages & 1) {
@@ -1656,6 +1676,7 @@ hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots,
     }
   }
   if (!(stages & 2)) return hipSuccess;
+  if (a.pieces >= 2) return launch_split(a, vsplit_first, vsplit, stream);
   switch (vsplit) {
     case 1: return launch_recurrence<8, 4>(a, stream);
     case 2: return launch_recurrence<4, 4>(a, stream);

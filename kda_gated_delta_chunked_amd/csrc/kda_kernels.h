@@ -124,8 +124,9 @@ inline void decomp_workspace_layout(int64_t N, int64_t T_total, int64_t H, int64
 // stream_ws: the prepare writes the workspace with non-temporal stores (for a
 // workspace that does not stay in the Infinity Cache until the recurrence).
 // With a.pieces >= 2 the recurrence runs as the chain split's two launches
-// with the scan of the piece transitions between them.
-hipError_t launch_decomp(const DecompArgs& a, int vsplit, int64_t prepare_slots, int stages,
+// with the scan of the piece transitions between them; the first of them
+// with vsplit_first workgroups per pair and role, the second with vsplit.
+hipError_t launch_decomp(const DecompArgs& a, int vsplit, int vsplit_first, int64_t prepare_slots, int stages,
                          bool stream_ws, hipStream_t stream);
 
 // State-pool decode: N requests advance by T tokens each from the pool
