@@ -265,7 +265,9 @@ void choose(const kda_problem* p, int cus, size_t ws_bytes, int32_t* variant, in
     // does not, four are, when they all fit at once (B2 T8192 0.335 / 0.307,
     // B1 T32768 1.070 / 0.984, B5 T8192 0.465 / 0.432, B1 T8192 H64 0.462 /
     // 0.436).  Past the CU count two (B8 T8192 0.614 / 0.751); one and eight
-    // are slower everywhere.
+    // are slower everywhere, also where the pairs outnumber the CUs (two /
+    // one: packed 32 ragged 0.553 / 0.562, 16 ragged + checkpoints 0.661 /
+    // 0.707, B32 T512 0.158 / 0.158).
     const int64_t pairs = (int64_t)p->num_seqs * p->num_heads;
     *vsplit = (cus > 0 && pairs * 4 <= cus && decomp_bytes(p, 1) > kDecompCacheBytes) ? 4 : 2;
   }
