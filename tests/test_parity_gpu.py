@@ -196,6 +196,27 @@ def test_chain_split_full_length(pieces, vsplit):
     _report(f"chain P{pieces} vs{vsplit} B1 T8192", assert_parity(gpu, ref, f"chain P{pieces}", p.cu_seqlens))
 
 
+def test_chain_split_first_launch_workgroups_bitwise():
+    # with the value split automatic the chain split's first launch takes its
+    # own workgroups per pair (at B1 T8192 H12 on 256 CUs: one of eight
+    # compute waves per pair and role, where the second launch runs two of
+    # four).  Every compute wave owns the same 16 state columns and runs the
+    # same products in the same order either way, so the results are those of
+    # the split with the second launch's count in both launches, bit for bit;
+    # and they meet the gates against the oracle
+    import kda_gated_delta_chunked_amd as K
+    p = synth.workload("b1_t8192")
+    variant, vsplit, pieces = K.plan(K.make_problem(p.N, p.T_total, p.H, scale=p.scale))
+    if variant != "decomp" or pieces < 3:
+        pytest.skip(f"no chain split on this device: {variant, vsplit, pieces}")
+    d = to_device(p)
+    auto = run_gpu(p, variant="auto", d=d)
+    same = run_gpu(p, variant="decomp", value_split=vsplit, chain_parts=pieces, d=d)
+    assert np.array_equal(auto["out"], same["out"]) and np.array_equal(auto["final"], same["final"])
+    ref = oracle.prefill_problem(p)
+    _report(f"b1_t8192 auto split P{pieces}", assert_parity(auto, ref, "b1_t8192 auto split", p.cu_seqlens))
+
+
 @pytest.mark.parametrize("kind", ["zero", "weak", "skew"])
 def test_chain_split_slow_decay(kind):
     # at slow decay a piece's transition is far from zero, so the scan carries
