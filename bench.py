@@ -525,7 +525,13 @@ def main() -> int:
     path = {"ms_per_call": round(ms_launch, 4), "algorithmic_bytes": alg_b,
             "achieved_GBps": round(alg_b / (ms_launch * 1e-3) / 1e9, 1),
             "frac_hbm": round(alg_b / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "kernels_ms": {kk: round(e["ms"], 4) for kk, e in kernels.items()}}
+            "kernels_ms": {kk: round(e["ms"], 4) for kk, e in kernels.items()},
+            # every launch's algorithmic rate against the HBM peak, not only
+            # the dominant one's (at B8 T8192 the two launches take about the
+            # same time, so which one is dominant can change with a change to
+            # either)
+            "kernels_frac_hbm": {kk: round(e["algorithmic_bytes"] / (e["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                 for kk, e in kernels.items()}}
     ex_fl = modelled_mfma_flops(p, variant, vsplit)
     alg_fl = algorithmic_flops(p)
     mfma = {"modelled_executed_tflops": round(ex_fl / (ms_launch * 1e-3) / 1e12, 1),
