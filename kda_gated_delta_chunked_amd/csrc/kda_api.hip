@@ -187,9 +187,11 @@ double split_cost(int64_t pairs, int64_t chunks, int vsplit_first, int vsplit, i
 }
 
 // Chain pieces (and the workgroups per pair they run with) for the two-launch
-// schedule: chain_parts when given, else the cheapest P by the model above --
+// schedule: chain_parts when given; else (AUTO) the split, up to chain_cap
+// pieces, whose modelled cost is below 0.9 of the unsplit run's -- over
 // vsplit 1, 2 and 4 when value_split is automatic -- and whose chain area the
-// workspace holds (none when no device is known).  The first split launch
+// workspace holds (none when no device is known).  Fewer than 3 pieces run
+// nothing side by side.  The first split launch
 // holds twice the workgroups of the second, so with value_split automatic it
 // takes its own count (vsplit_first): at B1 T8192 H12, 11 pieces, one
 // workgroup per pair and role fits the first launch in one round where two
